@@ -1,0 +1,188 @@
+"""Attention over the de-paged cache, in fp64 (oracle; test infrastructure only).
+
+Definition (Tutorial §2, "Attention(Q, K, V) = softmax(QK^T / sqrt(d)) V";
+Lecture 10 "KV Cache 原理": at a decode step the new token's query is scored
+against every cached key and the scores weight a sum of every cached value):
+
+    for query row q, keys K[0..lam), values V[0..lam), scale sigma:
+        s_t  = sigma * sum_k q[k] * K[t, k]
+        out  = sum_t exp(s_t) V[t] / sum_t exp(s_t)
+        lse  = log sum_t exp(s_t)
+
+The row maximum m is subtracted inside exp (exp(s_t - m) / sum exp(s_u - m) is
+the same softmax); it only keeps the fp64 exponentials finite.
+
+GQA (Lecture 10 "Grouped Query Attention"; Tutorial §3): query heads are split
+into groups that share one K/V head, n_kv_heads = n_heads / group_size.  The
+pages give no index rule; heads are taken in contiguous groups, so query head h
+reads KV head h // (n_heads / n_kv_heads).
+
+Verify (Guide §4.2, Lecture 10 "Speculative Decoding"): the target model scores
+the last token and the K draft tokens in ONE forward.  With seq_len L counting
+those nq = K + 1 positions, query position i (0 <= i < nq) sits at absolute
+position L - nq + i and, being causal, sees tokens t <= L - nq + i, that is the
+first lam_i = L - nq + 1 + i tokens.  Decode is nq = 1, lam = L.
+
+Context split (not on the pages; stated by the benchmark spec): the tokens visible to a row
+are cut into partitions, attention is taken over each (o_p, lse_p), and the
+partials are recombined with the log-sum-exp identity
+
+    M = max_p lse_p,  w_p = exp(lse_p - M),
+    out = sum_p w_p o_p / sum_p w_p,  lse = M + log sum_p w_p,
+
+which is exact because exp(lse_p) is partition p's softmax denominator.
+A row that sees no token has out = 0 and lse = -inf.
+"""
+
+import numpy as np
+
+from . import paging, storage
+
+
+def attend(q_rows, K, V, sigma, limits):
+    """fp64 attention of each row of ``q_rows`` ([R, d]) over the first
+    ``limits[r]`` rows of K and V ([L, d]).  Returns (out [R, d], lse [R])."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    R, d = q_rows.shape
+    out = np.zeros((R, d), dtype=np.float64)
+    lse = np.full((R,), -np.inf, dtype=np.float64)
+    for r in range(R):
+        lam = int(limits[r])
+        if lam <= 0:
+            continue
+        s = sigma * (K[:lam] @ q_rows[r])
+        m = s.max()
+        e = np.exp(s - m)
+        l = e.sum()
+        out[r] = (e @ V[:lam]) / l
+        lse[r] = m + np.log(l)
+    return out, lse
+
+
+def row_limits(seq_len, num_q_pos):
+    """Visible-token count of each query position (causal verify rows)."""
+    return [max(0, seq_len - num_q_pos + 1 + i) for i in range(num_q_pos)]
+
+
+def _group_rows(q_dec, b, g, G, num_q_pos):
+    """Rows (i, head) of sequence b that read KV head g, in (i, head) order."""
+    rows, idx = [], []
+    for i in range(num_q_pos):
+        for hg in range(G):
+            h = g * G + hg
+            rows.append(q_dec[b, i, h])
+            idx.append((i, h))
+    return np.stack(rows), idx
+
+
+def paged_attention(q, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens, sigma,
+                    num_q_pos=1, k_scale=None, v_scale=None, pairs=None, fast=True):
+    """Attention of every query row against its sequence's paged cache.
+
+    q: [B, nq, Hq, d] stored as ``q_kind``; caches in the project format (see
+    ``paging``).  Returns (out [B, nq, Hq, d], lse [B, nq, Hq]) in fp64.  With
+    ``pairs`` (a list of (b, g)) only those sequence/KV-head pairs are computed and
+    every other entry is NaN.  ``sigma`` is used as given (pass the fp32 value the
+    kernel receives, widened).
+    """
+    qd = storage.decode(q, q_kind)
+    B, nq, Hq, d = qd.shape
+    assert nq == num_q_pos
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    out = np.full((B, nq, Hq, d), np.nan)
+    lse = np.full((B, nq, Hq), np.nan)
+    if pairs is None:
+        pairs = [(b, g) for b in range(B) for g in range(Hkv)]
+    dep = paging.depage_fast if fast else paging.depage
+    for b, g in pairs:
+        L = int(seq_lens[b])
+        K, V = dep(k_cache, v_cache, kv_kind, block_tables[b], L, g, k_scale, v_scale)
+        rows, idx = _group_rows(qd, b, g, G, nq)
+        lim = row_limits(L, nq)
+        o, ls = attend(rows, K, V, sigma, [lim[i] for i, _ in idx])
+        for r, (i, h) in enumerate(idx):
+            out[b, i, h] = o[r]
+            lse[b, i, h] = ls[r]
+    return out, lse
+
+
+def partitions_used(seq_len, partition_tokens, max_partitions):
+    """Number of partitions a sequence of ``seq_len`` tokens occupies: one per
+    ``partition_tokens`` tokens, at most ``max_partitions`` (the last one then also
+    takes every remaining token)."""
+    if seq_len <= 0:
+        return 0
+    return min(-(-seq_len // partition_tokens), max_partitions)
+
+
+def partition_range(seq_len, p, partition_tokens, max_partitions):
+    """Token range [lo, hi) of partition p."""
+    n = partitions_used(seq_len, partition_tokens, max_partitions)
+    lo = p * partition_tokens
+    hi = seq_len if p == n - 1 else min(seq_len, (p + 1) * partition_tokens)
+    return lo, hi
+
+
+def paged_attention_partitions(q, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens,
+                               sigma, partition_tokens, max_partitions, num_q_pos=1,
+                               k_scale=None, v_scale=None, pairs=None):
+    """Per-partition partial attention (o_p, lse_p).
+
+    Returns (o [B, nq, Hq, P, d], lse [B, nq, Hq, P]) with P = max_partitions;
+    partition p of a row attends over the tokens of [lo_p, hi_p) that the row may
+    see.  Entries of partitions a sequence does not occupy are NaN.
+    """
+    qd = storage.decode(q, q_kind)
+    B, nq, Hq, d = qd.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    P = max_partitions
+    o = np.full((B, nq, Hq, P, d), np.nan)
+    ls = np.full((B, nq, Hq, P), np.nan)
+    if pairs is None:
+        pairs = [(b, g) for b in range(B) for g in range(Hkv)]
+    for b, g in pairs:
+        L = int(seq_lens[b])
+        K, V = paging.depage_fast(k_cache, v_cache, kv_kind, block_tables[b], L, g,
+                                  k_scale, v_scale)
+        rows, idx = _group_rows(qd, b, g, G, nq)
+        lim = row_limits(L, nq)
+        for p in range(partitions_used(L, partition_tokens, max_partitions)):
+            lo, hi = partition_range(L, p, partition_tokens, max_partitions)
+            # rows see tokens [lo, min(hi, lam)); shift K/V so the window starts at 0
+            lims = [max(0, min(hi, lim[i]) - lo) for i, _ in idx]
+            op, lp = attend(rows, K[lo:hi], V[lo:hi], sigma, lims)
+            for r, (i, h) in enumerate(idx):
+                o[b, i, h, p] = op[r]
+                ls[b, i, h, p] = lp[r]
+    return o, ls
+
+
+def lse_merge(o_parts, lse_parts, n_parts=None):
+    """Log-sum-exp recombination of partial attention results.
+
+    o_parts [..., P, d], lse_parts [..., P]; ``n_parts`` (broadcast against the
+    leading dims) limits each row to its first n partitions.  Partitions with
+    lse = -inf carry no weight.  Returns (out [..., d], lse [...]).
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    lead = lse_parts.shape[:-1]
+    P = lse_parts.shape[-1]
+    if n_parts is None:
+        n_parts = np.full(lead, P)
+    n_parts = np.broadcast_to(np.asarray(n_parts), lead)
+    out = np.zeros(lead + (o_parts.shape[-1],))
+    lse = np.full(lead, -np.inf)
+    for ix in np.ndindex(*lead):
+        n = int(n_parts[ix])
+        lp = lse_parts[ix][:n]
+        live = np.isfinite(lp)
+        if not live.any():
+            continue
+        M = lp[live].max()
+        w = np.exp(lp[live] - M)
+        out[ix] = (w[:, None] * o_parts[ix][:n][live]).sum(0) / w.sum()
+        lse[ix] = M + np.log(w.sum())
+    return out, lse

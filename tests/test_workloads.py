@@ -1,0 +1,138 @@
+"""Host harness: block manager semantics and the seeded workloads' structure."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import kvsize, paging
+
+
+def test_allocator_semantics():
+    a = W.BlockAllocator(10, 16)
+    assert a.allocate("x", 33) == [9, 8, 7]          # ceil(33/16) blocks, popped from the end
+    a.token_counts["x"] = 48
+    a.append_token("x")                               # 48 tokens fill 3 blocks -> new block
+    assert len(a.block_tables["x"]) == 4
+    a.append_token("x")
+    assert len(a.block_tables["x"]) == 4
+    with pytest.raises(RuntimeError):
+        a.allocate("y", 16 * 7)
+    a.release("x")
+    assert sorted(a.free_blocks) == list(range(10))
+    b = W.BlockAllocator(2, 16)
+    b.allocate("z", 32)
+    with pytest.raises(RuntimeError):
+        b.append_token("z")
+
+
+def test_fork_shares_prefix_refcounted():
+    a = W.BlockAllocator(20, 16)
+    a.allocate(0, 64)
+    a.fork(0, 1, 32, 64)
+    assert a.block_tables[1][:2] == a.block_tables[0][:2]
+    assert set(a.block_tables[1][2:]).isdisjoint(a.block_tables[0])
+    a.release(0)
+    assert a.block_tables[1][0] not in a.free_blocks      # still referenced
+    a.release(1)
+    assert sorted(a.free_blocks) == list(range(20))
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b", "verify_int8"])
+def test_tables_distinct_and_sized(name):
+    wl = W.generate(name)
+    seen = set()
+    for b, L in enumerate(wl.seq_lens.tolist()):
+        n = kvsize.blocks_needed(L)
+        row = wl.block_tables[b].tolist()
+        assert all(x >= 0 for x in row[:n]) and all(x == -1 for x in row[n:])
+        assert seen.isdisjoint(row[:n])
+        seen.update(row[:n])
+    assert max(seen) < wl.k_cache.shape[0]
+
+
+def test_tiny_config_lengths_and_append_slots():
+    wl = W.generate("tiny_fp32")
+    assert wl.seq_lens.tolist() == [38, 129, 201, 512]
+    assert wl.block_tables.shape[0] == 4 and wl.k_cache.shape == (256, 2, 16, 64)
+    for b, L in enumerate(wl.seq_lens.tolist()):
+        assert int(wl.slot_mapping[b]) == paging.slot_of(wl.block_tables[b].tolist(), L - 1)
+        blk, off = divmod(int(wl.slot_mapping[b]), 16)
+        assert torch.isnan(wl.k_cache[blk, :, off, :]).all()   # filled only by the append
+        assert torch.isnan(wl.v_cache[blk, :, :, off]).all()
+
+
+def test_shared_prefix_structure():
+    wl = W.generate("llama2_70b_prefix")
+    t = wl.block_tables
+    assert wl.k_cache.shape[0] == 5120
+    for grp in range(6):
+        rows = t[grp * 5: grp * 5 + 5]
+        assert (rows[:, :128] == rows[0, :128]).all()
+        priv = [set(r[128:].tolist()) for r in rows]
+        for i in range(5):
+            for j in range(i + 1, 5):
+                assert priv[i].isdisjoint(priv[j])
+    assert len(set(t.flatten().tolist())) == 5120
+
+
+def test_peaked_positions():
+    cfg = W.scaled("long_128k", lengths=(4096,) * 4)
+    wl = W.generate(cfg)
+    k = wl.k_cache.float()
+    big = (k.abs().amax(dim=(1, 3)) > 6.5)               # [NB, 16] slot-level
+    frac = big.float().mean().item()
+    assert 0.006 < frac < 0.014
+
+
+def test_int8_encoding_invariants():
+    wl = W.generate(W.scaled("verify_int8", batch=4, length_range=(20, 300)), poison=False)
+    occ = wl.occupancy
+    x32 = None
+    for name, cache, scale, slot_dim in (("k", wl.k_cache, wl.k_scale, 2),
+                                         ("v", wl.v_cache, wl.v_scale, 3)):
+        assert cache.dtype == torch.int8 and int(cache.abs().max()) <= 127
+        for blk in range(cache.shape[0]):
+            n = int(occ[blk])
+            if n == 0:
+                continue
+            live = cache[blk, :, :n, :] if slot_dim == 2 else cache[blk, :, :, :n]
+            # the largest-magnitude live element encodes to +-127 in every head
+            assert (live.abs().amax(dim=(1, 2)) == 127).all()
+            assert (scale[blk] > 0).all()
+
+
+def test_int8_dequant_error_bound():
+    cfg = W.scaled("verify_int8", batch=2, length_range=(40, 64))
+    gen_a = W.generate(cfg, poison=False)
+    # regenerate the fp32 pool the encoder saw (same seed, same draw order)
+    g = torch.Generator().manual_seed(cfg.seed)
+    lens = W._draw_lengths(cfg, g)
+    NB = gen_a.k_cache.shape[0]
+    torch.randperm(NB, generator=g)
+    k32 = W._randn_pool((NB, cfg.num_kv_heads, 16, cfg.head_dim), g)
+    deq = gen_a.k_cache.float() * gen_a.k_scale[:, :, None, None]
+    err = (deq - k32).abs()
+    bound = gen_a.k_scale[:, :, None, None] / 2 * (1 + 1e-6)
+    live = (torch.arange(16)[None, :] < gen_a.occupancy[:, None])[:, None, :, None]
+    assert bool(((err <= bound) | ~live).all())
+
+
+def test_seeded_determinism():
+    a = W.generate("tiny_fp32")
+    b = W.generate("tiny_fp32")
+    assert torch.equal(a.block_tables, b.block_tables)
+    assert torch.equal(a.q, b.q)
+    assert torch.equal(a.k_cache.nan_to_num(), b.k_cache.nan_to_num())
+
+
+def test_relabel_moves_data_with_tables():
+    wl = W.generate(W.scaled("tiny_fp32", head_dim=8))
+    perm = torch.randperm(256, generator=torch.Generator().manual_seed(1))
+    w2 = W.relabel_blocks(wl, perm)
+    for b in range(4):
+        L = int(wl.seq_lens[b])
+        K1, V1 = paging.depage(wl.k_cache.numpy(), wl.v_cache.numpy(), "f32",
+                               wl.block_tables[b].numpy(), L, 1)
+        K2, V2 = paging.depage(w2.k_cache.numpy(), w2.v_cache.numpy(), "f32",
+                               w2.block_tables[b].numpy(), L, 1)
+        assert np.array_equal(K1, K2, equal_nan=True) and np.array_equal(V1, V2, equal_nan=True)
