@@ -1,0 +1,181 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged GQA decode-attention library
+ * (libpaged_attn.so).
+ *
+ * The operation (devpress.csdn.net KV Cache / GQA / PagedAttention tutorial, section 2
+ * "KV Cache 到底缓存了什么？": Attention(Q,K,V) = softmax(Q K^T / sqrt(d)) V; CS336
+ * lecture 10, "KV Cache 原理": at each decode step the new token's K and V are appended
+ * to the cache and its query attends to every cached K and V):
+ *
+ *   for every sequence b, query position i and query head h, with g = h / (Hq / Hkv)
+ *   (GQA: a group of query heads shares one KV head -- lecture 10, "Grouped Query
+ *   Attention"), and lam = seq_lens[b] - nq + 1 + i visible tokens:
+ *     s_t  = sm_scale * dot(q[b,i,h,:], K[b,g,t,:])          t < lam
+ *     out  = sum_t exp(s_t) V[b,g,t,:] / sum_t exp(s_t)
+ *     lse  = log sum_t exp(s_t)                               (natural log)
+ *
+ * Paged storage (tutorial section 7 "PagedAttention 如何解决显存碎片？"; lecture 10
+ * "PagedAttention 与 vLLM"): the cache is cut into blocks of 16 tokens; block_tables[b][j]
+ * names the physical block holding tokens 16j .. 16j+15 of sequence b.  Inside a block
+ * this library uses
+ *
+ *   k_cache[num_blocks][num_kv_heads][16][head_dim]      (token-major)
+ *   v_cache[num_blocks][num_kv_heads][head_dim][16]      (dim-major)
+ *
+ * so one (block, KV head) tile of K or V is one contiguous 16 x head_dim piece of memory.
+ * int8 caches carry one fp32 scale per (physical block, KV head) for each of K and V:
+ * k_scale[num_blocks][num_kv_heads], v_scale[num_blocks][num_kv_heads]; the stored code x_q
+ * stands for x_q * scale (lecture 10 "Quantization 量化 / 基本概念", zero point 0).
+ *
+ * Conventions for every call:
+ *  - Pointers named as device memory must be device (HBM) pointers on the current HIP
+ *    device; the caller owns all of them, including workspaces.  The library never
+ *    allocates, frees or synchronises and keeps no mutable global state.
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream).  Every call
+ *    only enqueues work on it and returns.
+ *  - Return value: PA_OK (0) or a negative PA_ERR_* code.  Every argument check runs on
+ *    the host before any HIP call, so a rejected call touches no GPU state.
+ *    PA_ERR_LAUNCH reports a failed kernel launch (hipGetLastError).
+ *  - Device-side contract: table entries for logical blocks < ceil(seq_len/16) name
+ *    physical blocks in [0, num_blocks).  An entry outside that range is not read: its
+ *    tokens are skipped.  seq_lens[b] larger than 16 * max_blocks_per_seq is cut to that
+ *    capacity; negative lengths count as 0.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 };
+
+/* status codes */
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,       /* a required pointer is NULL                                   */
+  PA_ERR_DIMS = -2,       /* a size is < 1 (or < 0 where 0 is allowed), or Hq % Hkv != 0  */
+  PA_ERR_DTYPE = -3,      /* element-type combination not supported by the call           */
+  PA_ERR_HEAD_DIM = -4,   /* head_dim is not 64 or 128                                     */
+  PA_ERR_BLOCK_SIZE = -5, /* block_size is not 16                                          */
+  PA_ERR_PARTITION = -6,  /* partition_tokens not a positive multiple of 16, or
+                             max_partitions < 1                                            */
+  PA_ERR_LAUNCH = -7      /* a kernel launch failed                                        */
+};
+
+/* Shapes and element types shared by every call. */
+typedef struct pa_dims {
+  int32_t num_seqs;           /* B: sequences in the batch (>= 1)                          */
+  int32_t num_q_heads;        /* Hq (>= 1)                                                 */
+  int32_t num_kv_heads;       /* Hkv (>= 1, divides Hq; Hkv == 1 is MQA, Hkv == Hq is MHA)  */
+  int32_t head_dim;           /* d: 64 or 128                                              */
+  int32_t block_size;         /* tokens per block: must be 16                              */
+  int32_t max_blocks_per_seq; /* row length of block_tables (>= 1)                         */
+  int64_t num_blocks;         /* physical blocks in each of k_cache / v_cache (>= 1)       */
+  int32_t q_dtype;            /* PA_F32 or PA_BF16                                         */
+  int32_t kv_dtype;           /* PA_F32, PA_BF16 or PA_I8                                  */
+} pa_dims;
+/* Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, I8). */
+
+/*
+ * kv_append -- write each new token's K and V into its cache slot.
+ * Tutorial section 2 / lecture 10 "KV Cache 原理": a decode step appends the new token's
+ * K and V to the cache; tutorial section 7: the token lands in a block of the sequence's
+ * table.  The slot (physical_block * 16 + offset) of each token is given by the caller.
+ *   k_new, v_new   device, [num_tokens][num_kv_heads][head_dim], kv_dtype (F32 or BF16)
+ *   slot_mapping   device, [num_tokens] int64; slot < 0 means "skip this token";
+ *                  a slot >= num_blocks * 16 is also skipped
+ *   k_cache, v_cache device, the cache layout above; written in place (a bit copy)
+ * num_tokens may be 0 (nothing is launched).  int8 caches: PA_ERR_DTYPE.
+ */
+int kv_append(const pa_dims* dims, const void* k_new, const void* v_new,
+              const int64_t* slot_mapping, int32_t num_tokens, void* k_cache, void* v_cache,
+              void* stream);
+
+/*
+ * paged_decode_attn -- single-token decode attention over the paged cache (nq = 1).
+ *   q            device, [B][Hq][head_dim], q_dtype
+ *   k_cache, v_cache device, layout above, kv_dtype
+ *   k_scale, v_scale device, [num_blocks][Hkv] fp32; required for PA_I8, ignored otherwise
+ *   block_tables device, [B][max_blocks_per_seq] int32
+ *   seq_lens     device, [B] int32: tokens attended, including the new one
+ *   sm_scale     the softmax scale (1/sqrt(head_dim) for the pages' formula)
+ *   out          device, [B][Hq][head_dim] fp32; a sequence with no token gets zeros
+ */
+int paged_decode_attn(const pa_dims* dims, const void* q, const void* k_cache,
+                      const void* v_cache, const float* k_scale, const float* v_scale,
+                      const int32_t* block_tables, const int32_t* seq_lens, float sm_scale,
+                      float* out, void* stream);
+
+/*
+ * paged_verify_attn -- the causal verify forward of speculative decoding: nq query
+ * positions per sequence (the last accepted token plus nq - 1 draft tokens) scored in one
+ * pass (guide section 4.2 "数学原理": the target model scores all draft positions in a
+ * single forward; lecture 10 "Speculative Decoding").  seq_lens counts the nq positions,
+ * whose K/V are already in the cache; position i is token seq_len - nq + i and sees tokens
+ * 0 .. seq_len - nq + i.
+ *   num_q_pos    nq >= 1 (nq == 1 is paged_decode_attn)
+ *   q            device, [B][nq][Hq][head_dim], q_dtype
+ *   out          device, [B][nq][Hq][head_dim] fp32; a row that sees no token gets zeros
+ *   other arguments as paged_decode_attn.
+ */
+int paged_verify_attn(const pa_dims* dims, int32_t num_q_pos, const void* q,
+                      const void* k_cache, const void* v_cache, const float* k_scale,
+                      const float* v_scale, const int32_t* block_tables, const int32_t* seq_lens,
+                      float sm_scale, float* out, void* stream);
+
+/*
+ * paged_decode_attn_split -- decode attention with each sequence's context cut into
+ * partitions of partition_tokens tokens, each partition handled by its own workgroups.
+ * A sequence of L tokens occupies n = min(ceil(L / partition_tokens), max_partitions)
+ * partitions; the last one also takes any tokens beyond n * partition_tokens.  For each
+ * occupied partition p it writes the partition's normalised result and log-sum-exp:
+ *   part_out     device, [B][Hq][max_partitions][head_dim] fp32
+ *   part_lse     device, [B][Hq][max_partitions] fp32 (natural log; -inf if p saw no token)
+ * Entries of partitions a sequence does not occupy are not written.  lse_merge combines
+ * them.  Other arguments as paged_decode_attn.
+ */
+int paged_decode_attn_split(const pa_dims* dims, const void* q, const void* k_cache,
+                            const void* v_cache, const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            float sm_scale, int32_t partition_tokens, int32_t max_partitions,
+                            float* part_out, float* part_lse, void* stream);
+
+/*
+ * lse_merge -- recombine partition results exactly: with M = max_p lse_p and
+ * w_p = exp(lse_p - M), out = sum_p w_p o_p / sum_p w_p and lse = M + log sum_p w_p over the
+ * n occupied partitions of each sequence (n as in paged_decode_attn_split, from seq_lens).
+ * Partitions with lse_p = -inf carry no weight; if all do, out = 0 and lse = -inf.
+ *   part_out, part_lse device, as written by paged_decode_attn_split
+ *   out          device, [B][Hq][head_dim] fp32
+ *   out_lse      device, [B][Hq] fp32, or NULL
+ */
+int lse_merge(const pa_dims* dims, const float* part_out, const float* part_lse,
+              const int32_t* seq_lens, int32_t partition_tokens, int32_t max_partitions,
+              float* out, float* out_lse, void* stream);
+
+/* Bytes of part_out plus part_lse for paged_decode_attn_split (0 if dims are invalid). */
+size_t paged_split_workspace_bytes(const pa_dims* dims, int32_t max_partitions);
+
+/*
+ * kv_gather -- copy each sequence's tokens out of the pool into contiguous order, using
+ * the same block-table translation as the attention kernels (a check of that indexing).
+ *   k_out, v_out device, [B][Hkv][max_len][head_dim], kv_dtype (int8 stays int8)
+ * Tokens t >= min(seq_lens[b], max_len) are not written.
+ */
+int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* seq_lens, int32_t max_len,
+              void* k_out, void* v_out, void* stream);
+
+/* Text for a status code (static storage). */
+const char* paged_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,185 @@
+// C ABI of libpaged_attn.so: argument checks on the host, then one launch per call.
+// Every check here runs before any HIP call, so a rejected call leaves the GPU untouched
+// (and can be exercised on a host without a GPU).
+#include <limits.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "../../include/paged_attn.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+int check_dims(const pa_dims* d) {
+  if (d == nullptr) return PA_ERR_NULL;
+  if (d->block_size != 16) return PA_ERR_BLOCK_SIZE;
+  if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_HEAD_DIM;
+  if (d->num_seqs < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
+      d->max_blocks_per_seq < 1 || d->num_blocks < 1)
+    return PA_ERR_DIMS;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_DIMS;
+  // token positions are int32 inside the kernels
+  if ((int64_t)d->max_blocks_per_seq * 16 > INT_MAX) return PA_ERR_DIMS;
+  return PA_OK;
+}
+
+int check_attn_types(const pa_dims* d) {
+  if (d->q_dtype == PA_F32 && d->kv_dtype == PA_F32) return PA_OK;
+  if (d->q_dtype == PA_BF16 && (d->kv_dtype == PA_BF16 || d->kv_dtype == PA_I8)) return PA_OK;
+  return PA_ERR_DTYPE;
+}
+
+int check_attn_inputs(const pa_dims* d, const void* q, const void* k, const void* v,
+                      const float* ks, const float* vs, const int32_t* tables,
+                      const int32_t* lens) {
+  int st = check_dims(d);
+  if (st != PA_OK) return st;
+  st = check_attn_types(d);
+  if (st != PA_OK) return st;
+  if (!q || !k || !v || !tables || !lens) return PA_ERR_NULL;
+  if (d->kv_dtype == PA_I8 && (!ks || !vs)) return PA_ERR_NULL;
+  return PA_OK;
+}
+
+pa::AttnArgs make_args(const pa_dims* d, int32_t nq, const void* q, const void* k,
+                       const void* v, const float* ks, const float* vs,
+                       const int32_t* tables, const int32_t* lens, float sm_scale) {
+  pa::AttnArgs a{};
+  a.q = q;
+  a.k_cache = k;
+  a.v_cache = v;
+  a.k_scale = ks;
+  a.v_scale = vs;
+  a.block_tables = tables;
+  a.seq_lens = lens;
+  a.num_seqs = d->num_seqs;
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.group = d->num_q_heads / d->num_kv_heads;
+  a.head_dim = d->head_dim;
+  a.max_blocks = d->max_blocks_per_seq;
+  a.num_blocks = d->num_blocks;
+  a.num_q_pos = nq;
+  a.rows = nq * a.group;
+  a.scale_log2 = sm_scale * kLog2e;
+  a.part_tokens = 0;
+  a.max_parts = 1;
+  a.split = 0;
+  return a;
+}
+
+int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_BF16 ? 2 : 1); }
+
+}  // namespace
+
+extern "C" {
+
+int kv_append(const pa_dims* dims, const void* k_new, const void* v_new,
+              const int64_t* slot_mapping, int32_t num_tokens, void* k_cache, void* v_cache,
+              void* stream) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->kv_dtype != PA_F32 && dims->kv_dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (num_tokens < 0) return PA_ERR_DIMS;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  return pa::launch_append(k_new, v_new, slot_mapping, num_tokens, dims->num_kv_heads,
+                           dims->head_dim, dims->num_blocks, elem_bytes(dims->kv_dtype), k_cache,
+                           v_cache, stream);
+}
+
+int paged_verify_attn(const pa_dims* dims, int32_t num_q_pos, const void* q,
+                      const void* k_cache, const void* v_cache, const float* k_scale,
+                      const float* v_scale, const int32_t* block_tables, const int32_t* seq_lens,
+                      float sm_scale, float* out, void* stream) {
+  int st = check_attn_inputs(dims, q, k_cache, v_cache, k_scale, v_scale, block_tables, seq_lens);
+  if (st != PA_OK) return st;
+  if (!out) return PA_ERR_NULL;
+  if (num_q_pos < 1 || (int64_t)num_q_pos * (dims->num_q_heads / dims->num_kv_heads) > INT_MAX)
+    return PA_ERR_DIMS;
+  pa::AttnArgs a = make_args(dims, num_q_pos, q, k_cache, v_cache, k_scale, v_scale,
+                             block_tables, seq_lens, sm_scale);
+  a.out = out;
+  return pa::launch_attention(a, dims->q_dtype, dims->kv_dtype, stream);
+}
+
+int paged_decode_attn(const pa_dims* dims, const void* q, const void* k_cache,
+                      const void* v_cache, const float* k_scale, const float* v_scale,
+                      const int32_t* block_tables, const int32_t* seq_lens, float sm_scale,
+                      float* out, void* stream) {
+  return paged_verify_attn(dims, 1, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                           seq_lens, sm_scale, out, stream);
+}
+
+int paged_decode_attn_split(const pa_dims* dims, const void* q, const void* k_cache,
+                            const void* v_cache, const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            float sm_scale, int32_t partition_tokens, int32_t max_partitions,
+                            float* part_out, float* part_lse, void* stream) {
+  int st = check_attn_inputs(dims, q, k_cache, v_cache, k_scale, v_scale, block_tables, seq_lens);
+  if (st != PA_OK) return st;
+  if (partition_tokens <= 0 || partition_tokens % 16 != 0 || max_partitions < 1)
+    return PA_ERR_PARTITION;
+  if (!part_out || !part_lse) return PA_ERR_NULL;
+  pa::AttnArgs a = make_args(dims, 1, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                             seq_lens, sm_scale);
+  a.out = part_out;
+  a.part_lse = part_lse;
+  a.part_tokens = partition_tokens;
+  a.max_parts = max_partitions;
+  a.split = 1;
+  return pa::launch_attention(a, dims->q_dtype, dims->kv_dtype, stream);
+}
+
+int lse_merge(const pa_dims* dims, const float* part_out, const float* part_lse,
+              const int32_t* seq_lens, int32_t partition_tokens, int32_t max_partitions,
+              float* out, float* out_lse, void* stream) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (partition_tokens <= 0 || partition_tokens % 16 != 0 || max_partitions < 1)
+    return PA_ERR_PARTITION;
+  if (!part_out || !part_lse || !seq_lens || !out) return PA_ERR_NULL;
+  return pa::launch_merge(part_out, part_lse, seq_lens, dims->num_seqs, dims->num_q_heads,
+                          dims->head_dim, dims->max_blocks_per_seq, partition_tokens,
+                          max_partitions, out, out_lse, stream);
+}
+
+size_t paged_split_workspace_bytes(const pa_dims* dims, int32_t max_partitions) {
+  if (check_dims(dims) != PA_OK || max_partitions < 1) return 0;
+  const size_t rows = (size_t)dims->num_seqs * (size_t)dims->num_q_heads * (size_t)max_partitions;
+  return rows * ((size_t)dims->head_dim + 1) * sizeof(float);
+}
+
+int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* seq_lens, int32_t max_len,
+              void* k_out, void* v_out, void* stream) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->kv_dtype != PA_F32 && dims->kv_dtype != PA_BF16 && dims->kv_dtype != PA_I8)
+    return PA_ERR_DTYPE;
+  if (max_len < 0) return PA_ERR_DIMS;
+  if (max_len == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_tables || !seq_lens || !k_out || !v_out) return PA_ERR_NULL;
+  return pa::launch_gather(k_cache, v_cache, block_tables, seq_lens, dims->num_seqs,
+                           dims->num_kv_heads, dims->head_dim, dims->max_blocks_per_seq,
+                           dims->num_blocks, max_len, elem_bytes(dims->kv_dtype), k_out, v_out,
+                           stream);
+}
+
+const char* paged_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_DIMS: return "a size is out of range or num_q_heads % num_kv_heads != 0";
+    case PA_ERR_DTYPE: return "unsupported element-type combination";
+    case PA_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+    case PA_ERR_BLOCK_SIZE: return "block_size must be 16";
+    case PA_ERR_PARTITION: return "partition_tokens must be a positive multiple of 16 and max_partitions >= 1";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,524 @@
+// Paged GQA decode / verify attention for gfx950 (CDNA4).
+//
+// What is computed (devpress tutorial section 2: softmax(q K^T / sqrt(d)) V; lecture 10
+// "KV Cache 原理"; GQA sharing from lecture 10 "Grouped Query Attention"): every query
+// row of a sequence attends over the sequence's cached tokens, reached through its block
+// table (tutorial section 7).  A (sequence, KV head) pair serves nq * G query rows: the G
+// heads of the group at each of the nq positions (nq = 1 for decode, K + 1 for the
+// speculative verify forward of guide section 4.2).
+//
+// How, on CDNA4:
+//  * The G-head group is the N side of matrix-core (MFMA) tiles, so each K/V tile that is
+//    read from HBM is used by the whole group straight out of registers:
+//      S^T[16 tokens x 16 rows] = K_tile[16 x d] * Q^T[d x 16 rows]
+//      O^T[d x 16 rows]        += V_tile^T[d x 16 tokens] * P^T[16 tokens x 16 rows]
+//    K rows are token-major and V rows dim-major in HBM, which is exactly the register
+//    layout both MFMA A-operands want, so every lane issues contiguous 8/16-byte loads.
+//  * Online softmax in the log2 domain: per row a running max and a running sum; the
+//    output accumulators are rescaled only when some row's max grows.
+//  * P feeds the P*V MFMA in two 16-bit pieces (hi + lo) so the product keeps ~16
+//    significant bits of the fp32 probabilities; the fp32 path uses fp32 MFMA directly.
+//  * int8 K/V are decoded to exact fp16 in registers; the per-(block, head) K scale
+//    multiplies the scores and the V scale is folded into P.
+//  * A workgroup of W waves owns one (sequence, KV head, row group, partition); its waves
+//    take interleaved blocks and are merged through LDS at the end (same LSE identity as
+//    the cross-workgroup split).
+//  * Workgroup ids are remapped so that consecutive units (same KV head, neighbouring
+//    sequences -- e.g. sequences sharing a prefix) land on the same XCD and its L2.
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "pa_common.hpp"
+#include "../../include/paged_attn.h"
+
+namespace pa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------------------
+// Element-type traits.  Lane l of a wave has row16 = l % 16 and grp = l / 16.
+//   K operand (MFMA A, 16 tokens x d):  lane holds token row16, a grp-dependent d slice.
+//   Q operand (MFMA B, d x 16 rows):    lane holds query row row16, the same d slice.
+//   S^T result:                          lane holds tokens 4*grp + v (v = 0..3), row row16.
+//   V operand (MFMA A, 16 d x 16 tok):   lane holds d = 16*t + row16, tokens 4*grp .. +3.
+//   O^T accumulator:                     lane holds d = 16*t + 4*grp + v, row row16.
+// ---------------------------------------------------------------------------------------
+template <int D>
+struct Bf16Kv {
+  static constexpr int NK = D / 32;  // 16x16x32 bf16 steps for q.K
+  static constexpr int ND = D / 16;  // d tiles of the output
+  static constexpr int kElem = 2;
+  static constexpr int kQElem = 2;
+  struct Q { bf16x8 v[NK]; };
+  struct K { u32x4 v[NK]; };
+  struct V { u32x2 v[ND]; };
+
+  // d index of step kk, element j: 32*kk + 8*grp + j
+  __device__ static void load_q(Q& q, const void* row, bool valid, int grp) {
+    const uint16_t* p = static_cast<const uint16_t*>(row) + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      u32x4 x = valid ? *reinterpret_cast<const u32x4*>(p + 32 * kk) : u32x4{0, 0, 0, 0};
+      q.v[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  __device__ static void load_k(K& k, const void* tile, int row16, int grp) {
+    const uint16_t* p = static_cast<const uint16_t*>(tile) + row16 * D + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) k.v[kk] = *reinterpret_cast<const u32x4*>(p + 32 * kk);
+  }
+  __device__ static void load_v(V& v, const void* tile, int row16, int grp) {
+    const uint16_t* p = static_cast<const uint16_t*>(tile) + row16 * 16 + 4 * grp;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) v.v[t] = *reinterpret_cast<const u32x2*>(p + t * 256);
+  }
+  __device__ static f32x4 qk(const K& k, const Q& q) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k.v[kk]), q.v[kk],
+                                                  c, 0, 0, 0);
+    return c;
+  }
+  // zero V of tokens >= nvalid (poisoned tail slots must not reach the MFMA: 0 * NaN)
+  __device__ static void mask_v(V& v, int nvalid, int grp) {
+    const int t0 = 4 * grp;
+    const uint32_t m0 = (t0 + 0 < nvalid ? 0x0000FFFFu : 0u) | (t0 + 1 < nvalid ? 0xFFFF0000u : 0u);
+    const uint32_t m1 = (t0 + 2 < nvalid ? 0x0000FFFFu : 0u) | (t0 + 3 < nvalid ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int t = 0; t < ND; ++t) {
+      v.v[t].x &= m0;
+      v.v[t].y &= m1;
+    }
+  }
+  __device__ static void pv(f32x4* acc, const V& v, f32x4 p, float /*vfac*/) {
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = (__bf16)p[e];
+      lo[e] = (__bf16)(p[e] - (float)hi[e]);
+    }
+    const s16x4 h = __builtin_bit_cast(s16x4, hi);
+    const s16x4 l = __builtin_bit_cast(s16x4, lo);
+#pragma unroll
+    for (int t = 0; t < ND; ++t) {
+      const s16x4 a = __builtin_bit_cast(s16x4, v.v[t]);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, h, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, l, acc[t], 0, 0, 0);
+    }
+  }
+};
+
+template <int D>
+struct F32Kv {
+  static constexpr int NU = D / 16;  // float4 pieces per lane (d = 16*u + 4*grp + e)
+  static constexpr int ND = D / 16;
+  static constexpr int kElem = 4;
+  static constexpr int kQElem = 4;
+  struct Q { f32x4 v[NU]; };
+  struct K { f32x4 v[NU]; };
+  struct V { f32x4 v[ND]; };
+
+  __device__ static void load_q(Q& q, const void* row, bool valid, int grp) {
+    const float* p = static_cast<const float*>(row) + 4 * grp;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      q.v[u] = valid ? *reinterpret_cast<const f32x4*>(p + 16 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ static void load_k(K& k, const void* tile, int row16, int grp) {
+    const float* p = static_cast<const float*>(tile) + row16 * D + 4 * grp;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) k.v[u] = *reinterpret_cast<const f32x4*>(p + 16 * u);
+  }
+  __device__ static void load_v(V& v, const void* tile, int row16, int grp) {
+    const float* p = static_cast<const float*>(tile) + row16 * 16 + 4 * grp;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) v.v[t] = *reinterpret_cast<const f32x4*>(p + t * 256);
+  }
+  __device__ static f32x4 qk(const K& k, const Q& q) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(k.v[u][e], q.v[u][e], c, 0, 0, 0);
+    return c;
+  }
+  __device__ static void mask_v(V& v, int nvalid, int grp) {
+#pragma unroll
+    for (int t = 0; t < ND; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * grp + e >= nvalid) v.v[t][e] = 0.f;
+  }
+  __device__ static void pv(f32x4* acc, const V& v, f32x4 p, float /*vfac*/) {
+#pragma unroll
+    for (int t = 0; t < ND; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.v[t][e], p[e], acc[t], 0, 0, 0);
+  }
+};
+
+template <int D>
+struct I8Kv {
+  static constexpr int NH = D / 64;  // 16-byte K loads per lane (d = 64*h + 16*grp + 8*s + j)
+  static constexpr int ND = D / 16;
+  static constexpr int kElem = 1;
+  static constexpr int kQElem = 2;
+  struct Q { f16x8 v[2 * NH]; };
+  struct K { u32x4 v[NH]; };
+  struct V { uint32_t v[ND]; };
+
+  __device__ static void load_q(Q& q, const void* row, bool valid, int grp) {
+    const uint16_t* p = static_cast<const uint16_t*>(row) + 16 * grp;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 x = valid ? *reinterpret_cast<const u32x4*>(p + 64 * h + 8 * s) : u32x4{0, 0, 0, 0};
+        f16x8 f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[2 * j] = (_Float16)bf16_bits_to_f32(x[j] & 0xFFFFu);
+          f[2 * j + 1] = (_Float16)bf16_bits_to_f32(x[j] >> 16);
+        }
+        q.v[2 * h + s] = f;
+      }
+  }
+  __device__ static void load_k(K& k, const void* tile, int row16, int grp) {
+    const uint8_t* p = static_cast<const uint8_t*>(tile) + row16 * D + 16 * grp;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) k.v[h] = *reinterpret_cast<const u32x4*>(p + 64 * h);
+  }
+  __device__ static void load_v(V& v, const void* tile, int row16, int grp) {
+    const uint8_t* p = static_cast<const uint8_t*>(tile) + row16 * 16 + 4 * grp;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) v.v[t] = *reinterpret_cast<const uint32_t*>(p + t * 256);
+  }
+  __device__ static f32x4 qk(const K& k, const Q& q) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const f16x4 a0 = i8x4_to_f16x4(k.v[h].x), a1 = i8x4_to_f16x4(k.v[h].y);
+      const f16x4 a2 = i8x4_to_f16x4(k.v[h].z), a3 = i8x4_to_f16x4(k.v[h].w);
+      const f16x8 lo = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const f16x8 hi = {a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, q.v[2 * h], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, q.v[2 * h + 1], c, 0, 0, 0);
+    }
+    return c;
+  }
+  __device__ static void mask_v(V&, int, int) {}  // codes are finite; P = 0 removes them
+  // p is scaled by vfac = 256 * v_scale(block) / v_ref before the fp16 split, keeping
+  // small probabilities out of the fp16 subnormal range.
+  __device__ static void pv(f32x4* acc, const V& v, f32x4 p, float vfac) {
+    f16x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = p[e] * vfac;
+      hi[e] = (_Float16)x;
+      lo[e] = (_Float16)(x - (float)hi[e]);
+    }
+#pragma unroll
+    for (int t = 0; t < ND; ++t) {
+      const f16x4 a = i8x4_to_f16x4(v.v[t]);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, hi, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, lo, acc[t], 0, 0, 0);
+    }
+  }
+};
+
+template <class KV> struct IsInt8 { static constexpr bool value = false; };
+template <int D> struct IsInt8<I8Kv<D>> { static constexpr bool value = true; };
+
+// ---------------------------------------------------------------------------------------
+template <class KV, int D, int NT, int W>
+__global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
+  constexpr int ND = D / 16;
+  constexpr bool kInt8 = IsInt8<KV>::value;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int row16 = lane & 15;
+  const int grp = lane >> 4;
+
+  // ---- unit of work, with XCD-aware remapping of the workgroup id ----------------------
+  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
+  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg * a.max_parts;
+  const int64_t per_xcd = gridDim.x / 8;
+  const int64_t u = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (u >= units) return;
+  const int p = (int)(u % a.max_parts);
+  int64_t rest = u / a.max_parts;
+  const int rg = (int)(rest % nrg);
+  rest /= nrg;
+  const int b = (int)(rest % a.num_seqs);
+  const int g = (int)(rest / a.num_seqs);
+
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.max_blocks * kBlockTokens ? a.max_blocks * kBlockTokens : L);
+  int lo = 0, hi = L;
+  if (a.split) {
+    int nparts = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 0;
+    if (nparts > a.max_parts) nparts = a.max_parts;
+    if (p >= nparts) return;
+    lo = p * a.part_tokens;
+    hi = (p == nparts - 1) ? L : lo + a.part_tokens;
+  }
+  const int jb = lo / kBlockTokens;
+  const int je = (hi + kBlockTokens - 1) / kBlockTokens;
+
+  // ---- query rows handled by this lane -----------------------------------------------
+  typename KV::Q qop[NT];
+  int lim[NT];  // tokens [lo, lim) are visible to this lane's row
+  int row_base = rg * 16 * NT;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = row_base + nt * 16 + row16;
+    const bool valid = r < a.rows;
+    const int i = valid ? r / a.group : 0;
+    const int h = g * a.group + (valid ? r % a.group : 0);
+    const int64_t qoff = ((int64_t)(b * a.num_q_pos + i) * a.num_q_heads + h) * D;
+    KV::load_q(qop[nt], static_cast<const uint8_t*>(a.q) + qoff * KV::kQElem,
+               valid, grp);
+    int lam = valid ? L - a.num_q_pos + 1 + i : L;
+    lam = lam < 0 ? 0 : lam;
+    lim[nt] = lam < hi ? lam : hi;
+  }
+  // smallest visible limit of the rows in this row group (uniform)
+  int lim_min;
+  {
+    const int i0 = row_base / a.group;
+    int lam0 = L - a.num_q_pos + 1 + i0;
+    lam0 = lam0 < 0 ? 0 : lam0;
+    lim_min = lam0 < hi ? lam0 : hi;
+  }
+
+  const size_t tile_elems = (size_t)kBlockTokens * D;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache);
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+
+  // int8: fold each block's V scale relative to a reference scale into P
+  float v_ref = 1.f;
+  if (kInt8 && je > jb) {
+    const int ph = table[jb];
+    if (ph >= 0 && ph < a.num_blocks) {
+      const float s = a.v_scale[kv_tile(ph, g, a.num_kv_heads)];
+      if (s > 0.f && s < 3.0e38f) v_ref = s;
+    }
+  }
+  float inv_vref256 = kInt8 ? 256.f / v_ref : 1.f;
+
+  f32x4 acc[NT][ND];
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) acc[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- main loop: this wave takes blocks jb + w, jb + w + W, ... ----------------------
+  // Two register buffers ping-pong: the loads of the next block are in flight while the
+  // current one is consumed.  Lane i of `tchunk` holds the table entry of this wave's
+  // block number (64 * n + i), refilled every 64 blocks.
+  int tchunk = -1;
+  auto refill = [&](int kfirst) {
+    const int jj = jb + w + W * (kfirst + lane);
+    tchunk = jj < je ? table[jj] : -1;
+  };
+  refill(0);
+  auto issue = [&](typename KV::K& kk, typename KV::V& vv, int kidx, int& ph, bool& ok) {
+    const int jx = jb + w + W * kidx;
+    if (kidx > 0 && (kidx & 63) == 0) refill(kidx);
+    ph = jx < je ? __builtin_amdgcn_readlane(tchunk, kidx & 63) : -1;
+    ok = jx < je && ph >= 0 && (int64_t)ph < a.num_blocks;
+    if (ok) {
+      const int64_t tl = kv_tile(ph, g, a.num_kv_heads);
+      KV::load_k(kk, kbase + tl * tile_elems * KV::kElem, row16, grp);
+      KV::load_v(vv, vbase + tl * tile_elems * KV::kElem, row16, grp);
+    }
+  };
+  auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, int ph, bool ok) {
+    if (!ok) return;
+    const int jx = jb + w + W * kidx;
+    float sc = a.scale_log2;
+    float vfac = 1.f;
+    if (kInt8) {
+      const int64_t tl = kv_tile(ph, g, a.num_kv_heads);
+      sc *= a.k_scale[tl];
+      const float vs = a.v_scale[tl];
+      vfac = vs * inv_vref256;
+      if (vfac > 4096.f) {
+        // this block's V scale is far above the reference: move the reference to it so
+        // p * vfac stays well inside the fp16 range
+        const float r = v_ref / vs;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int t = 0; t < ND; ++t) acc[nt][t] *= r;
+        v_ref = vs;
+        inv_vref256 = 256.f / vs;
+        vfac = 256.f;
+      }
+    }
+    const int tok0 = jx * kBlockTokens;
+    const bool need_mask = tok0 + kBlockTokens > lim_min;
+    f32x4 pr[NT];
+    float alpha[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 s = KV::qk(kk, qop[nt]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = s[e] * sc;
+        if (need_mask && tok0 + 4 * grp + e >= lim[nt]) x = -INFINITY;
+        s[e] = x;
+      }
+      float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      bm = wave_max_across_groups(bm);
+      const float mn = fmaxf(m_run[nt], bm);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - mu);
+      m_run[nt] = mn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pr[nt][e] = __builtin_amdgcn_exp2f(s[e] - mu);
+      l_run[nt] = l_run[nt] * alpha[nt] + ((pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]));
+    }
+    bool rescale = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) rescale |= (alpha[nt] != 1.f);
+    if (__any(rescale)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int t = 0; t < ND; ++t) acc[nt][t] *= alpha[nt];
+    }
+    if (tok0 + kBlockTokens > hi) KV::mask_v(vv, hi - tok0, grp);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) KV::pv(acc[nt], vv, pr[nt], vfac);
+  };
+
+  {
+    typename KV::K k0, k1;
+    typename KV::V v0, v1;
+    int ph0 = -1, ph1 = -1;
+    bool ok0 = false, ok1 = false;
+    issue(k0, v0, 0, ph0, ok0);
+    for (int kidx = 0; jb + w + W * kidx < je; kidx += 2) {
+      issue(k1, v1, kidx + 1, ph1, ok1);
+      consume(k0, v0, kidx, ph0, ok0);
+      if (jb + w + W * (kidx + 1) >= je) break;
+      issue(k0, v0, kidx + 2, ph0, ok0);
+      consume(k1, v1, kidx + 1, ph1, ok1);
+    }
+  }
+
+  // ---- per-wave totals ---------------------------------------------------------------
+  const float out_factor = kInt8 ? v_ref * (1.f / 256.f) : 1.f;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    l_run[nt] = wave_sum_across_groups(l_run[nt]);
+    if (kInt8) {
+#pragma unroll
+      for (int t = 0; t < ND; ++t) acc[nt][t] *= out_factor;
+    }
+  }
+
+  // ---- merge the W waves through LDS (wave 0 finishes) -------------------------------
+  if constexpr (W > 1) {
+    __shared__ float sm_m[W - 1][NT * 16];
+    __shared__ float sm_l[W - 1][NT * 16];
+    __shared__ f32x4 sm_acc[W - 1][NT][ND][kWave];
+    if (w > 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (grp == 0) {
+          sm_m[w - 1][nt * 16 + row16] = m_run[nt];
+          sm_l[w - 1][nt * 16 + row16] = l_run[nt];
+        }
+#pragma unroll
+        for (int t = 0; t < ND; ++t) sm_acc[w - 1][nt][t][lane] = acc[nt][t];
+      }
+    }
+    __syncthreads();
+    if (w > 0) return;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float M = m_run[nt];
+#pragma unroll
+      for (int x = 0; x < W - 1; ++x) M = fmaxf(M, sm_m[x][nt * 16 + row16]);
+      const float Mu = (M == -INFINITY) ? 0.f : M;
+      const float f0 = __builtin_amdgcn_exp2f(m_run[nt] - Mu);
+      float lsum = l_run[nt] * f0;
+#pragma unroll
+      for (int t = 0; t < ND; ++t) acc[nt][t] *= f0;
+#pragma unroll
+      for (int x = 0; x < W - 1; ++x) {
+        const float fx = __builtin_amdgcn_exp2f(sm_m[x][nt * 16 + row16] - Mu);
+        lsum += sm_l[x][nt * 16 + row16] * fx;
+#pragma unroll
+        for (int t = 0; t < ND; ++t) acc[nt][t] += sm_acc[x][nt][t][lane] * fx;
+      }
+      m_run[nt] = M;
+      l_run[nt] = lsum;
+    }
+  }
+
+  // ---- normalise and write -----------------------------------------------------------
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = row_base + nt * 16 + row16;
+    if (r >= a.rows) continue;
+    const int i = r / a.group;
+    const int h = g * a.group + r % a.group;
+    const float lsum = l_run[nt];
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float lse = lsum > 0.f ? (m_run[nt] + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+    const int64_t orow = (int64_t)(b * a.num_q_pos + i) * a.num_q_heads + h;
+    float* dst = a.split ? a.out + (orow * a.max_parts + p) * D : a.out + orow * D;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) {
+      *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * grp) = acc[nt][t] * inv;
+    }
+    if (a.split && grp == 0) a.part_lse[orow * a.max_parts + p] = lse;
+  }
+}
+
+template <class KV, int D, int NT, int W>
+int launch_one(const AttnArgs& a, void* stream) {
+  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
+  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg * a.max_parts;
+  const int64_t grid = (units + 7) / 8 * 8;
+  if (grid > 0x7fffffff) return PA_ERR_DIMS;
+  hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W>), dim3((unsigned)grid), dim3(kWave * W), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+template <template <int> class KVT, int D>
+int launch_dim(const AttnArgs& a, void* stream) {
+  constexpr int W = 4;
+  if (a.rows <= 16) return launch_one<KVT<D>, D, 1, W>(a, stream);
+  return launch_one<KVT<D>, D, 2, W>(a, stream);
+}
+
+template <template <int> class KVT>
+int launch_kv(const AttnArgs& a, void* stream) {
+  return a.head_dim == 64 ? launch_dim<KVT, 64>(a, stream) : launch_dim<KVT, 128>(a, stream);
+}
+
+}  // namespace
+
+int launch_attention(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream) {
+  if (q_dtype == PA_F32 && kv_dtype == PA_F32) return launch_kv<F32Kv>(a, stream);
+  if (q_dtype == PA_BF16 && kv_dtype == PA_BF16) return launch_kv<Bf16Kv>(a, stream);
+  if (q_dtype == PA_BF16 && kv_dtype == PA_I8) return launch_kv<I8Kv>(a, stream);
+  return PA_ERR_DTYPE;
+}
+
+}  // namespace pa

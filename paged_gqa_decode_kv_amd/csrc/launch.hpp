@@ -1,0 +1,46 @@
+// Internal launcher interface between the C ABI (api.cpp) and the HIP kernels.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <stdint.h>
+
+namespace pa {
+
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* out;        // normalised output (direct) or per-partition output (split)
+  float* part_lse;   // split only: per-partition log-sum-exp
+  int32_t num_seqs, num_q_heads, num_kv_heads, group, head_dim, max_blocks;
+  int64_t num_blocks;
+  int32_t num_q_pos;        // query positions per sequence
+  int32_t rows;             // query rows per (sequence, KV head) = num_q_pos * group
+  int32_t part_tokens;      // split: tokens per partition
+  int32_t max_parts;        // split: partitions per row in the workspace; direct: 1
+  int32_t split;            // 0: direct, 1: write partials
+  float scale_log2;         // sm_scale * log2(e)
+};
+
+int launch_attention(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream);
+
+int launch_merge(const float* part_out, const float* part_lse, const int32_t* seq_lens,
+                 int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_blocks,
+                 int32_t part_tokens, int32_t max_parts, float* out, float* out_lse,
+                 void* stream);
+
+int launch_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                  int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                  int64_t num_blocks, int elem_bytes, void* k_cache, void* v_cache,
+                  void* stream);
+
+int launch_gather(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                  const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t max_blocks, int64_t num_blocks, int32_t max_len,
+                  int elem_bytes, void* k_out, void* v_out, void* stream);
+
+}  // namespace pa

@@ -1,0 +1,62 @@
+// Device-side building blocks shared by the paged-attention kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlockTokens = 16;  // tokens per KV block (lecture 10: "e.g. 16")
+constexpr int kWave = 64;         // CDNA wavefront width
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ---- block-table translation (the only place the paged address is formed) ----------
+// Logical block j of sequence b lives in physical block tables[b * max_blocks + j]; a
+// (physical block, KV head) tile of K or V is 16 * head_dim consecutive elements.
+__device__ __forceinline__ int64_t kv_tile(int64_t phys, int g, int num_kv_heads) {
+  return phys * num_kv_heads + g;
+}
+// element offset of token `off` (0..15), dim k inside a K tile / a V tile
+__device__ __forceinline__ int k_elem(int off, int k, int head_dim) { return off * head_dim + k; }
+__device__ __forceinline__ int v_elem(int off, int k) { return k * kBlockTokens + off; }
+
+// ---- small numeric helpers ------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// 4 packed int8 codes -> 4 exact fp16 values.  Flipping the sign bit maps code x to the
+// unsigned byte x + 128; placing that byte in the low mantissa bits of the fp16 pattern
+// 0x64XX gives the value 1024 + (x + 128), and subtracting 1152 leaves x exactly.
+__device__ __forceinline__ f16x4 i8x4_to_f16x4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
+  const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
+  return f16x4{a[0], a[1], b[0], b[1]};
+}
+
+__device__ __forceinline__ float wave_max_across_groups(float x) {
+  // lanes l, l^16, l^32, l^48 hold the same row; combine them
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_across_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace pa

@@ -1,0 +1,111 @@
+"""Shared helpers of the GPU parity tests: run a workload through the C ABI and through
+the oracle on the same seeded inputs."""
+import sys
+
+import numpy as np
+import torch
+
+import workloads as W
+from oracle import attention, paging
+
+KIND = {"f32": "f32", "bf16": "bf16", "i8": "i8"}
+TOL = {"f32": 1e-5, "bf16": 2e-3, "i8": 4e-3}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def raw(x):
+    """numpy view of a CPU tensor's stored elements (bf16 as int16 bit patterns)."""
+    if x is None:
+        return None
+    x = x.cpu()
+    return x.view(torch.int16).numpy() if x.dtype == torch.bfloat16 else x.numpy()
+
+
+def dims_of(P, wl):
+    c = wl.cfg
+    return P.make_dims(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                       wl.block_tables.shape[1], wl.k_cache.shape[0], c.q_dtype, c.kv_dtype)
+
+
+class Dev:
+    """Device copies of a workload's tensors."""
+
+    def __init__(self, wl):
+        dev = torch.device("cuda:0")
+        self.q = wl.q.to(dev)
+        self.k_cache = wl.k_cache.to(dev)
+        self.v_cache = wl.v_cache.to(dev)
+        self.k_scale = None if wl.k_scale is None else wl.k_scale.to(dev)
+        self.v_scale = None if wl.v_scale is None else wl.v_scale.to(dev)
+        self.block_tables = wl.block_tables.to(dev)
+        self.seq_lens = wl.seq_lens.to(dev)
+        self.slot_mapping = None if wl.slot_mapping is None else wl.slot_mapping.to(dev)
+        self.k_new = None if wl.k_new is None else wl.k_new.to(dev)
+        self.v_new = None if wl.v_new is None else wl.v_new.to(dev)
+
+
+def gpu_append(P, wl, dv):
+    d = dims_of(P, wl)
+    P.kv_append(d, dv.k_new, dv.v_new, dv.slot_mapping, wl.cfg.batch, dv.k_cache, dv.v_cache)
+
+
+def gpu_attention(P, wl, dv, seq_lens=None, split=None):
+    """Run decode / verify (or split + merge when split=(partition_tokens, max_partitions))."""
+    c = wl.cfg
+    d = dims_of(P, wl)
+    lens = dv.seq_lens if seq_lens is None else seq_lens
+    sm = float(np.float32(wl.sm_scale))
+    out = torch.full((c.batch, c.num_q_pos, c.num_q_heads, c.head_dim), float("nan"),
+                     dtype=torch.float32, device="cuda:0")
+    if split is None:
+        if c.num_q_pos == 1:
+            P.paged_decode_attn(d, dv.q, dv.k_cache, dv.v_cache, dv.k_scale, dv.v_scale,
+                                dv.block_tables, lens, sm, out)
+        else:
+            P.paged_verify_attn(d, c.num_q_pos, dv.q, dv.k_cache, dv.v_cache, dv.k_scale,
+                                dv.v_scale, dv.block_tables, lens, sm, out)
+        return out, None, None
+    pt, maxp = split
+    part_out = torch.full((c.batch, c.num_q_heads, maxp, c.head_dim), float("nan"),
+                          device="cuda:0")
+    part_lse = torch.full((c.batch, c.num_q_heads, maxp), float("nan"), device="cuda:0")
+    out_lse = torch.full((c.batch, c.num_q_heads), float("nan"), device="cuda:0")
+    P.paged_decode_attn_split(d, dv.q, dv.k_cache, dv.v_cache, dv.k_scale, dv.v_scale,
+                              dv.block_tables, lens, sm, pt, maxp, part_out, part_lse)
+    P.lse_merge(d, part_out, part_lse, lens, pt, maxp, out, out_lse)
+    return out, (part_out, part_lse), out_lse
+
+
+def oracle_caches(wl, appended=True):
+    """Host caches as the oracle sees them (after the step's append, by the oracle's own
+    scatter)."""
+    kc, vc = raw(wl.k_cache), raw(wl.v_cache)
+    if appended and wl.slot_mapping is not None:
+        kc, vc = paging.append(kc, vc, raw(wl.k_new), raw(wl.v_new), wl.slot_mapping.numpy())
+    return kc, vc
+
+
+def oracle_attention(wl, kc, vc, seq_lens=None, pairs=None):
+    c = wl.cfg
+    lens = wl.seq_lens.numpy() if seq_lens is None else np.asarray(seq_lens)
+    return attention.paged_attention(raw(wl.q), c.q_dtype, kc, vc, c.kv_dtype,
+                                     wl.block_tables.numpy(), lens, float(np.float32(wl.sm_scale)),
+                                     c.num_q_pos, raw(wl.k_scale), raw(wl.v_scale), pairs=pairs)
+
+
+def max_err(gpu_out, ref, pairs=None, group=None):
+    g = gpu_out.detach().cpu().numpy().astype(np.float64)
+    if pairs is not None:
+        sel = np.zeros(ref.shape, dtype=bool)
+        for b, kv in pairs:
+            sel[b, :, kv * group:(kv + 1) * group] = True
+        diff = np.abs(g[sel] - ref[sel])
+        assert np.isfinite(g[sel]).all(), "non-finite GPU output"
+    else:
+        assert np.isfinite(g).all(), "non-finite GPU output"
+        diff = np.abs(g - ref)
+    return float(diff.max()) if diff.size else 0.0

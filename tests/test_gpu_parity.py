@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same seeded
+inputs.  Bit-exact for append and gather; for attention max |gpu - oracle| within 1e-5
+(fp32 KV), 2e-3 (bf16 KV), 4e-3 (int8 KV)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention, paging
+from _helpers import (TOL, Dev, dims_of, gpu_append, gpu_attention, max_err, oracle_attention,
+                      oracle_caches, raw, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def P():
+    import paged_gqa_decode_kv_amd as P
+    assert torch.cuda.is_available()
+    return P
+
+
+def _bits(x):
+    x = x.detach().cpu()
+    if x.dtype == torch.float32:
+        return x.view(torch.int32)
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16)
+    return x
+
+
+def _small(name, spare=7, **kw):
+    base = dict(lengths=None, pool_blocks=None, shared_groups=0, shared_group_size=0,
+                shared_prefix_tokens=0, lengths_are_cached=False, peaked_fraction=0.0)
+    base.update(kw)
+    return W.generate(W.scaled(name, **base), spare_blocks=spare)
+
+
+def _check_attention(P, wl, tol=None, split=None, pairs=None, append=True):
+    c = wl.cfg
+    tol = TOL[c.kv_dtype] if tol is None else tol
+    say(f"[case] {c.name} B={c.batch} Hq={c.num_q_heads} Hkv={c.num_kv_heads} d={c.head_dim} "
+        f"nq={c.num_q_pos} kv={c.kv_dtype} split={split} seed={wl.meta['seed']}")
+    dv = Dev(wl)
+    if append and wl.slot_mapping is not None:
+        gpu_append(P, wl, dv)
+    out, parts, out_lse = gpu_attention(P, wl, dv, split=split)
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches(wl, appended=append)
+    ref, ref_lse = oracle_attention(wl, kc, vc, pairs=pairs)
+    err = max_err(out, ref, pairs, c.group_size)
+    say(f"  max abs err {err:.3e} (tol {tol:.0e})")
+    assert err <= tol
+    if out_lse is not None:
+        g = out_lse.cpu().numpy()[:, :]
+        r = ref_lse[:, 0, :]
+        sel = np.isfinite(r)
+        if pairs is not None:
+            m = np.zeros(r.shape, bool)
+            for b, kv in pairs:
+                m[b, kv * c.group_size:(kv + 1) * c.group_size] = True
+            sel &= m
+        assert np.all(np.abs(g[sel] - r[sel]) <= 1e-3 * np.maximum(1, np.abs(r[sel])))
+        empty = r == -np.inf
+        if pairs is None:
+            assert np.all(g[empty] == -np.inf)
+    return out, parts, dv
+
+
+# ---- append and gather: bit exact -------------------------------------------------
+@pytest.mark.parametrize("name,kw", [("tiny_fp32", {}),
+                                     ("llama3_8b", dict(batch=9, length_range=(1, 300)))])
+def test_kv_append_bit_exact(P, name, kw):
+    wl = W.generate(W.scaled(name, **kw), spare_blocks=3) if kw else W.generate(name)
+    say(f"[case] append {wl.cfg.name}")
+    dv = Dev(wl)
+    gpu_append(P, wl, dv)
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches(wl, appended=True)
+    assert np.array_equal(raw(dv.k_cache.cpu()).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(raw(dv.v_cache.cpu()).view(np.uint8), vc.view(np.uint8))
+
+
+def test_kv_append_skips_negative_and_out_of_pool_slots(P):
+    wl = W.generate(W.scaled("tiny_fp32", batch=4))
+    say("[case] append with skipped slots")
+    sm = wl.slot_mapping.clone()
+    sm[1] = -1
+    sm[2] = wl.k_cache.shape[0] * 16          # one past the pool
+    dv = Dev(wl)
+    dv.slot_mapping = sm.cuda()
+    d = dims_of(P, wl)
+    P.kv_append(d, dv.k_new, dv.v_new, dv.slot_mapping, 4, dv.k_cache, dv.v_cache)
+    torch.cuda.synchronize()
+    sm_or = sm.numpy().copy()
+    sm_or[2] = -1
+    kc, vc = paging.append(raw(wl.k_cache), raw(wl.v_cache), raw(wl.k_new), raw(wl.v_new), sm_or)
+    assert np.array_equal(raw(dv.k_cache.cpu()).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(raw(dv.v_cache.cpu()).view(np.uint8), vc.view(np.uint8))
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b", "verify_int8"])
+def test_kv_gather_bit_exact(P, name):
+    wl = _small(name, batch=5, length_range=(0, 333), append=False)
+    say(f"[case] gather {name}")
+    dv = Dev(wl)
+    c = wl.cfg
+    maxL = int(wl.seq_lens.max()) + 3
+    fill = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}[c.kv_dtype]
+    k_out = torch.full((c.batch, c.num_kv_heads, maxL, c.head_dim), 7, dtype=fill, device="cuda:0")
+    v_out = k_out.clone()
+    P.kv_gather(dims_of(P, wl), dv.k_cache, dv.v_cache, dv.block_tables, dv.seq_lens, maxL,
+                k_out, v_out)
+    torch.cuda.synchronize()
+    ko, vo = paging.gather(raw(wl.k_cache), raw(wl.v_cache), wl.block_tables.numpy(),
+                           wl.seq_lens.numpy(), raw(k_out.cpu()), raw(v_out.cpu()))
+    assert np.array_equal(raw(k_out.cpu()).view(np.uint8), ko.view(np.uint8))
+    assert np.array_equal(raw(v_out.cpu()).view(np.uint8), vo.view(np.uint8))
+
+
+# ---- attention, small shapes (several tiles, ragged tails, edge cases) ---------------
+def test_tiny_fp32_config(P):
+    wl = W.generate("tiny_fp32")
+    out, _, dv = _check_attention(P, wl)
+    # the same cache read with the pre-append lengths
+    say("[case] tiny_fp32 pre-append lengths")
+    lens = wl.seq_lens - 1
+    out2, _, _ = gpu_attention(P, wl, dv, seq_lens=lens.cuda())
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches(wl)
+    ref, _ = oracle_attention(wl, kc, vc, seq_lens=lens.numpy())
+    assert max_err(out2, ref) <= 1e-5
+
+
+CASES = [
+    # name, overrides
+    ("llama3_8b", dict(batch=6, length_range=(1, 700))),
+    ("llama3_8b", dict(batch=5, length_range=(1, 300), head_dim=64, num_q_heads=16, num_kv_heads=2)),
+    ("llama3_8b", dict(batch=3, length_range=(40, 400), num_q_heads=32, num_kv_heads=1)),   # MQA
+    ("llama3_8b", dict(batch=3, length_range=(40, 400), num_q_heads=4, num_kv_heads=4)),    # MHA
+    ("llama3_8b", dict(batch=2, length_range=(100, 300), num_q_heads=64, num_kv_heads=1)),  # 64 rows
+    ("llama2_70b_prefix", dict(batch=4, length_range=(17, 520))),                          # G = 8
+    ("tiny_fp32", dict(batch=5, length_range=(1, 400), head_dim=128, pool_blocks=None)),
+    ("tiny_fp32", dict(batch=4, length_range=(1, 200), num_q_heads=12, num_kv_heads=4)),
+    ("verify_int8", dict(batch=5, length_range=(6, 600))),
+    ("verify_int8", dict(batch=4, length_range=(1, 300), head_dim=64, num_q_heads=8,
+                         num_kv_heads=2)),
+    ("verify_int8", dict(batch=4, length_range=(1, 300), num_q_pos=1)),
+    ("verify_int8", dict(batch=4, length_range=(1, 40), num_q_pos=3, num_q_heads=16,
+                         num_kv_heads=8)),
+    ("llama3_8b", dict(batch=4, length_range=(1, 200), num_q_pos=4, append=False)),     # bf16 verify
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES)
+def test_attention_small(P, name, kw):
+    wl = _small(name, **kw)
+    _check_attention(P, wl)
+
+
+def test_empty_and_short_sequences(P):
+    wl = _small("llama3_8b", batch=6, lengths=(0, 1, 15, 16, 17, 0), append=False)
+    out, _, _ = _check_attention(P, wl)
+    assert (out[0] == 0).all() and (out[5] == 0).all()
+
+
+def test_verify_rows_that_see_nothing(P):
+    wl = _small("verify_int8", batch=3, lengths=(3, 6, 1))
+    out, _, _ = _check_attention(P, wl)
+    assert (out[0, :3] == 0).all() and (out[2, :5] == 0).all()
+
+
+@pytest.mark.parametrize("split", [(512, 16), (256, 3), (16, 400), (1024, 1)])
+def test_split_merge_small(P, split):
+    wl = _small("long_128k", batch=4, lengths=(3000, 1, 17, 4101), peaked_fraction=0.01)
+    out, (po, pl), _ = _check_attention(P, wl, split=split)
+    # partials against the oracle's per-partition results
+    kc, vc = oracle_caches(wl)
+    c = wl.cfg
+    ro, rl = attention.paged_attention_partitions(
+        raw(wl.q), "bf16", kc, vc, "bf16", wl.block_tables.numpy(), wl.seq_lens.numpy(),
+        float(np.float32(wl.sm_scale)), split[0], split[1])
+    po, pl = po.cpu().numpy(), pl.cpu().numpy()
+    for b, L in enumerate(wl.seq_lens.tolist()):
+        n = attention.partitions_used(L, *split)
+        assert np.abs(po[b, :, :n] - ro[b, 0, :, :n]).max() <= 2e-3
+        assert np.abs(pl[b, :, :n] - rl[b, 0, :, :n]).max() <= 1e-3
+
+
+# ---- invariances, bit for bit --------------------------------------------------------
+def test_block_relabel_and_batch_order_bit_identical(P):
+    wl = _small("llama3_8b", batch=6, length_range=(1, 500), append=False)
+    say("[case] relabel / shuffle invariance")
+    out1, _, _ = gpu_attention(P, wl, Dev(wl))
+    perm = torch.randperm(wl.k_cache.shape[0], generator=torch.Generator().manual_seed(5))
+    out2, _, _ = gpu_attention(P, W.relabel_blocks(wl, perm), Dev(W.relabel_blocks(wl, perm)))
+    bperm = torch.tensor([3, 0, 5, 1, 4, 2])
+    wl3 = W.permute_batch(wl, bperm)
+    out3, _, _ = gpu_attention(P, wl3, Dev(wl3))
+    out4, _, _ = gpu_attention(P, wl, Dev(wl))
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out1), _bits(out2))
+    assert torch.equal(_bits(out1[bperm]), _bits(out3))
+    assert torch.equal(_bits(out1), _bits(out4))
+
+
+def test_split_count_invariance(P):
+    wl = _small("llama3_8b", batch=3, length_range=(2000, 3000), append=False)
+    say("[case] split count invariance")
+    dv = Dev(wl)
+    outs = [gpu_attention(P, wl, dv, split=s)[0] for s in [(256, 16), (512, 8), (2048, 2)]]
+    outs.append(gpu_attention(P, wl, dv)[0])
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert (o - outs[0]).abs().max().item() <= 1e-4
+
+
+# ---- full-size configurations ---------------------------------------------------------
+def test_full_llama3_8b(P):
+    wl = W.generate("llama3_8b")
+    _check_attention(P, wl)
+    _check_attention(P, wl, split=(512, 8))
+
+
+def test_full_llama2_70b_shared_prefix(P):
+    wl = W.generate("llama2_70b_prefix")
+    _check_attention(P, wl)
+    wl2 = W.generate("llama2_70b_prefix", shuffle_batch=True)
+    _check_attention(P, wl2, pairs=[(b, g) for b in range(0, 32, 3) for g in range(8)])
+
+
+def test_full_long_128k(P):
+    wl = W.generate("long_128k")
+    pairs = [(0, 0), (1, 5), (2, 3), (3, 7)]
+    _check_attention(P, wl, split=(2048, 64), pairs=pairs)
+    _check_attention(P, wl, split=(4096, 8), pairs=pairs[:2])   # last partition absorbs the rest
+
+
+def test_full_verify_int8(P):
+    wl = W.generate("verify_int8")
+    _check_attention(P, wl)
