@@ -235,12 +235,13 @@ template <class KV> struct IsInt8 { static constexpr bool value = false; };
 template <int D> struct IsInt8<I8Kv<D>> { static constexpr bool value = true; };
 
 // ---------------------------------------------------------------------------------------
-template <class KV, int D, int NT, int W>
+template <class KV, int D, int NT, int W, int NBUF>
 __global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
   constexpr int ND = D / 16;
   constexpr bool kInt8 = IsInt8<KV>::value;
+  constexpr int kStage = 64;  // table entries staged in LDS per wave
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int row16 = lane & 15;
   const int grp = lane >> 4;
 
@@ -269,11 +270,13 @@ __global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
   }
   const int jb = lo / kBlockTokens;
   const int je = (hi + kBlockTokens - 1) / kBlockTokens;
+  // this wave's blocks: jb + w + W * k for k in [0, nk)
+  const int nk = je - jb - w > 0 ? (je - jb - w + W - 1) / W : 0;
 
   // ---- query rows handled by this lane -----------------------------------------------
   typename KV::Q qop[NT];
   int lim[NT];  // tokens [lo, lim) are visible to this lane's row
-  int row_base = rg * 16 * NT;
+  const int row_base = rg * 16 * NT;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = row_base + nt * 16 + row16;
@@ -281,8 +284,7 @@ __global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
     const int i = valid ? r / a.group : 0;
     const int h = g * a.group + (valid ? r % a.group : 0);
     const int64_t qoff = ((int64_t)(b * a.num_q_pos + i) * a.num_q_heads + h) * D;
-    KV::load_q(qop[nt], static_cast<const uint8_t*>(a.q) + qoff * KV::kQElem,
-               valid, grp);
+    KV::load_q(qop[nt], static_cast<const uint8_t*>(a.q) + qoff * KV::kQElem, valid, grp);
     int lam = valid ? L - a.num_q_pos + 1 + i : L;
     lam = lam < 0 ? 0 : lam;
     lim[nt] = lam < hi ? lam : hi;
@@ -296,18 +298,63 @@ __global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
     lim_min = lam0 < hi ? lam0 : hi;
   }
 
-  const size_t tile_elems = (size_t)kBlockTokens * D;
+  const size_t tile_bytes = (size_t)kBlockTokens * D * KV::kElem;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache);
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
 
-  // int8: fold each block's V scale relative to a reference scale into P
+  // ---- per-wave LDS staging of block-table entries (and int8 scales) -------------------
+  // Lane i fetches the entry of this wave's block k0 + i; the loop then reads them back
+  // from LDS, so no dependent HBM load sits between consecutive tile loads.
+  __shared__ int s_tbl[W][kStage];
+  __shared__ float s_ks[W][kInt8 ? kStage : 1];
+  __shared__ float s_vs[W][kInt8 ? kStage : 1];
+  auto stage = [&](int k0) {
+    const int k = k0 + lane;
+    int ph = -1;
+    if (k < nk) {
+      ph = table[jb + w + W * k];
+      if (ph < 0 || (int64_t)ph >= a.num_blocks) ph = -1;
+    }
+    s_tbl[w][lane] = ph;
+    if constexpr (kInt8) {
+      float ks = 0.f, vs = 0.f;
+      if (ph >= 0) {
+        ks = a.k_scale[kv_tile(ph, g, a.num_kv_heads)];
+        vs = a.v_scale[kv_tile(ph, g, a.num_kv_heads)];
+      }
+      s_ks[w][lane] = ks;
+      s_vs[w][lane] = vs;
+    }
+  };
+  stage(0);
+  auto lds_uniform_f = [](const float& x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+  };
+  // block k of this wave: physical block (-1 = none) and, for int8, its K and V scales
+  struct Slot {
+    int ph;
+    float ks, vs;
+  };
+  auto slot_at = [&](int k) -> Slot {
+    Slot sl{-1, 0.f, 0.f};
+    if (k < nk) {
+      const int si = k & (kStage - 1);
+      sl.ph = __builtin_amdgcn_readfirstlane(s_tbl[w][si]);
+      if constexpr (kInt8) {
+        sl.ks = lds_uniform_f(s_ks[w][si]);
+        sl.vs = lds_uniform_f(s_vs[w][si]);
+      }
+    }
+    return sl;
+  };
+
+  // int8: each block's V scale is folded into P relative to a reference scale
   float v_ref = 1.f;
-  if (kInt8 && je > jb) {
-    const int ph = table[jb];
-    if (ph >= 0 && ph < a.num_blocks) {
-      const float s = a.v_scale[kv_tile(ph, g, a.num_kv_heads)];
-      if (s > 0.f && s < 3.0e38f) v_ref = s;
+  if constexpr (kInt8) {
+    if (nk > 0) {
+      const float s0 = lds_uniform_f(s_vs[w][0]);
+      if (s0 > 0.f && s0 < 3.0e38f) v_ref = s0;
     }
   }
   float inv_vref256 = kInt8 ? 256.f / v_ref : 1.f;
@@ -322,36 +369,23 @@ __global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
     for (int t = 0; t < ND; ++t) acc[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- main loop: this wave takes blocks jb + w, jb + w + W, ... ----------------------
-  // Two register buffers ping-pong: the loads of the next block are in flight while the
-  // current one is consumed.  Lane i of `tchunk` holds the table entry of this wave's
-  // block number (64 * n + i), refilled every 64 blocks.
-  int tchunk = -1;
-  auto refill = [&](int kfirst) {
-    const int jj = jb + w + W * (kfirst + lane);
-    tchunk = jj < je ? table[jj] : -1;
+  // Loads are issued unconditionally: a slot with no block (past the end, or a table
+  // entry outside the pool) reads tile (0, g), which is always inside the pool, and is
+  // then not consumed.  Straight-line loads keep the wait counters exact, so NBUF - 1
+  // blocks stay in flight while one is consumed.
+  auto issue = [&](typename KV::K& kk, typename KV::V& vv, int ph) {
+    const int64_t tl = kv_tile(ph >= 0 ? ph : 0, g, a.num_kv_heads);
+    KV::load_k(kk, kbase + tl * tile_bytes, row16, grp);
+    KV::load_v(vv, vbase + tl * tile_bytes, row16, grp);
   };
-  refill(0);
-  auto issue = [&](typename KV::K& kk, typename KV::V& vv, int kidx, int& ph, bool& ok) {
-    const int jx = jb + w + W * kidx;
-    if (kidx > 0 && (kidx & 63) == 0) refill(kidx);
-    ph = jx < je ? __builtin_amdgcn_readlane(tchunk, kidx & 63) : -1;
-    ok = jx < je && ph >= 0 && (int64_t)ph < a.num_blocks;
-    if (ok) {
-      const int64_t tl = kv_tile(ph, g, a.num_kv_heads);
-      KV::load_k(kk, kbase + tl * tile_elems * KV::kElem, row16, grp);
-      KV::load_v(vv, vbase + tl * tile_elems * KV::kElem, row16, grp);
-    }
-  };
-  auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, int ph, bool ok) {
-    if (!ok) return;
+  auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, const Slot& sl) {
+    if (sl.ph < 0) return;
     const int jx = jb + w + W * kidx;
     float sc = a.scale_log2;
     float vfac = 1.f;
-    if (kInt8) {
-      const int64_t tl = kv_tile(ph, g, a.num_kv_heads);
-      sc *= a.k_scale[tl];
-      const float vs = a.v_scale[tl];
+    if constexpr (kInt8) {
+      sc *= sl.ks;
+      const float vs = sl.vs;
       vfac = vs * inv_vref256;
       if (vfac > 4096.f) {
         // this block's V scale is far above the reference: move the reference to it so
@@ -404,17 +438,24 @@ __global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
   };
 
   {
-    typename KV::K k0, k1;
-    typename KV::V v0, v1;
-    int ph0 = -1, ph1 = -1;
-    bool ok0 = false, ok1 = false;
-    issue(k0, v0, 0, ph0, ok0);
-    for (int kidx = 0; jb + w + W * kidx < je; kidx += 2) {
-      issue(k1, v1, kidx + 1, ph1, ok1);
-      consume(k0, v0, kidx, ph0, ok0);
-      if (jb + w + W * (kidx + 1) >= je) break;
-      issue(k0, v0, kidx + 2, ph0, ok0);
-      consume(k1, v1, kidx + 1, ph1, ok1);
+    typename KV::K kb[NBUF];
+    typename KV::V vb[NBUF];
+    Slot sb[NBUF];
+#pragma unroll
+    for (int s = 0; s < NBUF - 1; ++s) {
+      sb[s] = slot_at(s);
+      issue(kb[s], vb[s], sb[s].ph);
+    }
+    for (int k = 0; k < nk; k += NBUF) {
+#pragma unroll
+      for (int s = 0; s < NBUF; ++s) {
+        const int kn = k + s + NBUF - 1;  // block issued now, consumed NBUF - 1 steps later
+        const int sn = (s + NBUF - 1) % NBUF;
+        if ((kn & (kStage - 1)) == 0 && kn < nk) stage(kn);
+        sb[sn] = slot_at(kn);
+        issue(kb[sn], vb[sn], sb[sn].ph);
+        consume(kb[s], vb[s], k + s, sb[s]);
+      }
     }
   }
 
@@ -489,13 +530,13 @@ __global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
   }
 }
 
-template <class KV, int D, int NT, int W>
+template <class KV, int D, int NT, int W, int NBUF>
 int launch_one(const AttnArgs& a, void* stream) {
   const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg * a.max_parts;
   const int64_t grid = (units + 7) / 8 * 8;
   if (grid > 0x7fffffff) return PA_ERR_DIMS;
-  hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W>), dim3((unsigned)grid), dim3(kWave * W), 0,
+  hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF>), dim3((unsigned)grid), dim3(kWave * W), 0,
                      static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -503,8 +544,8 @@ int launch_one(const AttnArgs& a, void* stream) {
 template <template <int> class KVT, int D>
 int launch_dim(const AttnArgs& a, void* stream) {
   constexpr int W = 4;
-  if (a.rows <= 16) return launch_one<KVT<D>, D, 1, W>(a, stream);
-  return launch_one<KVT<D>, D, 2, W>(a, stream);
+  if (a.rows <= 16) return launch_one<KVT<D>, D, 1, W, 3>(a, stream);
+  return launch_one<KVT<D>, D, 2, W, 2>(a, stream);
 }
 
 template <template <int> class KVT>

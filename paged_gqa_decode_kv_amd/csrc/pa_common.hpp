@@ -47,16 +47,52 @@ __device__ __forceinline__ f16x4 i8x4_to_f16x4(uint32_t w) {
   return f16x4{a[0], a[1], b[0], b[1]};
 }
 
+// Lanes l, l^16, l^32 and l^48 hold the same query row.  gfx950's permlane swaps exchange
+// 16-lane rows (xor 16) and 32-lane halves (xor 32) on the VALU, without an LDS round trip:
+// given two registers that both hold x, v_permlane16_swap leaves rows (0,0,2,2) of x in
+// the first and rows (1,1,3,3) in the second, so every lane ends with its own value and
+// its partner's; v_permlane32_swap does the same for the two halves.
+// (The two results are copied to scalars before any bit cast: a bit cast applied directly
+// to an element of the returned vector reads element 0.)
+__device__ __forceinline__ void xor16_pair(float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void xor32_pair(float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float xor16_pair_max(float x) {
+  float a, b;
+  xor16_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float xor32_pair_max(float x) {
+  float a, b;
+  xor32_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float xor16_pair_sum(float x) {
+  float a, b;
+  xor16_pair(x, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float xor32_pair_sum(float x) {
+  float a, b;
+  xor32_pair(x, a, b);
+  return a + b;
+}
 __device__ __forceinline__ float wave_max_across_groups(float x) {
-  // lanes l, l^16, l^32, l^48 hold the same row; combine them
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  return xor32_pair_max(xor16_pair_max(x));
 }
 __device__ __forceinline__ float wave_sum_across_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  return xor32_pair_sum(xor16_pair_sum(x));
 }
 
 }  // namespace pa
