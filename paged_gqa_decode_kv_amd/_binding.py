@@ -36,10 +36,10 @@ class pa_dims(ctypes.Structure):
                 ("kv_dtype", ctypes.c_int32)]
 
 
-def _load():
-    if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is not built; run `python -m paged_gqa_decode_kv_amd.build`")
-    lib = ctypes.CDLL(_LIB_PATH)
+def _load(path=_LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m paged_gqa_decode_kv_amd.build`")
+    lib = ctypes.CDLL(path)
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     D = ctypes.POINTER(pa_dims)
     sig = {
