@@ -64,7 +64,8 @@ enum {
   PA_ERR_BLOCK_SIZE = -5, /* block_size is not 16                                          */
   PA_ERR_PARTITION = -6,  /* partition_tokens not a positive multiple of 16, or
                              max_partitions < 1                                            */
-  PA_ERR_LAUNCH = -7      /* a kernel launch failed                                        */
+  PA_ERR_LAUNCH = -7,     /* a kernel launch failed (or a device query failed)             */
+  PA_ERR_WORKSPACE = -8   /* workspace smaller than the size query returns, or misaligned  */
 };
 
 /* Shapes and element types shared by every call. */
@@ -170,6 +171,41 @@ size_t paged_split_workspace_bytes(const pa_dims* dims, int32_t max_partitions);
 int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* seq_lens, int32_t max_len,
               void* k_out, void* v_out, void* stream);
+
+/*
+ * paged_attn_balanced -- decode (nq = 1) or causal verify (nq > 1) attention with the work
+ * dealt evenly over num_workgroups workgroups, whatever the spread of sequence lengths.
+ * Every (KV head, query-row tile, sequence) segment of the batch is laid out, block after
+ * block, in one flat list (KV head outermost, sequence innermost) and workgroup w takes the
+ * contiguous slice [w * per, (w + 1) * per), per = ceil(total blocks / num_workgroups).  A
+ * segment cut by slice boundaries is attended piecewise and its pieces are recombined
+ * with the log-sum-exp identity (see lse_merge), inside this call: two kernels are
+ * enqueued on `stream` (attention, then merge).
+ *   num_q_pos    nq >= 1; q [B][nq][Hq][head_dim]; out [B][nq][Hq][head_dim] fp32
+ *   out_lse      device, [B][nq][Hq] fp32 (natural log; -inf for a row that sees no token),
+ *                or NULL
+ *   num_workgroups >= 1; paged_attn_balanced_workgroups gives the number that runs
+ *                concurrently on the current device, which is the intended value
+ *   workspace    device, >= paged_attn_balanced_workspace_bytes(dims, nq, num_workgroups)
+ *                bytes, 16-byte aligned; contents need no initialisation and are scratch
+ *                for the duration of the call (calls sharing one workspace must be ordered)
+ * B may be at most 2048 (PA_ERR_DIMS otherwise).  Other arguments as paged_verify_attn.
+ */
+int paged_attn_balanced(const pa_dims* dims, int32_t num_q_pos, const void* q,
+                        const void* k_cache, const void* v_cache, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables,
+                        const int32_t* seq_lens, float sm_scale, int32_t num_workgroups,
+                        void* workspace, size_t workspace_bytes, float* out, float* out_lse,
+                        void* stream);
+
+/* Workspace bytes paged_attn_balanced needs (0 if the arguments are invalid). */
+size_t paged_attn_balanced_workspace_bytes(const pa_dims* dims, int32_t num_q_pos,
+                                           int32_t num_workgroups);
+
+/* Workgroups of the balanced kernel that are resident at once on the current HIP device
+ * (compute units x workgroups per unit); a negative PA_ERR_* code on failure.  This call
+ * queries the device (HIP calls), unlike the argument checks. */
+int paged_attn_balanced_workgroups(const pa_dims* dims, int32_t num_q_pos);
 
 /* Text for a status code (static storage). */
 const char* paged_status_string(int status);

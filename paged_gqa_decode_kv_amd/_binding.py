@@ -16,7 +16,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_a
 PA_F32, PA_BF16, PA_I8 = 0, 1, 2
 PA_OK = 0
 PA_ERR_NULL, PA_ERR_DIMS, PA_ERR_DTYPE, PA_ERR_HEAD_DIM = -1, -2, -3, -4
-PA_ERR_BLOCK_SIZE, PA_ERR_PARTITION, PA_ERR_LAUNCH = -5, -6, -7
+PA_ERR_BLOCK_SIZE, PA_ERR_PARTITION, PA_ERR_LAUNCH, PA_ERR_WORKSPACE = -5, -6, -7, -8
 
 _DTYPE_CODE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8,
                "f32": PA_F32, "bf16": PA_BF16, "i8": PA_I8}
@@ -38,7 +38,7 @@ class pa_dims(ctypes.Structure):
 
 def _load(path=_LIB_PATH):
     if not os.path.exists(path):
-        raise ImportError(f"{path} is not built; run `python -m paged_gqa_decode_kv_amd.build`")
+        raise ImportError(f"{path} is not built; run `python paged_gqa_decode_kv_amd/build.py`")
     lib = ctypes.CDLL(path)
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     D = ctypes.POINTER(pa_dims)
@@ -49,6 +49,8 @@ def _load(path=_LIB_PATH):
         "paged_decode_attn_split": [D, P, P, P, P, P, P, P, F32, I32, I32, P, P, P],
         "lse_merge": [D, P, P, P, I32, I32, P, P, P],
         "kv_gather": [D, P, P, P, P, I32, P, P, P],
+        "paged_attn_balanced": [D, I32, P, P, P, P, P, P, P, F32, I32, P, ctypes.c_size_t, P, P, P],
+        "paged_attn_balanced_workgroups": [D, I32],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -56,6 +58,8 @@ def _load(path=_LIB_PATH):
         fn.restype = ctypes.c_int
     lib.paged_split_workspace_bytes.argtypes = [D, I32]
     lib.paged_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.paged_attn_balanced_workspace_bytes.argtypes = [D, I32, I32]
+    lib.paged_attn_balanced_workspace_bytes.restype = ctypes.c_size_t
     lib.paged_status_string.argtypes = [ctypes.c_int]
     lib.paged_status_string.restype = ctypes.c_char_p
     return lib
@@ -141,3 +145,23 @@ def kv_gather(dims, k_cache, v_cache, block_tables, seq_lens, max_len, k_out, v_
     _check("kv_gather", lib.kv_gather(ctypes.byref(dims), _p(k_cache), _p(v_cache),
                                       _p(block_tables), _p(seq_lens), max_len, _p(k_out),
                                       _p(v_out), _stream(stream)))
+
+
+def paged_attn_balanced_workgroups(dims, num_q_pos):
+    n = lib.paged_attn_balanced_workgroups(ctypes.byref(dims), num_q_pos)
+    _check("paged_attn_balanced_workgroups", n if n < 0 else PA_OK)
+    return n
+
+
+def paged_attn_balanced_workspace_bytes(dims, num_q_pos, num_workgroups):
+    return lib.paged_attn_balanced_workspace_bytes(ctypes.byref(dims), num_q_pos, num_workgroups)
+
+
+def paged_attn_balanced(dims, num_q_pos, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                        seq_lens, sm_scale, num_workgroups, workspace, out, out_lse=None,
+                        stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("paged_attn_balanced", lib.paged_attn_balanced(
+        ctypes.byref(dims), num_q_pos, _p(q), _p(k_cache), _p(v_cache), _p(k_scale), _p(v_scale),
+        _p(block_tables), _p(seq_lens), sm_scale, num_workgroups, _p(workspace), nbytes, _p(out),
+        _p(out_lse), _stream(stream)))

@@ -1,6 +1,7 @@
 """Build libpaged_attn.so in-tree with hipcc for gfx950.
 
-    python -m paged_gqa_decode_kv_amd.build        (or paged_gqa_decode_kv_amd.build.build())
+    python paged_gqa_decode_kv_amd/build.py        (a script: the package itself imports the
+                                                    library, so it cannot build it)
 
 Each source is compiled to an object under _build/ (in parallel), then linked into
 paged_gqa_decode_kv_amd/libpaged_attn.so.  A GPU is not needed: hipcc cross-compiles.

@@ -72,6 +72,35 @@ pa::AttnArgs make_args(const pa_dims* d, int32_t nq, const void* q, const void* 
 
 int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_BF16 ? 2 : 1); }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the balanced mode: block-count prefix, then partial lse, then partial rows.
+struct BalancedLayout {
+  size_t prefix, lse, out, total;
+};
+BalancedLayout balanced_layout(const pa_dims* d, int32_t nq, int32_t num_workgroups) {
+  const int64_t rows = (int64_t)nq * (d->num_q_heads / d->num_kv_heads);
+  const int rt = pa::balanced_row_tile((int32_t)rows);
+  const int64_t nrg = (rows + rt - 1) / rt;
+  const int64_t npid = (int64_t)num_workgroups + (int64_t)d->num_kv_heads * nrg * d->num_seqs;
+  BalancedLayout l;
+  l.prefix = 0;
+  l.lse = align256(((size_t)d->num_seqs + 1) * sizeof(int32_t));
+  l.out = l.lse + align256((size_t)npid * rt * sizeof(float));
+  l.total = l.out + (size_t)npid * rt * d->head_dim * sizeof(float);
+  return l;
+}
+
+int check_balanced(const pa_dims* d, int32_t nq, int32_t num_workgroups) {
+  int st = check_dims(d);
+  if (st != PA_OK) return st;
+  if (nq < 1 || num_workgroups < 1 || d->num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_DIMS;
+  if ((int64_t)nq * (d->num_q_heads / d->num_kv_heads) > INT_MAX) return PA_ERR_DIMS;
+  // block positions in the flat list of one KV head are int32 inside the kernel
+  if ((int64_t)d->num_seqs * d->max_blocks_per_seq > INT_MAX) return PA_ERR_DIMS;
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -168,6 +197,47 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
                            stream);
 }
 
+int paged_attn_balanced_workgroups(const pa_dims* dims, int32_t num_q_pos) {
+  int st = check_balanced(dims, num_q_pos, 1);
+  if (st != PA_OK) return st;
+  st = check_attn_types(dims);
+  if (st != PA_OK) return st;
+  return pa::balanced_workgroups(dims->q_dtype, dims->kv_dtype, dims->head_dim,
+                                 num_q_pos * (dims->num_q_heads / dims->num_kv_heads));
+}
+
+size_t paged_attn_balanced_workspace_bytes(const pa_dims* dims, int32_t num_q_pos,
+                                           int32_t num_workgroups) {
+  if (check_balanced(dims, num_q_pos, num_workgroups) != PA_OK) return 0;
+  return balanced_layout(dims, num_q_pos, num_workgroups).total;
+}
+
+int paged_attn_balanced(const pa_dims* dims, int32_t num_q_pos, const void* q,
+                        const void* k_cache, const void* v_cache, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables,
+                        const int32_t* seq_lens, float sm_scale, int32_t num_workgroups,
+                        void* workspace, size_t workspace_bytes, float* out, float* out_lse,
+                        void* stream) {
+  int st = check_attn_inputs(dims, q, k_cache, v_cache, k_scale, v_scale, block_tables, seq_lens);
+  if (st != PA_OK) return st;
+  st = check_balanced(dims, num_q_pos, num_workgroups);
+  if (st != PA_OK) return st;
+  if (!out || !workspace) return PA_ERR_NULL;
+  const BalancedLayout l = balanced_layout(dims, num_q_pos, num_workgroups);
+  if (workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return PA_ERR_WORKSPACE;
+  pa::AttnArgs a = make_args(dims, num_q_pos, q, k_cache, v_cache, k_scale, v_scale,
+                             block_tables, seq_lens, sm_scale);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.num_workgroups = num_workgroups;
+  a.ws_prefix = reinterpret_cast<int32_t*>(ws + l.prefix);
+  a.ws_lse = reinterpret_cast<float*>(ws + l.lse);
+  a.ws_out = reinterpret_cast<float*>(ws + l.out);
+  a.out = out;
+  a.ws_out_lse = out_lse;
+  return pa::launch_balanced(a, dims->q_dtype, dims->kv_dtype, out, out_lse, stream);
+}
+
 const char* paged_status_string(int status) {
   switch (status) {
     case PA_OK: return "ok";
@@ -178,6 +248,7 @@ const char* paged_status_string(int status) {
     case PA_ERR_BLOCK_SIZE: return "block_size must be 16";
     case PA_ERR_PARTITION: return "partition_tokens must be a positive multiple of 16 and max_partitions >= 1";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_WORKSPACE: return "workspace too small or not 16-byte aligned";
     default: return "unknown status";
   }
 }

@@ -249,8 +249,19 @@ template <class KV> struct IsInt8 { static constexpr bool value = false; };
 template <int D> struct IsInt8<I8Kv<D>> { static constexpr bool value = true; };
 
 // ---------------------------------------------------------------------------------------
+// Where a unit writes its rows.
+enum OutMode { kDirect = 0, kSplit = 1, kBalanced = 2 };
+
+// One unit of work: query rows [16*NT*rg, 16*NT*(rg+1)) of KV head g of sequence b, over
+// that sequence's tokens [lo, hi) (lo a multiple of 16).  The W waves of the workgroup
+// take interleaved blocks; their partial results are merged through LDS and wave 0
+// writes the normalised rows (and, except in direct mode, their log-sum-exp).
+// `slot` is the partition index (split mode) or the partial id (balanced mode).
+// Every wave of the workgroup must call this together (it contains barriers).
 template <class KV, int D, int NT, int W, int NBUF>
-__global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
+__device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int b, int g, int rg,
+                                            int L, int lo, int hi, int64_t slot,
+                                            float* out_lse = nullptr) {
   constexpr int ND = D / 16;
   constexpr bool kInt8 = IsInt8<KV>::value;
   constexpr int kStage = 64;  // table entries staged in LDS per wave
@@ -259,29 +270,6 @@ __global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
   const int row16 = lane & 15;
   const int grp = lane >> 4;
 
-  // ---- unit of work, with XCD-aware remapping of the workgroup id ----------------------
-  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
-  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg * a.max_parts;
-  const int64_t per_xcd = gridDim.x / 8;
-  const int64_t u = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (u >= units) return;
-  const int p = (int)(u % a.max_parts);
-  int64_t rest = u / a.max_parts;
-  const int rg = (int)(rest % nrg);
-  rest /= nrg;
-  const int b = (int)(rest % a.num_seqs);
-  const int g = (int)(rest / a.num_seqs);
-
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.max_blocks * kBlockTokens ? a.max_blocks * kBlockTokens : L);
-  int lo = 0, hi = L;
-  if (a.split) {
-    int nparts = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 0;
-    if (nparts > a.max_parts) nparts = a.max_parts;
-    if (p >= nparts) return;
-    lo = p * a.part_tokens;
-    hi = (p == nparts - 1) ? L : lo + a.part_tokens;
-  }
   const int jb = lo / kBlockTokens;
   const int je = (hi + kBlockTokens - 1) / kBlockTokens;
   // this wave's blocks: jb + w + W * k for k in [0, nk)
@@ -501,33 +489,38 @@ __global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    if (w > 0) return;
+    if (w == 0) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float M = m_run[nt];
+      for (int nt = 0; nt < NT; ++nt) {
+        float M = m_run[nt];
 #pragma unroll
-      for (int x = 0; x < W - 1; ++x) M = fmaxf(M, sm_m[x][nt * 16 + row16]);
-      const float Mu = (M == -INFINITY) ? 0.f : M;
-      const float f0 = __builtin_amdgcn_exp2f(m_run[nt] - Mu);
-      float lsum = l_run[nt] * f0;
+        for (int x = 0; x < W - 1; ++x) M = fmaxf(M, sm_m[x][nt * 16 + row16]);
+        const float Mu = (M == -INFINITY) ? 0.f : M;
+        const float f0 = __builtin_amdgcn_exp2f(m_run[nt] - Mu);
+        float lsum = l_run[nt] * f0;
 #pragma unroll
-      for (int t = 0; t < ND; ++t) acc[nt][t] *= f0;
+        for (int t = 0; t < ND; ++t) acc[nt][t] *= f0;
 #pragma unroll
-      for (int x = 0; x < W - 1; ++x) {
-        const float fx = __builtin_amdgcn_exp2f(sm_m[x][nt * 16 + row16] - Mu);
-        lsum += sm_l[x][nt * 16 + row16] * fx;
+        for (int x = 0; x < W - 1; ++x) {
+          const float fx = __builtin_amdgcn_exp2f(sm_m[x][nt * 16 + row16] - Mu);
+          lsum += sm_l[x][nt * 16 + row16] * fx;
 #pragma unroll
-        for (int t = 0; t < ND; ++t) acc[nt][t] += sm_acc[x][nt][t][lane] * fx;
+          for (int t = 0; t < ND; ++t) acc[nt][t] += sm_acc[x][nt][t][lane] * fx;
+        }
+        m_run[nt] = M;
+        l_run[nt] = lsum;
       }
-      m_run[nt] = M;
-      l_run[nt] = lsum;
     }
+    // LDS (merge buffers and the staged table) is reused by the workgroup's next unit
+    __syncthreads();
+    if (w != 0) return;
   }
 
   // ---- normalise and write -----------------------------------------------------------
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int r = row_base + nt * 16 + row16;
+    const int rl = nt * 16 + row16;  // row within the row group
+    const int r = row_base + rl;
     if (r >= a.rows) continue;
     const int i = r / a.group;
     const int h = g * a.group + r % a.group;
@@ -535,12 +528,132 @@ __global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const float lse = lsum > 0.f ? (m_run[nt] + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
     const int64_t orow = (int64_t)(b * a.num_q_pos + i) * a.num_q_heads + h;
-    float* dst = a.split ? a.out + (orow * a.max_parts + p) * D : a.out + orow * D;
+    float* dst;
+    float* lse_dst = nullptr;
+    if (mode == kDirect) {
+      dst = a.out + orow * D;
+      if (out_lse != nullptr) lse_dst = out_lse + orow;
+    } else if (mode == kSplit) {
+      dst = a.out + (orow * a.max_parts + slot) * D;
+      lse_dst = a.part_lse + orow * a.max_parts + slot;
+    } else {
+      dst = a.ws_out + (slot * 16 * NT + rl) * D;
+      lse_dst = a.ws_lse + slot * 16 * NT + rl;
+    }
 #pragma unroll
     for (int t = 0; t < ND; ++t) {
       *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * grp) = acc[nt][t] * inv;
     }
-    if (a.split && grp == 0) a.part_lse[orow * a.max_parts + p] = lse;
+    if (lse_dst != nullptr && grp == 0) *lse_dst = lse;
+  }
+}
+
+__device__ __forceinline__ int clamp_len(int L, int max_blocks) {
+  return L < 0 ? 0 : (L > max_blocks * kBlockTokens ? max_blocks * kBlockTokens : L);
+}
+
+// Workgroup id -> logical unit, so that consecutive units run on the same XCD (the
+// dispatcher deals workgroups to the 8 XCDs round-robin).  gridDim.x is a multiple of 8.
+__device__ __forceinline__ int64_t xcd_logical_id() {
+  const int64_t per_xcd = gridDim.x / 8;
+  return (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+}
+
+// Direct and split modes: one unit per (KV head, sequence, row group, partition).
+template <class KV, int D, int NT, int W, int NBUF>
+__global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
+  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
+  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg * a.max_parts;
+  const int64_t u = xcd_logical_id();
+  if (u >= units) return;
+  const int p = (int)(u % a.max_parts);
+  int64_t rest = u / a.max_parts;
+  const int rg = (int)(rest % nrg);
+  rest /= nrg;
+  const int b = (int)(rest % a.num_seqs);
+  const int g = (int)(rest / a.num_seqs);
+  const int L = clamp_len(a.seq_lens[b], a.max_blocks);
+  int lo = 0, hi = L;
+  if (a.split) {
+    int nparts = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 0;
+    if (nparts > a.max_parts) nparts = a.max_parts;
+    if (p >= nparts) return;
+    lo = p * a.part_tokens;
+    hi = (p == nparts - 1) ? L : lo + a.part_tokens;
+  }
+  attend_unit<KV, D, NT, W, NBUF>(a, a.split ? kSplit : kDirect, b, g, rg, L, lo, hi, p);
+}
+
+// Balanced mode.  All (segment, block) pairs of the batch are laid out in one flat list --
+// segment j = (KV head g, row group rg, sequence b) in order j = (g * nrg + rg) * B + b,
+// holding ceil(L_b / 16) blocks -- and workgroup w takes the contiguous slice
+// [w * per, (w + 1) * per) with per = ceil(total / num_workgroups).  Every workgroup
+// therefore streams the same number of blocks whatever the spread of sequence lengths.
+// A segment that lies wholly inside one slice is written out directly; otherwise each
+// piece becomes a partial result at partial id w + j (unique: along the slices both w and
+// j only grow) and a merge kernel combines the pieces of each cut segment.
+template <class KV, int D, int NT, int W, int NBUF>
+__global__ __launch_bounds__(kWave* W) void paged_attn_balanced_kernel(AttnArgs a) {
+  __shared__ int s_pref[kMaxBalancedSeqs + 1];
+  const int64_t wid = xcd_logical_id();
+  if (wid >= a.num_workgroups) return;
+  const int B = a.num_seqs;
+  // prefix over sequences of their block counts, by the whole workgroup
+  __shared__ int s_scan[kWave * W];
+  int carry = 0;
+  if (threadIdx.x == 0) s_pref[0] = 0;
+  for (int c0 = 0; c0 < B; c0 += kWave * W) {
+    const int bb = c0 + (int)threadIdx.x;
+    const int nb = bb < B ? (clamp_len(a.seq_lens[bb], a.max_blocks) + kBlockTokens - 1) / kBlockTokens : 0;
+    s_scan[threadIdx.x] = nb;
+    __syncthreads();
+    for (int off = 1; off < kWave * W; off <<= 1) {
+      const int t = threadIdx.x >= (unsigned)off ? s_scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      s_scan[threadIdx.x] += t;
+      __syncthreads();
+    }
+    if (bb < B) s_pref[bb + 1] = carry + s_scan[threadIdx.x];
+    carry += s_scan[kWave * W - 1];
+    __syncthreads();
+  }
+  if (wid == 0) {
+    for (int k = threadIdx.x; k <= B; k += kWave * W) a.ws_prefix[k] = s_pref[k];
+  }
+  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
+  const int64_t T = s_pref[B];
+  const int64_t total = T * a.num_kv_heads * nrg;
+  const int64_t per = (total + a.num_workgroups - 1) / a.num_workgroups;
+  int64_t x = wid * per;
+  const int64_t x1 = x + per < total ? x + per : total;
+  while (x < x1) {
+    const int64_t gr = x / T;
+    const int r = (int)(x - gr * T);
+    // sequence holding flat block r: largest b with s_pref[b] <= r (then r < s_pref[b + 1])
+    int lo_b = 0, hi_b = B - 1;
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if (s_pref[mid] <= r) lo_b = mid; else hi_b = mid - 1;
+    }
+    const int b = lo_b;
+    const int64_t seg_end = gr * T + s_pref[b + 1];
+    const int64_t xe = seg_end < x1 ? seg_end : x1;
+    const int g = (int)(gr / nrg);
+    const int rg = (int)(gr % nrg);
+    const int L = clamp_len(a.seq_lens[b], a.max_blocks);
+    const int lb = r - s_pref[b];
+    const int lo = lb * kBlockTokens;
+    const int hi_t = (lb + (int)(xe - x)) * kBlockTokens;
+    const int hi = hi_t < L ? hi_t : L;
+    const int64_t j = gr * B + b;
+    const int64_t s0 = gr * T + s_pref[b];
+    if (x == s0 && xe == seg_end) {
+      // the whole segment lies in this slice: write the final rows directly
+      attend_unit<KV, D, NT, W, NBUF>(a, kDirect, b, g, rg, L, lo, hi, 0, a.ws_out_lse);
+    } else {
+      attend_unit<KV, D, NT, W, NBUF>(a, kBalanced, b, g, rg, L, lo, hi, wid + j);
+    }
+    x = xe;
   }
 }
 
@@ -555,36 +668,88 @@ int launch_one(const AttnArgs& a, void* stream) {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+template <class KV, int D, int NT, int W, int NBUF>
+int launch_balanced_one(const AttnArgs& a, void* stream) {
+  const int64_t grid = ((int64_t)a.num_workgroups + 7) / 8 * 8;
+  hipLaunchKernelGGL((paged_attn_balanced_kernel<KV, D, NT, W, NBUF>), dim3((unsigned)grid),
+                     dim3(kWave * W), 0, static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+template <class KV, int D, int NT, int W, int NBUF>
+int occupancy_one() {
+  int cus = 0, per_cu = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_LAUNCH;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&paged_attn_balanced_kernel<KV, D, NT, W, NBUF>),
+          kWave * W, 0) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  const int64_t n = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+  return n > 0x7fffffff ? 0x7fffffff : (int)n;
+}
+
 // waves per workgroup and register buffers per wave (build-time tunables)
 #ifndef PA_WAVES
 #define PA_WAVES 4
 #endif
 #ifndef PA_NBUF_1
-#define PA_NBUF_1 3
+#define PA_NBUF_1 2
 #endif
 #ifndef PA_NBUF_2
 #define PA_NBUF_2 2
 #endif
 
+enum Op { kLaunch, kLaunchBalanced, kOccupancy };
+
 template <template <int> class KVT, int D>
-int launch_dim(const AttnArgs& a, void* stream) {
+int dispatch_dim(const AttnArgs& a, Op op, void* stream) {
   constexpr int W = PA_WAVES;
-  if (a.rows <= 16) return launch_one<KVT<D>, D, 1, W, PA_NBUF_1>(a, stream);
-  return launch_one<KVT<D>, D, 2, W, PA_NBUF_2>(a, stream);
+  if (a.rows <= 16) {
+    using KV = KVT<D>;
+    if (op == kLaunch) return launch_one<KV, D, 1, W, PA_NBUF_1>(a, stream);
+    if (op == kLaunchBalanced) return launch_balanced_one<KV, D, 1, W, PA_NBUF_1>(a, stream);
+    return occupancy_one<KV, D, 1, W, PA_NBUF_1>();
+  }
+  using KV = KVT<D>;
+  if (op == kLaunch) return launch_one<KV, D, 2, W, PA_NBUF_2>(a, stream);
+  if (op == kLaunchBalanced) return launch_balanced_one<KV, D, 2, W, PA_NBUF_2>(a, stream);
+  return occupancy_one<KV, D, 2, W, PA_NBUF_2>();
 }
 
 template <template <int> class KVT>
-int launch_kv(const AttnArgs& a, void* stream) {
-  return a.head_dim == 64 ? launch_dim<KVT, 64>(a, stream) : launch_dim<KVT, 128>(a, stream);
+int dispatch_kv(const AttnArgs& a, Op op, void* stream) {
+  return a.head_dim == 64 ? dispatch_dim<KVT, 64>(a, op, stream) : dispatch_dim<KVT, 128>(a, op, stream);
+}
+
+int dispatch(const AttnArgs& a, int q_dtype, int kv_dtype, Op op, void* stream) {
+  if (q_dtype == PA_F32 && kv_dtype == PA_F32) return dispatch_kv<F32Kv>(a, op, stream);
+  if (q_dtype == PA_BF16 && kv_dtype == PA_BF16) return dispatch_kv<Bf16Kv>(a, op, stream);
+  if (q_dtype == PA_BF16 && kv_dtype == PA_I8) return dispatch_kv<I8Kv>(a, op, stream);
+  return PA_ERR_DTYPE;
 }
 
 }  // namespace
 
 int launch_attention(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream) {
-  if (q_dtype == PA_F32 && kv_dtype == PA_F32) return launch_kv<F32Kv>(a, stream);
-  if (q_dtype == PA_BF16 && kv_dtype == PA_BF16) return launch_kv<Bf16Kv>(a, stream);
-  if (q_dtype == PA_BF16 && kv_dtype == PA_I8) return launch_kv<I8Kv>(a, stream);
-  return PA_ERR_DTYPE;
+  return dispatch(a, q_dtype, kv_dtype, kLaunch, stream);
+}
+
+int balanced_row_tile(int32_t rows) { return rows <= 16 ? 16 : 32; }
+
+int balanced_workgroups(int q_dtype, int kv_dtype, int head_dim, int32_t rows) {
+  AttnArgs a{};
+  a.head_dim = head_dim;
+  a.rows = rows;
+  return dispatch(a, q_dtype, kv_dtype, kOccupancy, nullptr);
+}
+
+int launch_balanced(const AttnArgs& a, int q_dtype, int kv_dtype, float* out, float* out_lse,
+                    void* stream) {
+  int st = dispatch(a, q_dtype, kv_dtype, kLaunchBalanced, stream);
+  if (st != PA_OK) return st;
+  return launch_balanced_merge(a, out, out_lse, stream);
 }
 
 }  // namespace pa

@@ -24,9 +24,29 @@ struct AttnArgs {
   int32_t max_parts;        // split: partitions per row in the workspace; direct: 1
   int32_t split;            // 0: direct, 1: write partials
   float scale_log2;         // sm_scale * log2(e)
+  // balanced mode
+  int32_t num_workgroups;   // workgroups the flat block list is dealt to
+  float* ws_out;            // partial rows  [num_workgroups + segments][row tile][head_dim]
+  float* ws_lse;            // partial lse   [num_workgroups + segments][row tile]
+  int32_t* ws_prefix;       // block-count prefix over sequences [num_seqs + 1]
+  float* ws_out_lse;        // final lse [B][nq][Hq] for whole segments, or null
 };
 
+// most sequences the balanced mode accepts in one call (its prefix lives in LDS)
+constexpr int kMaxBalancedSeqs = 2048;
+
 int launch_attention(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream);
+
+// rows of one partial (16 or 32): the row tile the kernel uses for `rows` query rows
+int balanced_row_tile(int32_t rows);
+// workgroups that fit on the current device at once for the balanced kernel (< 0: error)
+int balanced_workgroups(int q_dtype, int kv_dtype, int head_dim, int32_t rows);
+// attention + merge on `stream`; the AttnArgs workspace pointers must be set
+int launch_balanced(const AttnArgs& a, int q_dtype, int kv_dtype, float* out, float* out_lse,
+                    void* stream);
+
+// merge of the balanced mode's partials into out [B][nq][Hq][d] (and out_lse, if given)
+int launch_balanced_merge(const AttnArgs& a, float* out, float* out_lse, void* stream);
 
 int launch_merge(const float* part_out, const float* part_lse, const int32_t* seq_lens,
                  int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_blocks,

@@ -61,7 +61,91 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
     out_lse[row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
 }
 
+
+// Balanced mode: segment j (KV head g, row group rg, sequence b) occupies flat blocks
+// [S_j, S_{j+1}) with S_j = (g * nrg + rg) * T + prefix[b]; workgroup w covered
+// [w * per, (w + 1) * per), so the workgroups that wrote a partial for segment j are
+// w = S_j / per .. (S_{j+1} - 1) / per, at partial ids w + j.  A segment inside one slice
+// was written out by the attention kernel and is skipped here; an empty segment gets zeros.
+// One workgroup per segment, one wave per query row of its row tile.
+template <int D>
+__global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int row_tile,
+                                                              float* __restrict__ out,
+                                                              float* __restrict__ out_lse) {
+  constexpr int PER = D / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int nwv = blockDim.x / kWave;
+  const int64_t j = blockIdx.x;
+  const int B = a.num_seqs;
+  const int nrg = (a.rows + row_tile - 1) / row_tile;
+  const int64_t gr = j / B;
+  const int b = (int)(j % B);
+  const int g = (int)(gr / nrg);
+  const int rg = (int)(gr % nrg);
+
+  const int64_t T = a.ws_prefix[B];
+  const int64_t total = T * a.num_kv_heads * nrg;
+  const int64_t per = (total + a.num_workgroups - 1) / a.num_workgroups;
+  const int64_t s0 = gr * T + a.ws_prefix[b];
+  const int64_t s1 = gr * T + a.ws_prefix[b + 1];
+  const int64_t w0 = s1 > s0 ? s0 / per : 0;
+  const int64_t w1 = s1 > s0 ? (s1 - 1) / per : -1;
+  if (s1 > s0 && w0 == w1) return;   // written by the attention kernel
+
+  for (int rl = wv; rl < row_tile; rl += nwv) {
+    const int r = rg * row_tile + rl;
+    if (r >= a.rows) break;
+    const int i = r / a.group;
+    const int h = g * a.group + r % a.group;
+    const int64_t orow = (int64_t)(b * a.num_q_pos + i) * a.num_q_heads + h;
+    // max lse over the pieces: lanes take pieces, then a wave reduction
+    float M = -INFINITY;
+    for (int64_t w = w0 + lane; w <= w1; w += kWave)
+      M = fmaxf(M, a.ws_lse[(w + j) * row_tile + rl]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+    float wsum = 0.f;
+    if (M != -INFINITY) {
+      for (int64_t w = w0; w <= w1; ++w) {
+        const int64_t pid = (w + j) * row_tile + rl;
+        const float lp = a.ws_lse[pid];
+        const float wgt = lp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lp - M) * kLog2e);
+        wsum += wgt;
+        const float* o = a.ws_out + pid * D;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] += wgt == 0.f ? 0.f : wgt * o[lane + k * kWave];
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) out[orow * D + lane + k * kWave] = acc[k] * inv;
+    if (out_lse != nullptr && lane == 0)
+      out_lse[orow] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
+  }
+}
+
 }  // namespace
+
+int launch_balanced_merge(const AttnArgs& a, float* out, float* out_lse, void* stream) {
+  const int rt = balanced_row_tile(a.rows);
+  const int nrg = (a.rows + rt - 1) / rt;
+  const int64_t grid = (int64_t)a.num_kv_heads * nrg * a.num_seqs;
+  if (grid > 0x7fffffff) return PA_ERR_DIMS;
+  const int rows_in_tile = a.rows < rt ? a.rows : rt;
+  const int waves = rows_in_tile < 16 ? rows_in_tile : 16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL(balanced_merge_kernel<64>, dim3((unsigned)grid), dim3(kWave * waves), 0, s,
+                       a, rt, out, out_lse);
+  else
+    hipLaunchKernelGGL(balanced_merge_kernel<128>, dim3((unsigned)grid), dim3(kWave * waves), 0, s,
+                       a, rt, out, out_lse);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
 
 int launch_merge(const float* part_out, const float* part_lse, const int32_t* seq_lens,
                  int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_blocks,

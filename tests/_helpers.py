@@ -53,14 +53,24 @@ def gpu_append(P, wl, dv):
     P.kv_append(d, dv.k_new, dv.v_new, dv.slot_mapping, wl.cfg.batch, dv.k_cache, dv.v_cache)
 
 
-def gpu_attention(P, wl, dv, seq_lens=None, split=None):
-    """Run decode / verify (or split + merge when split=(partition_tokens, max_partitions))."""
+def gpu_attention(P, wl, dv, seq_lens=None, split=None, balanced=None):
+    """Run decode / verify (or split + merge when split=(partition_tokens, max_partitions),
+    or the balanced mode with `balanced` workgroups, 0 = the library's resident count).
+    Returns (out, partials or None, out_lse or None)."""
     c = wl.cfg
     d = dims_of(P, wl)
     lens = dv.seq_lens if seq_lens is None else seq_lens
     sm = float(np.float32(wl.sm_scale))
     out = torch.full((c.batch, c.num_q_pos, c.num_q_heads, c.head_dim), float("nan"),
                      dtype=torch.float32, device="cuda:0")
+    if balanced is not None:
+        G = balanced or P.paged_attn_balanced_workgroups(d, c.num_q_pos)
+        nbytes = P.paged_attn_balanced_workspace_bytes(d, c.num_q_pos, G)
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda:0")   # no init needed
+        out_lse = torch.full((c.batch, c.num_q_pos, c.num_q_heads), float("nan"), device="cuda:0")
+        P.paged_attn_balanced(d, c.num_q_pos, dv.q, dv.k_cache, dv.v_cache, dv.k_scale,
+                              dv.v_scale, dv.block_tables, lens, sm, G, ws, out, out_lse)
+        return out, None, out_lse
     if split is None:
         if c.num_q_pos == 1:
             P.paged_decode_attn(d, dv.q, dv.k_cache, dv.v_cache, dv.k_scale, dv.v_scale,

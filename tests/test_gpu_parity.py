@@ -36,15 +36,16 @@ def _small(name, spare=7, **kw):
     return W.generate(W.scaled(name, **base), spare_blocks=spare)
 
 
-def _check_attention(P, wl, tol=None, split=None, pairs=None, append=True):
+def _check_attention(P, wl, tol=None, split=None, pairs=None, append=True, balanced=None):
     c = wl.cfg
     tol = TOL[c.kv_dtype] if tol is None else tol
     say(f"[case] {c.name} B={c.batch} Hq={c.num_q_heads} Hkv={c.num_kv_heads} d={c.head_dim} "
-        f"nq={c.num_q_pos} kv={c.kv_dtype} split={split} seed={wl.meta['seed']}")
+        f"nq={c.num_q_pos} kv={c.kv_dtype} split={split} balanced={balanced} "
+        f"seed={wl.meta['seed']}")
     dv = Dev(wl)
     if append and wl.slot_mapping is not None:
         gpu_append(P, wl, dv)
-    out, parts, out_lse = gpu_attention(P, wl, dv, split=split)
+    out, parts, out_lse = gpu_attention(P, wl, dv, split=split, balanced=balanced)
     torch.cuda.synchronize()
     kc, vc = oracle_caches(wl, appended=append)
     ref, ref_lse = oracle_attention(wl, kc, vc, pairs=pairs)
@@ -52,13 +53,13 @@ def _check_attention(P, wl, tol=None, split=None, pairs=None, append=True):
     say(f"  max abs err {err:.3e} (tol {tol:.0e})")
     assert err <= tol
     if out_lse is not None:
-        g = out_lse.cpu().numpy()[:, :]
-        r = ref_lse[:, 0, :]
+        g = out_lse.cpu().numpy().reshape(ref_lse.shape)
+        r = ref_lse
         sel = np.isfinite(r)
         if pairs is not None:
             m = np.zeros(r.shape, bool)
             for b, kv in pairs:
-                m[b, kv * c.group_size:(kv + 1) * c.group_size] = True
+                m[b, ..., kv * c.group_size:(kv + 1) * c.group_size] = True
             sel &= m
         assert np.all(np.abs(g[sel] - r[sel]) <= 1e-3 * np.maximum(1, np.abs(r[sel])))
         empty = r == -np.inf
@@ -187,6 +188,47 @@ def test_split_merge_small(P, split):
         assert np.abs(pl[b, :, :n] - rl[b, 0, :, :n]).max() <= 1e-3
 
 
+# ---- balanced mode: the batch's blocks dealt evenly over G workgroups -----------------
+@pytest.mark.parametrize("G", [1, 3, 7, 64, 0])
+@pytest.mark.parametrize("name,kw", [
+    ("llama3_8b", dict(batch=6, length_range=(1, 700))),
+    ("verify_int8", dict(batch=5, length_range=(1, 600))),
+    ("tiny_fp32", dict(batch=5, length_range=(1, 400))),
+])
+def test_balanced_small(P, name, kw, G):
+    wl = _small(name, **kw)
+    _check_attention(P, wl, balanced=G)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("llama3_8b", dict(batch=3, length_range=(40, 400), num_q_heads=64, num_kv_heads=1)),  # 64 rows
+    ("llama3_8b", dict(batch=6, lengths=(0, 1, 15, 16, 17, 0), append=False)),
+    ("verify_int8", dict(batch=3, lengths=(3, 6, 1))),
+    ("llama3_8b", dict(batch=4, length_range=(1, 200), num_q_pos=4, append=False)),
+    ("llama2_70b_prefix", dict(batch=4, length_range=(17, 520), head_dim=64)),
+])
+def test_balanced_edge_cases(P, name, kw):
+    wl = _small(name, **kw)
+    _check_attention(P, wl, balanced=0)
+    _check_attention(P, wl, balanced=5)
+
+
+def test_balanced_workspace_errors(P):
+    wl = _small("llama3_8b", batch=2, length_range=(1, 50), append=False)
+    c = wl.cfg
+    d = dims_of(P, wl)
+    dv = Dev(wl)
+    n = P.paged_attn_balanced_workspace_bytes(d, 1, 4)
+    assert n > 0
+    ws = torch.empty(n - 4, dtype=torch.uint8, device="cuda:0")
+    out = torch.empty((c.batch, 1, c.num_q_heads, c.head_dim), device="cuda:0")
+    with pytest.raises(P.PagedAttnError) as e:
+        P.paged_attn_balanced(d, 1, dv.q, dv.k_cache, dv.v_cache, None, None, dv.block_tables,
+                              dv.seq_lens, 0.1, 4, ws, out)
+    assert e.value.status == -8
+    assert P.paged_attn_balanced_workgroups(d, 1) >= 256
+
+
 # ---- invariances, bit for bit --------------------------------------------------------
 def test_block_relabel_and_batch_order_bit_identical(P):
     wl = _small("llama3_8b", batch=6, length_range=(1, 500), append=False)
@@ -220,11 +262,13 @@ def test_full_llama3_8b(P):
     wl = W.generate("llama3_8b")
     _check_attention(P, wl)
     _check_attention(P, wl, split=(512, 8))
+    _check_attention(P, wl, balanced=0)
 
 
 def test_full_llama2_70b_shared_prefix(P):
     wl = W.generate("llama2_70b_prefix")
     _check_attention(P, wl)
+    _check_attention(P, wl, balanced=0)
     wl2 = W.generate("llama2_70b_prefix", shuffle_batch=True)
     _check_attention(P, wl2, pairs=[(b, g) for b in range(0, 32, 3) for g in range(8)])
 
@@ -234,8 +278,10 @@ def test_full_long_128k(P):
     pairs = [(0, 0), (1, 5), (2, 3), (3, 7)]
     _check_attention(P, wl, split=(2048, 64), pairs=pairs)
     _check_attention(P, wl, split=(4096, 8), pairs=pairs[:2])   # last partition absorbs the rest
+    _check_attention(P, wl, balanced=0, pairs=pairs)
 
 
 def test_full_verify_int8(P):
     wl = W.generate("verify_int8")
     _check_attention(P, wl)
+    _check_attention(P, wl, balanced=0)
