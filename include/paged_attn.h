@@ -19,10 +19,14 @@
  * names the physical block holding tokens 16j .. 16j+15 of sequence b.  Inside a block
  * this library uses
  *
- *   k_cache[num_blocks][num_kv_heads][16][head_dim]      (token-major)
- *   v_cache[num_blocks][num_kv_heads][head_dim][16]      (dim-major)
+ *   k_cache[num_blocks][num_kv_heads][head_dim / x][16][x]   x = 16 / element bytes
+ *                                                         (x = 4 fp32, 8 bf16, 16 int8)
+ *   v_cache[num_blocks][num_kv_heads][head_dim][16]
  *
  * so one (block, KV head) tile of K or V is one contiguous 16 x head_dim piece of memory.
+ * Inside a K tile, element k of the token at offset o sits at [k / x][o][k % x]: each
+ * 16-byte column of the 16 tokens' K rows is contiguous.  Inside a V tile, element k of
+ * that token sits at [k][o].
  * int8 caches carry one fp32 scale per (physical block, KV head) for each of K and V:
  * k_scale[num_blocks][num_kv_heads], v_scale[num_blocks][num_kv_heads]; the stored code x_q
  * stands for x_q * scale (lecture 10 "Quantization 量化 / 基本概念", zero point 0).

@@ -12,13 +12,13 @@ therefore in physical block table[t // 16], at offset t % 16 inside it.
 What the pages leave open is the element order inside a physical block.  The
 cache format used throughout this project (and stated in include/paged_attn.h):
 
-    k_cache[num_blocks, num_kv_heads, 16, head_dim]   token-major rows
-    v_cache[num_blocks, num_kv_heads, head_dim, 16]   dim-major rows
+    k_cache[num_blocks, num_kv_heads, head_dim / x, 16, x]   x = 16 / element bytes
+    v_cache[num_blocks, num_kv_heads, head_dim, 16]
 
-so K of token t, KV head g is k_cache[table[t//16], g, t%16, :] and V of it is
-v_cache[table[t//16], g, :, t%16].  For int8 storage one fp32 scale per
-(physical block, KV head) applies to each tensor: k_scale[num_blocks,
-num_kv_heads], v_scale[num_blocks, num_kv_heads].
+so K of token t, KV head g is k_cache[table[t//16], g, :, t%16, :] read in (column,
+element) order, and V of it is v_cache[table[t//16], g, :, t%16].  For int8 storage
+one fp32 scale per (physical block, KV head) applies to each tensor:
+k_scale[num_blocks, num_kv_heads], v_scale[num_blocks, num_kv_heads].
 
 A "slot" is the flat index physical_block * 16 + offset of one token position.
 """
@@ -28,6 +28,11 @@ import numpy as np
 from . import storage
 
 BLOCK_SIZE = 16
+
+
+def k_row(k_cache, blk, g, off):
+    """Stored K row (head_dim elements) of one token: the 16-byte columns in order."""
+    return np.asarray(k_cache[blk, g, :, off, :]).reshape(-1)
 
 
 def token_location(table_row, t, block_size=BLOCK_SIZE):
@@ -49,14 +54,14 @@ def depage(k_cache, v_cache, kind, table_row, seq_len, g, k_scale=None, v_scale=
     physical block its table entry names (Tutorial §7), one token at a time --
     the plain definition, no blocking.  Decoding follows ``storage.decode``.
     """
-    d = k_cache.shape[-1]
+    d = v_cache.shape[2]
     K = np.empty((seq_len, d), dtype=np.float64)
     V = np.empty((seq_len, d), dtype=np.float64)
     for t in range(seq_len):
         blk, off = token_location(table_row, t, block_size)
         ks = None if k_scale is None else k_scale[blk, g]
         vs = None if v_scale is None else v_scale[blk, g]
-        K[t] = storage.decode(k_cache[blk, g, off, :], kind, ks)
+        K[t] = storage.decode(k_row(k_cache, blk, g, off), kind, ks)
         V[t] = storage.decode(v_cache[blk, g, :, off], kind, vs)
     return K, V
 
@@ -73,7 +78,9 @@ def depage_fast(k_cache, v_cache, kind, table_row, seq_len, g, k_scale=None, v_s
     off = t % block_size
     ks = None if k_scale is None else np.asarray(k_scale)[blk, g][:, None]
     vs = None if v_scale is None else np.asarray(v_scale)[blk, g][:, None]
-    K = storage.decode(k_cache[blk, g, off, :], kind, ks)
+    kc = np.asarray(k_cache)
+    kr = kc[blk, g, :, off, :].reshape(seq_len, kc.shape[2] * kc.shape[4])
+    K = storage.decode(kr, kind, ks)
     V = storage.decode(v_cache[blk, g, :, off], kind, vs)
     return K, V
 
@@ -94,7 +101,7 @@ def append(k_cache, v_cache, k_new, v_new, slot_mapping, block_size=BLOCK_SIZE):
             continue
         blk, off = divmod(int(s), block_size)
         for g in range(kc.shape[1]):
-            kc[blk, g, off, :] = k_new[i, g, :]
+            kc[blk, g, :, off, :] = np.asarray(k_new[i, g, :]).reshape(kc.shape[2], kc.shape[4])
             vc[blk, g, :, off] = v_new[i, g, :]
     return kc, vc
 
@@ -112,6 +119,6 @@ def gather(k_cache, v_cache, block_tables, seq_lens, k_out, v_out, block_size=BL
         for t in range(L):
             blk, off = token_location(block_tables[b], t, block_size)
             for g in range(ko.shape[1]):
-                ko[b, g, t, :] = k_cache[blk, g, off, :]
+                ko[b, g, t, :] = k_row(k_cache, blk, g, off)
                 vo[b, g, t, :] = v_cache[blk, g, :, off]
     return ko, vo

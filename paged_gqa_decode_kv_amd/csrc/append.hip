@@ -3,9 +3,9 @@
 // Append (devpress tutorial section 2; lecture 10 "KV Cache 原理"): each decode step
 // writes the new token's K and V into the cache.  The caller gives the slot
 // (physical_block * 16 + offset) of every new token, as a block manager hands them out
-// (tutorial section 7); the kernel is a plain bit copy into that slot.  K lands in a
-// token-major row (head_dim contiguous elements), V in column `offset` of the dim-major
-// V tile.  One thread per (token, KV head, dim); negative or out-of-pool slots are skipped.
+// (tutorial section 7); the kernel is a plain bit copy into that slot.  K lands in row
+// `offset` of each 16-byte column of the K tile, V in column `offset` of the dim-major V
+// tile.  One thread per (token, KV head, dim); negative or out-of-pool slots are skipped.
 //
 // Gather copies every sequence's tokens out of the pool in logical order through the same
 // tile addressing the attention kernels use, so its output checks that translation
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   const int64_t blk = slot / kBlockTokens;
   const int off = (int)(slot % kBlockTokens);
   const int64_t tile = kv_tile(blk, g, num_kv_heads) * (int64_t)kBlockTokens * head_dim;
-  k_cache[tile + k_elem(off, k, head_dim)] = k_new[idx];
+  k_cache[tile + k_elem<sizeof(T)>(off, k)] = k_new[idx];
   v_cache[tile + v_elem(off, k)] = v_new[idx];
 }
 
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(
   if (phys < 0 || phys >= num_blocks) return;
   const int off = tpos % kBlockTokens;
   const int64_t tile = kv_tile(phys, g, num_kv_heads) * (int64_t)kBlockTokens * head_dim;
-  k_out[idx] = k_cache[tile + k_elem(off, k, head_dim)];
+  k_out[idx] = k_cache[tile + k_elem<sizeof(T)>(off, k)];
   v_out[idx] = v_cache[tile + v_elem(off, k)];
 }
 

@@ -12,12 +12,14 @@
 //    read from HBM is used by the whole group straight out of registers:
 //      S^T[16 tokens x 16 rows] = K_tile[16 x d] * Q^T[d x 16 rows]
 //      O^T[d x 16 rows]        += V_tile^T[d x 16 tokens] * P^T[16 tokens x 16 rows]
-//    K rows are token-major and V rows dim-major in HBM, which is exactly the register
-//    layout both MFMA A-operands want, so every lane issues contiguous 8/16-byte loads.
+//    K tiles are stored as 16-byte token columns and V tiles dim-major, which is exactly
+//    the register layout both MFMA A-operands want: each K load instruction reads 1 KiB
+//    in lane order and each V load 512 contiguous bytes.
 //  * Online softmax in the log2 domain: per row a running max and a running sum; the
 //    output accumulators are rescaled only when some row's max grows.
-//  * P feeds the P*V MFMA in two 16-bit pieces (hi + lo) so the product keeps ~16
-//    significant bits of the fp32 probabilities; the fp32 path uses fp32 MFMA directly.
+//  * P feeds the bf16 P*V MFMA in two 16-bit pieces (hi + lo) so the product keeps ~16
+//    significant bits of the fp32 probabilities; the int8 path rounds P once to fp16
+//    (11 bits) and the fp32 path uses fp32 MFMA directly.
 //  * int8 K/V are decoded to exact fp16 in registers; the per-(block, head) K scale
 //    multiplies the scores and the V scale is folded into P.
 //  * A workgroup of W waves owns one (sequence, KV head, row group, partition); its waves
@@ -78,16 +80,22 @@ struct Bf16Kv {
       q.v[kk] = __builtin_bit_cast(bf16x8, x);
     }
   }
-  __device__ static void load_k(K& k, const void* tile, int row16, int grp) {
-    const uint16_t* p = static_cast<const uint16_t*>(tile) + row16 * D + 8 * grp;
+  // lane (token row16, grp) step kk: column 4*kk + grp of the K tile, at kk*1 KiB + lane*16
+  __device__ static void load_k(K& k, const void* tile, int lane) {
+    const uint8_t* p = static_cast<const uint8_t*>(tile) + lane * 16;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) k.v[kk] = stream_load<u32x4>(p + 32 * kk);
+    for (int kk = 0; kk < NK; ++kk) k.v[kk] = stream_load<u32x4>(p + 1024 * kk);
   }
   __device__ static void load_v(V& v, const void* tile, int row16, int grp) {
     const uint16_t* p = static_cast<const uint16_t*>(tile) + row16 * 16 + 4 * grp;
 #pragma unroll
     for (int t = 0; t < ND; ++t) v.v[t] = stream_load<u32x2>(p + t * 256);
   }
+  // the loaded tiles are the MFMA operands already
+  using KMat = K;
+  using VMat = V;
+  __device__ static const K& k_mat(const K& k) { return k; }
+  __device__ static const V& v_mat(const V& v) { return v; }
   __device__ static f32x4 qk(const K& k, const Q& q) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -141,16 +149,20 @@ struct F32Kv {
     for (int u = 0; u < NU; ++u)
       q.v[u] = valid ? *reinterpret_cast<const f32x4*>(p + 16 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  __device__ static void load_k(K& k, const void* tile, int row16, int grp) {
-    const float* p = static_cast<const float*>(tile) + row16 * D + 4 * grp;
+  __device__ static void load_k(K& k, const void* tile, int lane) {
+    const uint8_t* p = static_cast<const uint8_t*>(tile) + lane * 16;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) k.v[u] = stream_load<f32x4>(p + 16 * u);
+    for (int u = 0; u < NU; ++u) k.v[u] = stream_load<f32x4>(p + 1024 * u);
   }
   __device__ static void load_v(V& v, const void* tile, int row16, int grp) {
     const float* p = static_cast<const float*>(tile) + row16 * 16 + 4 * grp;
 #pragma unroll
     for (int t = 0; t < ND; ++t) v.v[t] = stream_load<f32x4>(p + t * 256);
   }
+  using KMat = K;
+  using VMat = V;
+  __device__ static const K& k_mat(const K& k) { return k; }
+  __device__ static const V& v_mat(const V& v) { return v; }
   __device__ static f32x4 qk(const K& k, const Q& q) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -202,46 +214,54 @@ struct I8Kv {
         q.v[2 * h + s] = f;
       }
   }
-  __device__ static void load_k(K& k, const void* tile, int row16, int grp) {
-    const uint8_t* p = static_cast<const uint8_t*>(tile) + row16 * D + 16 * grp;
+  __device__ static void load_k(K& k, const void* tile, int lane) {
+    const uint8_t* p = static_cast<const uint8_t*>(tile) + lane * 16;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) k.v[h] = stream_load<u32x4>(p + 64 * h);
+    for (int h = 0; h < NH; ++h) k.v[h] = stream_load<u32x4>(p + 1024 * h);
   }
   __device__ static void load_v(V& v, const void* tile, int row16, int grp) {
     const uint8_t* p = static_cast<const uint8_t*>(tile) + row16 * 16 + 4 * grp;
 #pragma unroll
     for (int t = 0; t < ND; ++t) v.v[t] = stream_load<uint32_t>(p + t * 256);
   }
-  __device__ static f32x4 qk(const K& k, const Q& q) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+  // int8 codes decoded once per block to exact fp16 MFMA operands (shared by all row tiles)
+  struct KMat { f16x8 v[2 * NH]; };
+  struct VMat { f16x4 v[ND]; };
+  __device__ static KMat k_mat(const K& k) {
+    KMat m;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const f16x4 a0 = i8x4_to_f16x4(k.v[h].x), a1 = i8x4_to_f16x4(k.v[h].y);
       const f16x4 a2 = i8x4_to_f16x4(k.v[h].z), a3 = i8x4_to_f16x4(k.v[h].w);
-      const f16x8 lo = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      const f16x8 hi = {a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, q.v[2 * h], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, q.v[2 * h + 1], c, 0, 0, 0);
+      m.v[2 * h] = f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      m.v[2 * h + 1] = f16x8{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
     }
+    return m;
+  }
+  __device__ static VMat v_mat(const V& v) {
+    VMat m;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) m.v[t] = i8x4_to_f16x4(v.v[t]);
+    return m;
+  }
+  __device__ static f32x4 qk(const KMat& k, const Q& q) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2 * NH; ++s)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(k.v[s], q.v[s], c, 0, 0, 0);
     return c;
   }
   __device__ static void mask_v(V&, int, int) {}  // codes are finite; P = 0 removes them
-  // p is scaled by vfac = 256 * v_scale(block) / v_ref before the fp16 split, keeping
-  // small probabilities out of the fp16 subnormal range.
-  __device__ static void pv(f32x4* acc, const V& v, f32x4 p, float vfac) {
-    f16x4 hi, lo;
+  // p is scaled by vfac = 256 * v_scale(block) / v_ref and rounded once to fp16 (relative
+  // error <= 2^-11 per weight, so |error of out| <= 2^-11 * max|V|, inside the int8
+  // tolerance); the factor 256 keeps small weights out of the fp16 subnormal range.
+  __device__ static void pv(f32x4* acc, const VMat& v, f32x4 p, float vfac) {
+    f16x4 ph;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = p[e] * vfac;
-      hi[e] = (_Float16)x;
-      lo[e] = (_Float16)(x - (float)hi[e]);
-    }
+    for (int e = 0; e < 4; ++e) ph[e] = (_Float16)(p[e] * vfac);
 #pragma unroll
-    for (int t = 0; t < ND; ++t) {
-      const f16x4 a = i8x4_to_f16x4(v.v[t]);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, hi, acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, lo, acc[t], 0, 0, 0);
-    }
+    for (int t = 0; t < ND; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(v.v[t], ph, acc[t], 0, 0, 0);
   }
 };
 
@@ -377,7 +397,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   // blocks stay in flight while one is consumed.
   auto issue = [&](typename KV::K& kk, typename KV::V& vv, int ph) {
     const int64_t tl = kv_tile(ph >= 0 ? ph : 0, g, a.num_kv_heads);
-    KV::load_k(kk, kbase + tl * tile_bytes, row16, grp);
+    KV::load_k(kk, kbase + tl * tile_bytes, lane);
     KV::load_v(vv, vbase + tl * tile_bytes, row16, grp);
   };
   auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, const Slot& sl) {
@@ -406,9 +426,10 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
     const bool need_mask = tok0 + kBlockTokens > lim_min;
     f32x4 pr[NT];
     float alpha[NT];
+    const auto& km = KV::k_mat(kk);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      f32x4 s = KV::qk(kk, qop[nt]);
+      f32x4 s = KV::qk(km, qop[nt]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = s[e] * sc;
@@ -435,8 +456,9 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
         for (int t = 0; t < ND; ++t) acc[nt][t] *= alpha[nt];
     }
     if (tok0 + kBlockTokens > hi) KV::mask_v(vv, hi - tok0, grp);
+    const auto& vm = KV::v_mat(vv);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) KV::pv(acc[nt], vv, pr[nt], vfac);
+    for (int nt = 0; nt < NT; ++nt) KV::pv(acc[nt], vm, pr[nt], vfac);
   };
 
   {
@@ -559,9 +581,18 @@ __device__ __forceinline__ int64_t xcd_logical_id() {
   return (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 }
 
+// Occupancy the register allocation is asked to allow (waves per SIMD).  With a target
+// above one wave the accumulators share the unified register file with the rest, which
+// lets one row tile fit three waves per SIMD and two row tiles two.
+// (fp32 tiles are twice as large, so they get one step less.)
+template <class KV, int NT> struct WavesPerEU {
+  static constexpr int value = (KV::kElem == 4 ? 2 : 3) - (NT == 1 ? 0 : 1);
+};
+
 // Direct and split modes: one unit per (KV head, sequence, row group, partition).
 template <class KV, int D, int NT, int W, int NBUF>
-__global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(WavesPerEU<KV, NT>::value)))
+void paged_attn_kernel(AttnArgs a) {
   const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg * a.max_parts;
   const int64_t u = xcd_logical_id();
@@ -593,7 +624,8 @@ __global__ __launch_bounds__(kWave* W) void paged_attn_kernel(AttnArgs a) {
 // piece becomes a partial result at partial id w + j (unique: along the slices both w and
 // j only grow) and a merge kernel combines the pieces of each cut segment.
 template <class KV, int D, int NT, int W, int NBUF>
-__global__ __launch_bounds__(kWave* W) void paged_attn_balanced_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(WavesPerEU<KV, NT>::value)))
+void paged_attn_balanced_kernel(AttnArgs a) {
   __shared__ int s_pref[kMaxBalancedSeqs + 1];
   const int64_t wid = xcd_logical_id();
   if (wid >= a.num_workgroups) return;

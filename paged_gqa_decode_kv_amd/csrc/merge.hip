@@ -100,9 +100,10 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
     const int h = g * a.group + r % a.group;
     const int64_t orow = (int64_t)(b * a.num_q_pos + i) * a.num_q_heads + h;
     // max lse over the pieces: lanes take pieces, then a wave reduction
+    const int64_t npc = w1 - w0 + 1;
     float M = -INFINITY;
-    for (int64_t w = w0 + lane; w <= w1; w += kWave)
-      M = fmaxf(M, a.ws_lse[(w + j) * row_tile + rl]);
+    for (int64_t q = lane; q < npc; q += kWave)
+      M = fmaxf(M, a.ws_lse[(w0 + q + j) * row_tile + rl]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float acc[PER];
@@ -110,14 +111,38 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
     float wsum = 0.f;
     if (M != -INFINITY) {
-      for (int64_t w = w0; w <= w1; ++w) {
-        const int64_t pid = (w + j) * row_tile + rl;
-        const float lp = a.ws_lse[pid];
-        const float wgt = lp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lp - M) * kLog2e);
-        wsum += wgt;
-        const float* o = a.ws_out + pid * D;
+      for (int64_t q0 = 0; q0 < npc; q0 += kWave) {
+        // lane q holds the weight of piece q0 + q
+        float wl = 0.f;
+        if (q0 + lane < npc) {
+          const float lp = a.ws_lse[(w0 + q0 + lane + j) * row_tile + rl];
+          wl = lp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lp - M) * kLog2e);
+        }
+        float ws = wl;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) acc[k] += wgt == 0.f ? 0.f : wgt * o[lane + k * kWave];
+        for (int off = 32; off > 0; off >>= 1) ws += __shfl_xor(ws, off);
+        wsum += ws;
+        const int nq = (int)(npc - q0 < kWave ? npc - q0 : kWave);
+        // four pieces per step so their row loads are in flight together
+        for (int q = 0; q < nq; q += 4) {
+          float wq[4];
+          const float* o[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int qq = q + u < nq ? q + u : q;
+            wq[u] = q + u < nq ? __shfl(wl, qq) : 0.f;
+            o[u] = a.ws_out + ((w0 + q0 + qq + j) * row_tile + rl) * D;
+          }
+          float v[4][PER];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < PER; ++k) v[u][k] = o[u][lane + k * kWave];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < PER; ++k) acc[k] += wq[u] == 0.f ? 0.f : wq[u] * v[u][k];
+        }
       }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

@@ -25,8 +25,16 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int64_t kv_tile(int64_t phys, int g, int num_kv_heads) {
   return phys * num_kv_heads + g;
 }
-// element offset of token `off` (0..15), dim k inside a K tile / a V tile
-__device__ __forceinline__ int k_elem(int off, int k, int head_dim) { return off * head_dim + k; }
+// Element offset of token `off` (0..15), dim k inside a K tile: the tile is stored as
+// 16-byte columns, [k / x][off][k % x] with x = 16 / element bytes, so that the 16 tokens'
+// bytes [16c, 16c + 16) are contiguous -- one lane's MFMA operand per 16 bytes, one load
+// instruction per 1 KiB.
+template <int kElemBytes>
+__device__ __forceinline__ int k_elem(int off, int k) {
+  constexpr int x = 16 / kElemBytes;
+  return (k / x) * (kBlockTokens * x) + off * x + (k % x);
+}
+// ... and inside a V tile: [k][off]
 __device__ __forceinline__ int v_elem(int off, int k) { return k * kBlockTokens + off; }
 
 // ---- small numeric helpers ------------------------------------------------------------

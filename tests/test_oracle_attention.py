@@ -194,7 +194,7 @@ def test_verify_causal_closed_form():
     # output is the mean of 0..p = p / 2 in every dimension.
     L, nq, d, G = 37, 6, 4, 2
     tables = np.array([[2, 0, 1]], dtype=np.int32)
-    kc = np.ones((3, 1, 16, d), np.float32)
+    kc = np.ones((3, 1, d // 4, 16, 4), np.float32)
     vc = np.zeros((3, 1, d, 16), np.float32)
     for t in range(48):
         vc[tables[0, t // 16], 0, :, t % 16] = t

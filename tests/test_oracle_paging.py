@@ -51,15 +51,18 @@ def test_worked_block_table():
 
 
 def _labelled_pool(NB, H, d, kind):
-    """Pool whose every element encodes its own (block, head, slot, dim) position."""
-    blk = np.arange(NB)[:, None, None, None]
-    g = np.arange(H)[None, :, None, None]
-    off = np.arange(16)[None, None, :, None]
-    k = np.arange(d)[None, None, None, :]
-    kval = ((blk * 8 + g) * 16 + off) * 64.0 + k                 # [NB,H,16,d], exact in fp32
-    vval = -(((blk * 8 + g) * 16 + off) * 64.0 + k)
-    vval = np.transpose(vval, (0, 1, 3, 2)).copy()                  # [NB,H,d,16]
-    return kval.astype(np.float32), vval.astype(np.float32)
+    """fp32 pool whose every element encodes its own (block, head, slot, dim) position,
+    laid out as the header states: K [NB, H, d/4, 16, 4], V [NB, H, d, 16]."""
+    kval = np.empty((NB, H, d // 4, 16, 4), np.float32)
+    vval = np.empty((NB, H, d, 16), np.float32)
+    for blk in range(NB):
+        for g in range(H):
+            for off in range(16):
+                for k in range(d):
+                    label = ((blk * 8 + g) * 16 + off) * 64.0 + k    # exact in fp32
+                    kval[blk, g, k // 4, off, k % 4] = label
+                    vval[blk, g, k, off] = -label
+    return kval, vval
 
 
 def test_depage_reads_documented_layout():
@@ -82,17 +85,17 @@ def test_depage_fast_equals_depage(kind):
     rng = np.random.default_rng(3)
     NB, H, d = 64, 2, 16
     if kind == "f32":
-        kc = rng.standard_normal((NB, H, 16, d)).astype(np.float32)
+        kc = rng.standard_normal((NB, H, d // 4, 16, 4)).astype(np.float32)
         vc = rng.standard_normal((NB, H, d, 16)).astype(np.float32)
         ks = vs = None
     elif kind == "bf16":
-        kc = rng.integers(0, 2**16, (NB, H, 16, d)).astype(np.uint16)
+        kc = rng.integers(0, 2**16, (NB, H, d // 8, 16, 8)).astype(np.uint16)
         vc = rng.integers(0, 2**16, (NB, H, d, 16)).astype(np.uint16)
         kc[(kc & 0x7F80) == 0x7F80] = 0x3F80  # no inf/nan patterns
         vc[(vc & 0x7F80) == 0x7F80] = 0x3F80
         ks = vs = None
     else:
-        kc = rng.integers(-127, 128, (NB, H, 16, d)).astype(np.int8)
+        kc = rng.integers(-127, 128, (NB, H, d // 16, 16, 16)).astype(np.int8)
         vc = rng.integers(-127, 128, (NB, H, d, 16)).astype(np.int8)
         ks = rng.random((NB, H)).astype(np.float32)
         vs = rng.random((NB, H)).astype(np.float32)
@@ -105,17 +108,19 @@ def test_depage_fast_equals_depage(kind):
 
 
 def test_append_writes_slot_and_nothing_else():
-    NB, H, d = 8, 2, 4
+    NB, H, d = 8, 2, 16
     kc, vc = _labelled_pool(NB, H, d, "f32")
     k_new = np.arange(3 * H * d, dtype=np.float32).reshape(3, H, d) + 0.5
     v_new = -k_new
     slots = np.array([5 * 16 + 3, -1, 0 * 16 + 15], dtype=np.int64)
     kc2, vc2 = paging.append(kc, vc, k_new, v_new, slots)
-    assert np.array_equal(kc2[5, :, 3, :], k_new[0]) and np.array_equal(vc2[5, :, :, 3], v_new[0])
-    assert np.array_equal(kc2[0, :, 15, :], k_new[2]) and np.array_equal(vc2[0, :, :, 15], v_new[2])
+    for g in range(H):
+        assert np.array_equal(paging.k_row(kc2, 5, g, 3), k_new[0, g])
+        assert np.array_equal(paging.k_row(kc2, 0, g, 15), k_new[2, g])
+    assert np.array_equal(vc2[5, :, :, 3], v_new[0]) and np.array_equal(vc2[0, :, :, 15], v_new[2])
     mask_k = np.ones(kc.shape, bool)
-    mask_k[5, :, 3, :] = False
-    mask_k[0, :, 15, :] = False
+    mask_k[5, :, :, 3, :] = False
+    mask_k[0, :, :, 15, :] = False
     mask_v = np.ones(vc.shape, bool)
     mask_v[5, :, :, 3] = False
     mask_v[0, :, :, 15] = False

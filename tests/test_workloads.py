@@ -53,11 +53,12 @@ def test_tables_distinct_and_sized(name):
 def test_tiny_config_lengths_and_append_slots():
     wl = W.generate("tiny_fp32")
     assert wl.seq_lens.tolist() == [38, 129, 201, 512]
-    assert wl.block_tables.shape[0] == 4 and wl.k_cache.shape == (256, 2, 16, 64)
+    assert wl.block_tables.shape[0] == 4 and wl.k_cache.shape == (256, 2, 16, 16, 4)
+    assert wl.v_cache.shape == (256, 2, 64, 16)
     for b, L in enumerate(wl.seq_lens.tolist()):
         assert int(wl.slot_mapping[b]) == paging.slot_of(wl.block_tables[b].tolist(), L - 1)
         blk, off = divmod(int(wl.slot_mapping[b]), 16)
-        assert torch.isnan(wl.k_cache[blk, :, off, :]).all()   # filled only by the append
+        assert torch.isnan(W.k_token_rows(wl.k_cache)[blk, :, off, :]).all()  # only the append fills it
         assert torch.isnan(wl.v_cache[blk, :, :, off]).all()
 
 
@@ -78,7 +79,7 @@ def test_shared_prefix_structure():
 def test_peaked_positions():
     cfg = W.scaled("long_128k", lengths=(4096,) * 4)
     wl = W.generate(cfg)
-    k = wl.k_cache.float()
+    k = W.k_token_rows(wl.k_cache).float()
     big = (k.abs().amax(dim=(1, 3)) > 6.5)               # [NB, 16] slot-level
     frac = big.float().mean().item()
     assert 0.006 < frac < 0.014
@@ -87,15 +88,14 @@ def test_peaked_positions():
 def test_int8_encoding_invariants():
     wl = W.generate(W.scaled("verify_int8", batch=4, length_range=(20, 300)), poison=False)
     occ = wl.occupancy
-    x32 = None
-    for name, cache, scale, slot_dim in (("k", wl.k_cache, wl.k_scale, 2),
-                                         ("v", wl.v_cache, wl.v_scale, 3)):
+    for cache, scale in ((W.k_token_rows(wl.k_cache), wl.k_scale),
+                         (wl.v_cache.transpose(2, 3), wl.v_scale)):
         assert cache.dtype == torch.int8 and int(cache.abs().max()) <= 127
         for blk in range(cache.shape[0]):
             n = int(occ[blk])
             if n == 0:
                 continue
-            live = cache[blk, :, :n, :] if slot_dim == 2 else cache[blk, :, :, :n]
+            live = cache[blk, :, :n, :]
             # the largest-magnitude live element encodes to +-127 in every head
             assert (live.abs().amax(dim=(1, 2)) == 127).all()
             assert (scale[blk] > 0).all()
@@ -106,15 +106,28 @@ def test_int8_dequant_error_bound():
     gen_a = W.generate(cfg, poison=False)
     # regenerate the fp32 pool the encoder saw (same seed, same draw order)
     g = torch.Generator().manual_seed(cfg.seed)
-    lens = W._draw_lengths(cfg, g)
+    W._draw_lengths(cfg, g)
     NB = gen_a.k_cache.shape[0]
     torch.randperm(NB, generator=g)
     k32 = W._randn_pool((NB, cfg.num_kv_heads, 16, cfg.head_dim), g)
-    deq = gen_a.k_cache.float() * gen_a.k_scale[:, :, None, None]
+    deq = W.k_token_rows(gen_a.k_cache).float() * gen_a.k_scale[:, :, None, None]
     err = (deq - k32).abs()
     bound = gen_a.k_scale[:, :, None, None] / 2 * (1 + 1e-6)
     live = (torch.arange(16)[None, :] < gen_a.occupancy[:, None])[:, None, :, None]
     assert bool(((err <= bound) | ~live).all())
+
+
+def test_k_encoding_roundtrip():
+    x = torch.arange(3 * 2 * 16 * 64, dtype=torch.float32).reshape(3, 2, 16, 64)
+    for dt, xw in ((torch.float32, 4), (torch.bfloat16, 8), (torch.int8, 16)):
+        t = (x % 100).to(dt)
+        enc = W.encode_k(t)
+        assert enc.shape == (3, 2, 64 // xw, 16, xw)
+        # element k of token o at [k // x][o][k % x]
+        assert enc[1, 1, 5 // xw, 7, 5 % xw] == t[1, 1, 7, 5]
+        assert torch.equal(W.k_token_rows(enc), t)
+    v = W.encode_v(x)
+    assert v.shape == (3, 2, 64, 16) and v[2, 0, 9, 4] == x[2, 0, 4, 9]
 
 
 def test_seeded_determinism():

@@ -6,8 +6,10 @@ storage types, hands out pool blocks the way a KV block manager does, and
 encodes int8 caches.  Everything it returns is a CPU ``torch`` tensor.
 
 Cache format (the library's, see include/paged_attn.h):
-    k_cache [num_blocks, num_kv_heads, 16, head_dim]
+    k_cache [num_blocks, num_kv_heads, head_dim / x, 16, x]   x = 16 / element bytes
     v_cache [num_blocks, num_kv_heads, head_dim, 16]
+The generator works on token-major [num_blocks, num_kv_heads, 16, head_dim] arrays and
+encodes them into that format as its last step (``encode_k`` / ``encode_v``).
     k_scale, v_scale [num_blocks, num_kv_heads] fp32 (int8 caches only)
     block_tables [B, max_blocks] int32 (unused entries = -1)
     seq_lens [B] int32, q [B, nq, Hq, d], slot_mapping [B] int64
@@ -247,9 +249,9 @@ def generate(cfg, seed=None, *, poison=True, spare_blocks=0, shuffle_batch=False
         tables[i, : len(row)] = torch.tensor(row, dtype=torch.int32)
     occ = torch.tensor(alloc.occupancy(), dtype=torch.int32)
 
-    # ---- K/V pool ------------------------------------------------------------------
+    # ---- K/V pool, token-major [NB, Hkv, 16, d] until encoded --------------------------
     k32 = _randn_pool((NB, Hkv, BLOCK_SIZE, d), gen)
-    v32 = _randn_pool((NB, Hkv, d, BLOCK_SIZE), gen)
+    v32 = _randn_pool((NB, Hkv, BLOCK_SIZE, d), gen)
     if cfg.peaked_fraction > 0:
         nslots = NB * BLOCK_SIZE
         pick = torch.randperm(nslots, generator=gen)[: round(cfg.peaked_fraction * nslots)]
@@ -261,24 +263,24 @@ def generate(cfg, seed=None, *, poison=True, spare_blocks=0, shuffle_batch=False
     live = torch.arange(BLOCK_SIZE)[None, :] < occ[:, None]          # [NB, 16]
     k_scale = v_scale = None
     if cfg.kv_dtype == "i8":
-        k_cache, k_scale = _quantise_int8(k32, live, slot_dim=2)
-        v_cache, v_scale = _quantise_int8(v32, live, slot_dim=3)
+        k_tok, k_scale = _quantise_int8(k32, live)
+        v_tok, v_scale = _quantise_int8(v32, live)
         if poison:
             for blk in (occ < BLOCK_SIZE).nonzero().flatten().tolist():
                 n = int(occ[blk])
-                k_cache[blk, :, n:, :] = 127
-                v_cache[blk, :, :, n:] = -127
+                k_tok[blk, :, n:, :] = 127
+                v_tok[blk, :, n:, :] = -127
                 if n == 0:
                     k_scale[blk] = float("nan")
                     v_scale[blk] = float("nan")
     else:
         dt = _TORCH_DT[cfg.kv_dtype]
-        k_cache, v_cache = k32.to(dt), v32.to(dt)
+        k_tok, v_tok = k32.to(dt), v32.to(dt)
         if poison:
             for blk in (occ < BLOCK_SIZE).nonzero().flatten().tolist():
                 n = int(occ[blk])
-                k_cache[blk, :, n:, :] = float("nan")
-                v_cache[blk, :, :, n:] = float("nan")
+                k_tok[blk, :, n:, :] = float("nan")
+                v_tok[blk, :, n:, :] = float("nan")
     del k32, v32
 
     # ---- the step's new token: position L-1 of each sequence ------------------------
@@ -297,8 +299,10 @@ def generate(cfg, seed=None, *, poison=True, spare_blocks=0, shuffle_batch=False
         if poison:  # the slot the append must fill starts out as NaN
             for s in slots:
                 blk, off = divmod(s, BLOCK_SIZE)
-                k_cache[blk, :, off, :] = float("nan")
-                v_cache[blk, :, :, off] = float("nan")
+                k_tok[blk, :, off, :] = float("nan")
+                v_tok[blk, :, off, :] = float("nan")
+    k_cache, v_cache = encode_k(k_tok), encode_v(v_tok)
+    del k_tok, v_tok
 
     wl = Workload(cfg, q, k_cache, v_cache, k_scale, v_scale, tables,
                   torch.tensor(lens, dtype=torch.int32), slot_mapping, k_new, v_new, occ,
@@ -340,20 +344,37 @@ def relabel_blocks(wl: Workload, perm):
                    occupancy=mv(wl.occupancy))
 
 
-def _quantise_int8(x32, live, slot_dim):
-    """Symmetric int8 encoding per (block, KV head): scale = max|x| / 127 over the
-    block's live slots, x_q = round-half-even(x / scale) clamped to [-127, 127]
-    (Lecture 10's affine rule with zero point 0; In-depth §5.2 per-head scales)."""
-    NB, H = x32.shape[0], x32.shape[1]
-    shape = [NB, 1, 1, 1]
-    shape[slot_dim] = BLOCK_SIZE
-    m = live.reshape(shape).expand_as(x32)
+def _quantise_int8(x32, live):
+    """Symmetric int8 encoding per (block, KV head) of a token-major [NB, H, 16, d] pool:
+    scale = max|x| / 127 over the block's live slots, x_q = round-half-even(x / scale)
+    clamped to [-127, 127] (Lecture 10's affine rule with zero point 0; In-depth §5.2
+    per-head scales)."""
+    m = live[:, None, :, None].expand_as(x32)
     amax = torch.where(m, x32.abs(), torch.zeros(())).amax(dim=(2, 3))      # [NB, H]
     scale = (amax / 127.0).to(torch.float32)
     safe = torch.where(scale > 0, scale, torch.ones(()))
     xq = torch.round(x32 / safe[:, :, None, None]).clamp_(-127, 127)
     xq = torch.where(scale[:, :, None, None] > 0, xq, torch.zeros(()))
     return xq.to(torch.int8), scale
+
+
+def encode_k(k_tok):
+    """Token-major K [NB, H, 16, d] -> the cache format [NB, H, d/x, 16, x], x = 16 / element
+    bytes (each 16-byte column of the 16 tokens' rows contiguous)."""
+    NB, H, T, d = k_tok.shape
+    x = 16 // k_tok.element_size()
+    return k_tok.reshape(NB, H, T, d // x, x).permute(0, 1, 3, 2, 4).contiguous()
+
+
+def encode_v(v_tok):
+    """Token-major V [NB, H, 16, d] -> the cache format [NB, H, d, 16]."""
+    return v_tok.transpose(2, 3).contiguous()
+
+
+def k_token_rows(k_cache):
+    """The cache-format K pool viewed back as token-major [NB, H, 16, d] (a copy)."""
+    NB, H, C, T, x = k_cache.shape
+    return k_cache.permute(0, 1, 3, 2, 4).reshape(NB, H, T, C * x)
 
 
 def scaled(cfg, **changes) -> Config:
