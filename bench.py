@@ -4,10 +4,12 @@
 
 One step is one decode step of one attention layer of the Llama-3-8B-shaped workload
 (batch 64, 32 query / 8 KV heads, head_dim 128, bf16 KV, contexts U[512, 4096], seed
-1001): kv_append of the 64 new tokens followed by paged decode attention (context split
-+ log-sum-exp merge, or the single-pass kernel).  Inputs are resident in HBM before the
-timed region; two copies of the KV pool are used in turn so that consecutive steps do not
-find the previous step's KV in the 256 MB Infinity Cache.
+1001): kv_append of the 64 new tokens followed by paged decode attention -- by default
+the balanced kernel (the batch's blocks dealt evenly over the workgroups) and its merge;
+--path split / direct time the fixed-partition split + merge or the single-pass kernel.
+Inputs are resident in HBM before the timed region; two copies of the KV pool are used in
+turn so that consecutive steps do not find the previous step's KV in the 256 MB Infinity
+Cache.
 
 Printed: ONE JSON line.  value = algorithmic KV bytes per step / step time (GB/s);
 roofline.achieved = the same bytes / the attention kernel's mean duration, timed with
@@ -39,18 +41,21 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--path", choices=["split", "direct"], default="split")
+    ap.add_argument("--path", choices=["balanced", "split", "direct"], default="balanced")
+    ap.add_argument("--workgroups", type=int, default=0, help="balanced path; 0 = library default")
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="first run a 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
 
 
 class Runner:
     """Device-resident inputs of one workload and one decode step through the C ABI."""
 
-    def __init__(self, P, wl, path, partition, copies=2):
+    def __init__(self, P, wl, path, partition, copies=2, workgroups=0):
         import torch
         self.P, self.wl, self.torch = P, wl, torch
         c = wl.cfg
@@ -73,7 +78,10 @@ class Runner:
         self.sm = float(np.float32(c.sm_scale))
         self.out = torch.empty((c.batch, c.num_q_pos, c.num_q_heads, c.head_dim),
                                dtype=torch.float32, device=dev)
+        self.path = path
         self.split = path == "split" and c.num_q_pos == 1 and partition
+        if path == "split" and not self.split:
+            self.path = "direct"
         if self.split:
             self.pt = partition
             self.maxp = -(-int(wl.seq_lens.max()) // partition)
@@ -81,6 +89,10 @@ class Runner:
                                         dtype=torch.float32, device=dev)
             self.part_lse = torch.empty((c.batch, c.num_q_heads, self.maxp),
                                         dtype=torch.float32, device=dev)
+        if path == "balanced":
+            self.G = workgroups or P.paged_attn_balanced_workgroups(self.dims, c.num_q_pos)
+            nbytes = P.paged_attn_balanced_workspace_bytes(self.dims, c.num_q_pos, self.G)
+            self.ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
 
     def step(self, i, ev=None):
         P, c = self.P, self.wl.cfg
@@ -91,7 +103,13 @@ class Runner:
             P.kv_append(self.dims, self.k_new, self.v_new, self.slots, c.batch, kc, vc)
         if ev is not None:
             ev[1].record()
-        if self.split:
+        if self.path == "balanced":
+            P.paged_attn_balanced(self.dims, c.num_q_pos, self.q, kc, vc, ks, vs, self.tables,
+                                  self.lens, self.sm, self.G, self.ws, self.out)
+            if ev is not None:
+                ev[2].record()
+            P.paged_attn_balanced_merge(self.dims, c.num_q_pos, self.G, self.ws, self.out)
+        elif self.split:
             P.paged_decode_attn_split(self.dims, self.q, kc, vc, ks, vs, self.tables, self.lens,
                                       self.sm, self.pt, self.maxp, self.part_out, self.part_lse)
             if ev is not None:
@@ -142,41 +160,87 @@ def summarize(wl, wall, steps, app, attn, merge):
 
 
 def cpu_baseline(wl, seconds):
-    """The fp64 oracle on the first (sequence, KV head) pairs of the same workload until
-    about `seconds` of host time is spent; rate in the same unit (KV GB/s)."""
+    """The fp64 oracle, as it stands, run on the host over the same workload: whole
+    passes over all (sequence, KV head) pairs, repeated until about `seconds` of host time
+    is spent (a pass cut short when one pass alone is longer); rate in the same unit."""
+    import torch
     from oracle import attention, paging
     c = wl.cfg
-    raw = lambda x: None if x is None else (x.view(__import__("torch").int16).numpy()
-                                            if x.dtype.is_floating_point and x.element_size() == 2
-                                            else x.numpy())
+
+    def raw(x):
+        if x is None:
+            return None
+        return x.view(torch.int16).numpy() if x.dtype == torch.bfloat16 else x.numpy()
     kc, vc = raw(wl.k_cache), raw(wl.v_cache)
     if wl.slot_mapping is not None:
         kc, vc = paging.append(kc, vc, raw(wl.k_new), raw(wl.v_new), wl.slot_mapping.numpy())
     elem = {"f32": 4, "bf16": 2, "i8": 1}[c.kv_dtype]
     pairs_done, nbytes = 0, 0
     t0 = time.perf_counter()
-    for b in range(c.batch):
-        for g in range(c.num_kv_heads):
-            attention.paged_attention(raw(wl.q), c.q_dtype, kc, vc, c.kv_dtype,
-                                      wl.block_tables.numpy(), wl.seq_lens.numpy(),
-                                      float(np.float32(c.sm_scale)), c.num_q_pos,
-                                      raw(wl.k_scale), raw(wl.v_scale), pairs=[(b, g)])
-            pairs_done += 1
-            nbytes += int(wl.seq_lens[b]) * 2 * c.head_dim * elem
-            if time.perf_counter() - t0 > seconds:
+    done = False
+    while not done:
+        for b in range(c.batch):
+            for g in range(c.num_kv_heads):
+                attention.paged_attention(raw(wl.q), c.q_dtype, kc, vc, c.kv_dtype,
+                                          wl.block_tables.numpy(), wl.seq_lens.numpy(),
+                                          float(np.float32(c.sm_scale)), c.num_q_pos,
+                                          raw(wl.k_scale), raw(wl.v_scale), pairs=[(b, g)])
+                pairs_done += 1
+                nbytes += int(wl.seq_lens[b]) * 2 * c.head_dim * elem
+                done = time.perf_counter() - t0 > seconds
+                if done:
+                    break
+            if done:
                 break
-        if time.perf_counter() - t0 > seconds:
-            break
     dt = time.perf_counter() - t0
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": blas, "kind": "oracle",
-            "sample": f"{pairs_done} of {c.batch * c.num_kv_heads} (sequence, KV head) pairs of "
-                      f"{c.name} seed {wl.meta['seed']}, fp64 numpy, {dt:.1f} s",
+    npairs = c.batch * c.num_kv_heads
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas,
+            "kind": "oracle",
+            "sample": f"{pairs_done} (sequence, KV head) pairs ({pairs_done / npairs:.2f} passes "
+                      f"over the {npairs} of {c.name}, seed {wl.meta['seed']}), fp64 numpy, "
+                      f"{dt:.1f} s",
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+KERNEL_SOURCES = ["paged_gqa_decode_kv_amd/csrc/attn.hip", "paged_gqa_decode_kv_amd/csrc/pa_common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama3_8b_balanced_traffic.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from the committed counter summary,
+    or None if there is none or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def calibration_copy(torch, nbytes=1 << 30):
+    """A plain device-to-device copy of known size, for scaling the HBM counters."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def main():
@@ -191,12 +255,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate:
+        calibration_copy(torch)
 
     main_name = "llama3_8b"
     wl = W.generate(main_name, poison=False)
     part = args.partition or PARTITION[main_name]
-    r = Runner(P, wl, args.path, part)
-    res = summarize(wl, *_m(r, args), )
+    r = Runner(P, wl, args.path, part, workgroups=args.workgroups)
+    res = summarize(wl, *_m(r, args))
+    G = getattr(r, "G", None)
     del r
     torch.cuda.empty_cache()
 
@@ -205,17 +272,19 @@ def main():
         for name in ("llama2_70b_prefix", "long_128k", "verify_int8"):
             w2 = W.generate(name, poison=False)
             copies = 1 if name == "long_128k" else 2
-            path = "split" if PARTITION[name] else "direct"
-            r2 = Runner(P, w2, path, PARTITION[name], copies=copies)
+            r2 = Runner(P, w2, "balanced", None, copies=copies)
             s = summarize(w2, *_m(r2, args, steps=min(args.steps, 20), warmup=3))
-            s["path"] = path if r2.split else "direct"
-            s["partition_tokens"] = PARTITION[name] if r2.split else None
+            s["path"] = "balanced"
+            s["workgroups"] = r2.G
             s["pct_hbm_peak"] = s["kv_GBps"] / HBM_PEAK_GBS * 100
+            s["attn_kernel_frac_of_peak"] = s["attn_kernel_GBps"] / HBM_PEAK_GBS
             others[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in s.items()}
             del r2, w2
             torch.cuda.empty_cache()
 
     achieved = res["attn_kernel_GBps"]
+    kernel = {"balanced": "paged_attn_balanced_kernel", "split": "paged_attn_kernel (split)",
+              "direct": "paged_attn_kernel (direct)"}[args.path]
     line = {
         "metric": METRIC,
         "value": round(res["kv_GBps"], 2),
@@ -232,15 +301,15 @@ def main():
         "config": {"workload": "llama3_8b_layer_decode", "batch": 64, "q_heads": 32,
                    "kv_heads": 8, "head_dim": 128, "block_size": 16, "kv_dtype": "bf16",
                    "context": "uniform [512, 4096] (+ the appended token)", "seed": 1001,
-                   "path": args.path, "partition_tokens": part if args.path == "split" else None,
+                   "path": args.path, "workgroups": G,
+                   "partition_tokens": part if args.path == "split" else None,
                    "kv_bytes_per_step": res["kv_bytes"]},
         "us_per_step": round(res["us_per_step"], 2),
         "pct_hbm_peak": round(res["kv_GBps"] / HBM_PEAK_GBS * 100, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attn_kernel (split)" if args.path == "split" else
-                               "paged_attn_kernel (direct)",
-                     "kernel_us_mean": round(res["attn_kernel_us_mean"], 2),
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if args.path == "balanced" else None,
+                     "kernel": kernel, "kernel_us_mean": round(res["attn_kernel_us_mean"], 2),
                      "bytes_per_launch": res["kv_bytes"]},
         "timing": {k: round(v, 3) for k, v in res.items() if k.endswith("_us_mean") or
                    k.endswith("_us_median") or k.endswith("_us_p95")},

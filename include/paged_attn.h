@@ -182,18 +182,22 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
  * Every (KV head, query-row tile, sequence) segment of the batch is laid out, block after
  * block, in one flat list (KV head outermost, sequence innermost) and workgroup w takes the
  * contiguous slice [w * per, (w + 1) * per), per = ceil(total blocks / num_workgroups).  A
- * segment cut by slice boundaries is attended piecewise and its pieces are recombined
- * with the log-sum-exp identity (see lse_merge), inside this call: two kernels are
- * enqueued on `stream` (attention, then merge).
+ * segment that lies inside one slice is written to out (and out_lse) by this call; a
+ * segment cut by slice boundaries leaves one partial result per piece in the workspace,
+ * and paged_attn_balanced_merge, enqueued next on the same stream with the same
+ * arguments, recombines them with the log-sum-exp identity (see lse_merge).  The pair is
+ * the complete operation.
  *   num_q_pos    nq >= 1; q [B][nq][Hq][head_dim]; out [B][nq][Hq][head_dim] fp32
  *   out_lse      device, [B][nq][Hq] fp32 (natural log; -inf for a row that sees no token),
  *                or NULL
- *   num_workgroups >= 1; paged_attn_balanced_workgroups gives the number that runs
- *                concurrently on the current device, which is the intended value
+ *   num_workgroups >= 1; paged_attn_balanced_workgroups gives a good value for the current
+ *                device (twice its compute units)
  *   workspace    device, >= paged_attn_balanced_workspace_bytes(dims, nq, num_workgroups)
  *                bytes, 16-byte aligned; contents need no initialisation and are scratch
- *                for the duration of the call (calls sharing one workspace must be ordered)
- * B may be at most 2048 (PA_ERR_DIMS otherwise).  Other arguments as paged_verify_attn.
+ *                from this call to the end of the merge (calls sharing one workspace must be
+ *                ordered)
+ * B may be at most 2048 and B * max_blocks_per_seq below 2^31 (PA_ERR_DIMS otherwise).
+ * Other arguments as paged_verify_attn.
  */
 int paged_attn_balanced(const pa_dims* dims, int32_t num_q_pos, const void* q,
                         const void* k_cache, const void* v_cache, const float* k_scale,
@@ -202,13 +206,20 @@ int paged_attn_balanced(const pa_dims* dims, int32_t num_q_pos, const void* q,
                         void* workspace, size_t workspace_bytes, float* out, float* out_lse,
                         void* stream);
 
+/* Second half of paged_attn_balanced: writes the rows of cut segments (and of empty
+ * sequences: zeros, lse -inf) from the partials the attention call left in the workspace.
+ * dims, num_q_pos, num_workgroups, workspace, out and out_lse as in that call. */
+int paged_attn_balanced_merge(const pa_dims* dims, int32_t num_q_pos, int32_t num_workgroups,
+                              void* workspace, size_t workspace_bytes, float* out,
+                              float* out_lse, void* stream);
+
 /* Workspace bytes paged_attn_balanced needs (0 if the arguments are invalid). */
 size_t paged_attn_balanced_workspace_bytes(const pa_dims* dims, int32_t num_q_pos,
                                            int32_t num_workgroups);
 
-/* Workgroups of the balanced kernel that are resident at once on the current HIP device
- * (compute units x workgroups per unit); a negative PA_ERR_* code on failure.  This call
- * queries the device (HIP calls), unlike the argument checks. */
+/* A good num_workgroups for paged_attn_balanced on the current HIP device: two per compute
+ * unit, or fewer if the kernel cannot keep two resident per unit; a negative PA_ERR_* code
+ * on failure.  This call queries the device (HIP calls), unlike the argument checks. */
 int paged_attn_balanced_workgroups(const pa_dims* dims, int32_t num_q_pos);
 
 /* Text for a status code (static storage). */

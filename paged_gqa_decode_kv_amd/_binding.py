@@ -51,6 +51,7 @@ def _load(path=_LIB_PATH):
         "kv_gather": [D, P, P, P, P, I32, P, P, P],
         "paged_attn_balanced": [D, I32, P, P, P, P, P, P, P, F32, I32, P, ctypes.c_size_t, P, P, P],
         "paged_attn_balanced_workgroups": [D, I32],
+        "paged_attn_balanced_merge": [D, I32, I32, P, ctypes.c_size_t, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -164,4 +165,12 @@ def paged_attn_balanced(dims, num_q_pos, q, k_cache, v_cache, k_scale, v_scale, 
     _check("paged_attn_balanced", lib.paged_attn_balanced(
         ctypes.byref(dims), num_q_pos, _p(q), _p(k_cache), _p(v_cache), _p(k_scale), _p(v_scale),
         _p(block_tables), _p(seq_lens), sm_scale, num_workgroups, _p(workspace), nbytes, _p(out),
+        _p(out_lse), _stream(stream)))
+
+
+def paged_attn_balanced_merge(dims, num_q_pos, num_workgroups, workspace, out, out_lse=None,
+                              stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("paged_attn_balanced_merge", lib.paged_attn_balanced_merge(
+        ctypes.byref(dims), num_q_pos, num_workgroups, _p(workspace), nbytes, _p(out),
         _p(out_lse), _stream(stream)))

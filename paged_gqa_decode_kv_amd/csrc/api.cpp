@@ -212,6 +212,23 @@ size_t paged_attn_balanced_workspace_bytes(const pa_dims* dims, int32_t num_q_po
   return balanced_layout(dims, num_q_pos, num_workgroups).total;
 }
 
+namespace {
+int balanced_args(const pa_dims* dims, int32_t num_q_pos, int32_t num_workgroups, void* workspace,
+                  size_t workspace_bytes, float* out, float* out_lse, pa::AttnArgs* a) {
+  const BalancedLayout l = balanced_layout(dims, num_q_pos, num_workgroups);
+  if (workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return PA_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a->num_workgroups = num_workgroups;
+  a->ws_prefix = reinterpret_cast<int32_t*>(ws + l.prefix);
+  a->ws_lse = reinterpret_cast<float*>(ws + l.lse);
+  a->ws_out = reinterpret_cast<float*>(ws + l.out);
+  a->out = out;
+  a->ws_out_lse = out_lse;
+  return PA_OK;
+}
+}  // namespace
+
 int paged_attn_balanced(const pa_dims* dims, int32_t num_q_pos, const void* q,
                         const void* k_cache, const void* v_cache, const float* k_scale,
                         const float* v_scale, const int32_t* block_tables,
@@ -223,19 +240,30 @@ int paged_attn_balanced(const pa_dims* dims, int32_t num_q_pos, const void* q,
   st = check_balanced(dims, num_q_pos, num_workgroups);
   if (st != PA_OK) return st;
   if (!out || !workspace) return PA_ERR_NULL;
-  const BalancedLayout l = balanced_layout(dims, num_q_pos, num_workgroups);
-  if (workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
-    return PA_ERR_WORKSPACE;
   pa::AttnArgs a = make_args(dims, num_q_pos, q, k_cache, v_cache, k_scale, v_scale,
                              block_tables, seq_lens, sm_scale);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  a.num_workgroups = num_workgroups;
-  a.ws_prefix = reinterpret_cast<int32_t*>(ws + l.prefix);
-  a.ws_lse = reinterpret_cast<float*>(ws + l.lse);
-  a.ws_out = reinterpret_cast<float*>(ws + l.out);
-  a.out = out;
-  a.ws_out_lse = out_lse;
-  return pa::launch_balanced(a, dims->q_dtype, dims->kv_dtype, out, out_lse, stream);
+  st = balanced_args(dims, num_q_pos, num_workgroups, workspace, workspace_bytes, out, out_lse, &a);
+  if (st != PA_OK) return st;
+  return pa::launch_balanced(a, dims->q_dtype, dims->kv_dtype, stream);
+}
+
+int paged_attn_balanced_merge(const pa_dims* dims, int32_t num_q_pos, int32_t num_workgroups,
+                              void* workspace, size_t workspace_bytes, float* out,
+                              float* out_lse, void* stream) {
+  int st = check_balanced(dims, num_q_pos, num_workgroups);
+  if (st != PA_OK) return st;
+  if (!out || !workspace) return PA_ERR_NULL;
+  pa::AttnArgs a{};
+  a.num_seqs = dims->num_seqs;
+  a.num_q_heads = dims->num_q_heads;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.group = dims->num_q_heads / dims->num_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.num_q_pos = num_q_pos;
+  a.rows = num_q_pos * a.group;
+  st = balanced_args(dims, num_q_pos, num_workgroups, workspace, workspace_bytes, out, out_lse, &a);
+  if (st != PA_OK) return st;
+  return pa::launch_balanced_merge(a, out, out_lse, stream);
 }
 
 const char* paged_status_string(int status) {

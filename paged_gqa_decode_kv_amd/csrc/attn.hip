@@ -718,7 +718,9 @@ int occupancy_one() {
           &per_cu, reinterpret_cast<const void*>(&paged_attn_balanced_kernel<KV, D, NT, W, NBUF>),
           kWave * W, 0) != hipSuccess)
     return PA_ERR_LAUNCH;
-  const int64_t n = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+  // two workgroups per compute unit measured best on MI355X for all four workloads
+  // (three per unit make the slices, and so the per-piece start-up, more numerous)
+  const int64_t n = (int64_t)cus * (per_cu >= 2 ? 2 : 1);
   return n > 0x7fffffff ? 0x7fffffff : (int)n;
 }
 
@@ -777,11 +779,8 @@ int balanced_workgroups(int q_dtype, int kv_dtype, int head_dim, int32_t rows) {
   return dispatch(a, q_dtype, kv_dtype, kOccupancy, nullptr);
 }
 
-int launch_balanced(const AttnArgs& a, int q_dtype, int kv_dtype, float* out, float* out_lse,
-                    void* stream) {
-  int st = dispatch(a, q_dtype, kv_dtype, kLaunchBalanced, stream);
-  if (st != PA_OK) return st;
-  return launch_balanced_merge(a, out, out_lse, stream);
+int launch_balanced(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream) {
+  return dispatch(a, q_dtype, kv_dtype, kLaunchBalanced, stream);
 }
 
 }  // namespace pa

@@ -41,9 +41,8 @@ int launch_attention(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream)
 int balanced_row_tile(int32_t rows);
 // workgroups that fit on the current device at once for the balanced kernel (< 0: error)
 int balanced_workgroups(int q_dtype, int kv_dtype, int head_dim, int32_t rows);
-// attention + merge on `stream`; the AttnArgs workspace pointers must be set
-int launch_balanced(const AttnArgs& a, int q_dtype, int kv_dtype, float* out, float* out_lse,
-                    void* stream);
+// balanced attention on `stream`; the AttnArgs workspace pointers must be set
+int launch_balanced(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream);
 
 // merge of the balanced mode's partials into out [B][nq][Hq][d] (and out_lse, if given)
 int launch_balanced_merge(const AttnArgs& a, float* out, float* out_lse, void* stream);

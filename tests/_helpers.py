@@ -70,6 +70,7 @@ def gpu_attention(P, wl, dv, seq_lens=None, split=None, balanced=None):
         out_lse = torch.full((c.batch, c.num_q_pos, c.num_q_heads), float("nan"), device="cuda:0")
         P.paged_attn_balanced(d, c.num_q_pos, dv.q, dv.k_cache, dv.v_cache, dv.k_scale,
                               dv.v_scale, dv.block_tables, lens, sm, G, ws, out, out_lse)
+        P.paged_attn_balanced_merge(d, c.num_q_pos, G, ws, out, out_lse)
         return out, None, out_lse
     if split is None:
         if c.num_q_pos == 1:

@@ -1,0 +1,141 @@
+"""The C ABI on a host without a GPU: the library loads, exports every function the header
+declares, and every argument check returns its status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_gqa_decode_kv_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const\s+char\s*\*)\s*\*?\s*"
+                       r"(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["kv_append", "paged_decode_attn", "paged_verify_attn", "paged_decode_attn_split",
+              "lse_merge", "paged_attn_balanced", "paged_attn_balanced_merge",
+              "paged_attn_balanced_workspace_bytes", "paged_attn_balanced_workgroups",
+              "paged_split_workspace_bytes", "kv_gather", "paged_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(P.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def _dims(**kw):
+    base = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=64, max_blocks_per_seq=4,
+                num_blocks=16, q_dtype="bf16", kv_dtype="bf16")
+    base.update(kw)
+    return P.make_dims(**base)
+
+
+FAKE = 0x1000  # a non-NULL address that is never dereferenced: every call below fails its checks
+
+
+def _decode(d, q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, t=FAKE, lens=FAKE, out=FAKE):
+    args = [ctypes.c_void_p(x) if x else None for x in (q, k, v, ks, vs, t, lens)]
+    return P.lib.paged_decode_attn(ctypes.byref(d), *args, 0.125,
+                                   ctypes.c_void_p(out) if out else None, None)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(block_size=8), -5),
+    (dict(head_dim=96), -4),
+    (dict(num_seqs=0), -2),
+    (dict(num_q_heads=6, num_kv_heads=4), -2),
+    (dict(num_kv_heads=0), -2),
+    (dict(max_blocks_per_seq=0), -2),
+    (dict(num_blocks=0), -2),
+    (dict(q_dtype="f32", kv_dtype="bf16"), -3),
+    (dict(q_dtype="bf16", kv_dtype="f32"), -3),
+])
+def test_decode_dimension_and_type_checks(change, status):
+    d = _dims()
+    for k, v in change.items():
+        setattr(d, k, {"f32": 0, "bf16": 1, "i8": 2}.get(v, v) if isinstance(v, str) else v)
+    assert _decode(d) == status
+
+
+def test_null_pointer_checks():
+    d = _dims()
+    assert P.lib.paged_decode_attn(None, None, None, None, None, None, None, None, 0.1, None,
+                                   None) == -1
+    assert _decode(d, q=0) == -1
+    assert _decode(d, lens=0) == -1
+    assert _decode(d, out=0) == -1
+    di8 = _dims(kv_dtype="i8")
+    assert _decode(di8) == -1                 # int8 needs both scale arrays
+    assert _decode(di8, ks=FAKE) == -1
+
+
+def test_append_checks():
+    d = _dims()
+    f = ctypes.c_void_p(FAKE)
+    assert P.lib.kv_append(ctypes.byref(d), f, f, f, -1, f, f, None) == -2
+    assert P.lib.kv_append(ctypes.byref(d), f, f, f, 0, f, f, None) == 0     # nothing to do
+    assert P.lib.kv_append(ctypes.byref(d), None, f, f, 4, f, f, None) == -1
+    di8 = _dims(kv_dtype="i8")
+    assert P.lib.kv_append(ctypes.byref(di8), f, f, f, 4, f, f, None) == -3
+
+
+def test_verify_and_split_checks():
+    d = _dims()
+    f = ctypes.c_void_p(FAKE)
+    assert P.lib.paged_verify_attn(ctypes.byref(d), 0, f, f, f, None, None, f, f, 0.1, f,
+                                   None) == -2
+    for pt, mp in [(0, 4), (24, 4), (-16, 4), (16, 0)]:
+        assert P.lib.paged_decode_attn_split(ctypes.byref(d), f, f, f, None, None, f, f, 0.1,
+                                             pt, mp, f, f, None) == -6
+        assert P.lib.lse_merge(ctypes.byref(d), f, f, f, pt, mp, f, None, None) == -6
+    assert P.lib.paged_decode_attn_split(ctypes.byref(d), f, f, f, None, None, f, f, 0.1, 32, 4,
+                                         None, f, None) == -1
+    assert P.lib.kv_gather(ctypes.byref(d), f, f, f, f, -1, f, f, None) == -2
+    assert P.lib.kv_gather(ctypes.byref(d), f, f, f, f, 0, f, f, None) == 0
+
+
+def test_balanced_checks_and_sizes():
+    d = _dims()
+    f = ctypes.c_void_p(FAKE)
+    n = P.paged_attn_balanced_workspace_bytes(d, 1, 8)
+    # prefix (3 ints -> 256 B) | lse (8 + 2*1*2 partials x 16 rows) | rows (x 64 dims)
+    npid = 8 + 2 * 2
+    assert n == 256 + ((npid * 16 * 4 + 255) // 256) * 256 + npid * 16 * 64 * 4
+    assert P.paged_attn_balanced_workspace_bytes(d, 6, 8) > n          # 24 rows -> 32-row tile
+    assert P.paged_attn_balanced_workspace_bytes(d, 0, 8) == 0
+    assert P.paged_attn_balanced_workspace_bytes(d, 1, 0) == 0
+    big = _dims(num_seqs=4096)
+    assert P.paged_attn_balanced_workspace_bytes(big, 1, 8) == 0       # more than 2048 sequences
+    call = P.lib.paged_attn_balanced
+    assert call(ctypes.byref(d), 1, f, f, f, None, None, f, f, 0.1, 8, f, n - 1, f, None,
+                None) == -8
+    assert call(ctypes.byref(d), 1, f, f, f, None, None, f, f, 0.1, 8, ctypes.c_void_p(FAKE + 4),
+                n, f, None, None) == -8                                 # misaligned
+    assert call(ctypes.byref(d), 1, f, f, f, None, None, f, f, 0.1, 0, f, n, f, None, None) == -2
+    assert P.lib.paged_attn_balanced_merge(ctypes.byref(d), 1, 8, f, n - 1, f, None, None) == -8
+    assert P.lib.paged_split_workspace_bytes(ctypes.byref(d), 3) == 2 * 8 * 3 * (64 + 1) * 4
+
+
+def test_status_strings():
+    for st in range(0, -9, -1):
+        assert P.paged_status_string(st) and P.paged_status_string(st) != "unknown status"
+    assert P.paged_status_string(-99) == "unknown status"
+
+
+def test_binding_raises_on_status():
+    d = _dims(head_dim=80)
+    with pytest.raises(P.PagedAttnError) as e:
+        P.paged_decode_attn(d, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 0.1, FAKE)
+    assert e.value.status == -4

@@ -227,6 +227,9 @@ def test_balanced_workspace_errors(P):
                               dv.seq_lens, 0.1, 4, ws, out)
     assert e.value.status == -8
     assert P.paged_attn_balanced_workgroups(d, 1) >= 256
+    with pytest.raises(P.PagedAttnError) as e:
+        P.paged_attn_balanced_merge(d, 1, 4, ws, out)
+    assert e.value.status == -8
 
 
 # ---- invariances, bit for bit --------------------------------------------------------
