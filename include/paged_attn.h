@@ -178,10 +178,11 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
 
 /*
  * paged_attn_balanced -- decode (nq = 1) or causal verify (nq > 1) attention with the work
- * dealt evenly over num_workgroups workgroups, whatever the spread of sequence lengths.
- * Every (KV head, query-row tile, sequence) segment of the batch is laid out, block after
- * block, in one flat list (KV head outermost, sequence innermost) and workgroup w takes the
- * contiguous slice [w * per, (w + 1) * per), per = ceil(total blocks / num_workgroups).  A
+ * dealt evenly over the waves of num_workgroups workgroups (four waves each), whatever the
+ * spread of sequence lengths.  Every (KV head, query-row tile, sequence) segment of the
+ * batch is laid out, block after block, in one flat list (KV head outermost, sequence
+ * innermost) and wave v takes the contiguous slice [v * per, (v + 1) * per),
+ * per = ceil(total blocks / waves).  A
  * segment that lies inside one slice is written to out (and out_lse) by this call; a
  * segment cut by slice boundaries leaves one partial result per piece in the workspace,
  * and paged_attn_balanced_merge, enqueued next on the same stream with the same
@@ -196,7 +197,8 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
  *                bytes, 16-byte aligned; contents need no initialisation and are scratch
  *                from this call to the end of the merge (calls sharing one workspace must be
  *                ordered)
- * B may be at most 2048 and B * max_blocks_per_seq below 2^31 (PA_ERR_DIMS otherwise).
+ * B may be at most 2048, and B * max_blocks_per_seq * num_kv_heads * (row tiles) and
+ * num_blocks * num_kv_heads must stay below 2^31 (PA_ERR_DIMS otherwise).
  * Other arguments as paged_verify_attn.
  */
 int paged_attn_balanced(const pa_dims* dims, int32_t num_q_pos, const void* q,

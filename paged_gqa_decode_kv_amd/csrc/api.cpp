@@ -82,7 +82,8 @@ BalancedLayout balanced_layout(const pa_dims* d, int32_t nq, int32_t num_workgro
   const int64_t rows = (int64_t)nq * (d->num_q_heads / d->num_kv_heads);
   const int rt = pa::balanced_row_tile((int32_t)rows);
   const int64_t nrg = (rows + rt - 1) / rt;
-  const int64_t npid = (int64_t)num_workgroups + (int64_t)d->num_kv_heads * nrg * d->num_seqs;
+  const int64_t npid = (int64_t)num_workgroups * pa::balanced_waves() +
+                       (int64_t)d->num_kv_heads * nrg * d->num_seqs;
   BalancedLayout l;
   l.prefix = 0;
   l.lse = align256(((size_t)d->num_seqs + 1) * sizeof(int32_t));
@@ -95,9 +96,16 @@ int check_balanced(const pa_dims* d, int32_t nq, int32_t num_workgroups) {
   int st = check_dims(d);
   if (st != PA_OK) return st;
   if (nq < 1 || num_workgroups < 1 || d->num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_DIMS;
-  if ((int64_t)nq * (d->num_q_heads / d->num_kv_heads) > INT_MAX) return PA_ERR_DIMS;
-  // block positions in the flat list of one KV head are int32 inside the kernel
-  if ((int64_t)d->num_seqs * d->max_blocks_per_seq > INT_MAX) return PA_ERR_DIMS;
+  const int64_t rows = (int64_t)nq * (d->num_q_heads / d->num_kv_heads);
+  if (rows > INT_MAX) return PA_ERR_DIMS;
+  if ((int64_t)num_workgroups * pa::balanced_waves() > INT_MAX) return PA_ERR_DIMS;
+  // inside the kernel block positions of the flat list, block counts of a slice and tile
+  // indices (physical block * KV heads + head) are int32
+  const int rt = pa::balanced_row_tile((int32_t)rows);
+  const int64_t nrg = (rows + rt - 1) / rt;
+  if ((int64_t)d->num_seqs * d->max_blocks_per_seq > INT_MAX / (d->num_kv_heads * nrg))
+    return PA_ERR_DIMS;
+  if (d->num_blocks > INT_MAX / d->num_kv_heads) return PA_ERR_DIMS;
   return PA_OK;
 }
 
@@ -220,6 +228,7 @@ int balanced_args(const pa_dims* dims, int32_t num_q_pos, int32_t num_workgroups
     return PA_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a->num_workgroups = num_workgroups;
+  a->num_workers = num_workgroups * pa::balanced_waves();
   a->ws_prefix = reinterpret_cast<int32_t*>(ws + l.prefix);
   a->ws_lse = reinterpret_cast<float*>(ws + l.lse);
   a->ws_out = reinterpret_cast<float*>(ws + l.out);

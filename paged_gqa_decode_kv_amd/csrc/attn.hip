@@ -272,32 +272,111 @@ template <int D> struct IsInt8<I8Kv<D>> { static constexpr bool value = true; };
 // Where a unit writes its rows.
 enum OutMode { kDirect = 0, kSplit = 1, kBalanced = 2 };
 
-// One unit of work: query rows [16*NT*rg, 16*NT*(rg+1)) of KV head g of sequence b, over
-// that sequence's tokens [lo, hi) (lo a multiple of 16).  The W waves of the workgroup
-// take interleaved blocks; their partial results are merged through LDS and wave 0
-// writes the normalised rows (and, except in direct mode, their log-sum-exp).
-// `slot` is the partition index (split mode) or the partial id (balanced mode).
-// Every wave of the workgroup must call this together (it contains barriers).
-template <class KV, int D, int NT, int W, int NBUF>
-__device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int b, int g, int rg,
-                                            int L, int lo, int hi, int64_t slot,
-                                            float* out_lse = nullptr) {
-  constexpr int ND = D / 16;
-  constexpr bool kInt8 = IsInt8<KV>::value;
-  constexpr int kStage = 64;  // table entries staged in LDS per wave
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int row16 = lane & 15;
-  const int grp = lane >> 4;
+// Running online-softmax state of one wave's query rows (a tile of 16 * NT rows) over
+// the blocks it has consumed: the output accumulators (O^T layout), and per row the
+// running max (log2 domain, equal in the four lanes of a row) and this lane's share of the
+// running sum.  For int8 the V scales are folded into P relative to v_ref.
+template <class KV, int D, int NT>
+struct Rows {
+  static constexpr int ND = D / 16;
+  static constexpr bool kInt8 = IsInt8<KV>::value;
+  f32x4 acc[NT][ND];
+  float m[NT], l[NT];
+  float v_ref, inv_vref256;
 
-  const int jb = lo / kBlockTokens;
-  const int je = (hi + kBlockTokens - 1) / kBlockTokens;
-  // this wave's blocks: jb + w + W * k for k in [0, nk)
-  const int nk = je - jb - w > 0 ? (je - jb - w + W - 1) / W : 0;
+  __device__ __forceinline__ void reset(float vref) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      m[nt] = -INFINITY;
+      l[nt] = 0.f;
+#pragma unroll
+      for (int t = 0; t < ND; ++t) acc[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    v_ref = kInt8 ? vref : 1.f;
+    inv_vref256 = kInt8 ? 256.f / vref : 1.f;
+  }
 
-  // ---- query rows handled by this lane -----------------------------------------------
-  typename KV::Q qop[NT];
-  int lim[NT];  // tokens [lo, lim) are visible to this lane's row
+  // One 16-token block whose first token is tok0: rows see tokens < lim[nt] (lim_min is
+  // the smallest over the wave's rows); tokens >= hi are past the sequence end and their
+  // V may be poisoned.  sc = softmax scale * log2(e) (times the block's K scale for int8);
+  // vs = the block's V scale (int8).
+  __device__ __forceinline__ void update(const typename KV::Q* qop, const int* lim, int lim_min,
+                                         int hi, typename KV::K& kk, typename KV::V& vv,
+                                         int tok0, float sc, float vs, int grp) {
+    float vfac = 1.f;
+    if constexpr (kInt8) {
+      vfac = vs * inv_vref256;
+      if (vfac > 4096.f) {
+        // this block's V scale is far above the reference: move the reference to it so
+        // p * vfac stays well inside the fp16 range
+        const float r = v_ref / vs;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int t = 0; t < ND; ++t) acc[nt][t] *= r;
+        v_ref = vs;
+        inv_vref256 = 256.f / vs;
+        vfac = 256.f;
+      }
+    }
+    const bool need_mask = tok0 + kBlockTokens > lim_min;
+    f32x4 pr[NT];
+    float alpha[NT];
+    const auto& km = KV::k_mat(kk);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 sv = KV::qk(km, qop[nt]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = sv[e] * sc;
+        if (need_mask && tok0 + 4 * grp + e >= lim[nt]) x = -INFINITY;
+        sv[e] = x;
+      }
+      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      bm = wave_max_across_groups(bm);
+      const float mn = fmaxf(m[nt], bm);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - mu);
+      m[nt] = mn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pr[nt][e] = __builtin_amdgcn_exp2f(sv[e] - mu);
+      l[nt] = l[nt] * alpha[nt] + ((pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]));
+    }
+    bool rescale = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) rescale |= (alpha[nt] != 1.f);
+    if (__any(rescale)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int t = 0; t < ND; ++t) acc[nt][t] *= alpha[nt];
+    }
+    if (tok0 + kBlockTokens > hi) KV::mask_v(vv, hi - tok0, grp);
+    const auto& vm = KV::v_mat(vv);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) KV::pv(acc[nt], vm, pr[nt], vfac);
+  }
+
+  // After the last block: full row sums in every lane of the row; int8 scale undone.
+  __device__ __forceinline__ void totals() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      l[nt] = wave_sum_across_groups(l[nt]);
+      if (kInt8) {
+        const float f = v_ref * (1.f / 256.f);
+#pragma unroll
+        for (int t = 0; t < ND; ++t) acc[nt][t] *= f;
+      }
+    }
+  }
+};
+
+// Query rows of row tile rg for KV head g of sequence b: the MFMA B operand of each 16-row
+// tile and the causal limit of this lane's row (tokens [.., lim) visible; lim capped at
+// hi).  Returns the smallest limit over the tile's rows.
+template <class KV, int D, int NT>
+__device__ __forceinline__ int load_rows(const AttnArgs& a, int b, int g, int rg, int L, int hi,
+                                         typename KV::Q* qop, int* lim, int row16, int grp) {
   const int row_base = rg * 16 * NT;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -311,14 +390,73 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
     lam = lam < 0 ? 0 : lam;
     lim[nt] = lam < hi ? lam : hi;
   }
-  // smallest visible limit of the rows in this row group (uniform)
-  int lim_min;
-  {
-    const int i0 = row_base / a.group;
-    int lam0 = L - a.num_q_pos + 1 + i0;
-    lam0 = lam0 < 0 ? 0 : lam0;
-    lim_min = lam0 < hi ? lam0 : hi;
+  const int i0 = row_base / a.group;
+  int lam0 = L - a.num_q_pos + 1 + i0;
+  lam0 = lam0 < 0 ? 0 : lam0;
+  return lam0 < hi ? lam0 : hi;
+}
+
+// Normalise a wave's finished rows and write them: to out (direct mode, plus out_lse if
+// given), to a partition slot (split mode) or to a partial id of the workspace (balanced).
+template <class KV, int D, int NT>
+__device__ __forceinline__ void write_rows(const AttnArgs& a, const Rows<KV, D, NT>& st,
+                                           OutMode mode, int b, int g, int rg, int64_t slot,
+                                           float* out_lse, int row16, int grp) {
+  constexpr int ND = D / 16;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int rl = nt * 16 + row16;  // row within the row tile
+    const int r = rg * 16 * NT + rl;
+    if (r >= a.rows) continue;
+    const int i = r / a.group;
+    const int h = g * a.group + r % a.group;
+    const float lsum = st.l[nt];
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float lse = lsum > 0.f ? (st.m[nt] + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+    const int64_t orow = (int64_t)(b * a.num_q_pos + i) * a.num_q_heads + h;
+    float* dst;
+    float* lse_dst = nullptr;
+    if (mode == kDirect) {
+      dst = a.out + orow * D;
+      if (out_lse != nullptr) lse_dst = out_lse + orow;
+    } else if (mode == kSplit) {
+      dst = a.out + (orow * a.max_parts + slot) * D;
+      lse_dst = a.part_lse + orow * a.max_parts + slot;
+    } else {
+      dst = a.ws_out + (slot * 16 * NT + rl) * D;
+      lse_dst = a.ws_lse + slot * 16 * NT + rl;
+    }
+#pragma unroll
+    for (int t = 0; t < ND; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * grp) = st.acc[nt][t] * inv;
+    if (lse_dst != nullptr && grp == 0) *lse_dst = lse;
   }
+}
+
+// One unit of work: query rows [16*NT*rg, 16*NT*(rg+1)) of KV head g of sequence b, over
+// that sequence's tokens [lo, hi) (lo a multiple of 16).  The W waves of the workgroup
+// take interleaved blocks; their partial results are merged through LDS and wave 0
+// writes the normalised rows (and, except in direct mode, their log-sum-exp).
+// `slot` is the partition index (split mode).  Every wave of the workgroup must call this
+// together (it contains barriers).
+template <class KV, int D, int NT, int W, int NBUF>
+__device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int b, int g, int rg,
+                                            int L, int lo, int hi, int64_t slot) {
+  constexpr int ND = D / 16;
+  constexpr bool kInt8 = IsInt8<KV>::value;
+  constexpr int kStage = 64;  // table entries staged in LDS per wave
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int row16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const int jb = lo / kBlockTokens;
+  const int je = (hi + kBlockTokens - 1) / kBlockTokens;
+  // this wave's blocks: jb + w + W * k for k in [0, nk)
+  const int nk = je - jb - w > 0 ? (je - jb - w + W - 1) / W : 0;
+
+  typename KV::Q qop[NT];
+  int lim[NT];
+  const int lim_min = load_rows<KV, D, NT>(a, b, g, rg, L, hi, qop, lim, row16, grp);
 
   const size_t tile_bytes = (size_t)kBlockTokens * D * KV::kElem;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache);
@@ -379,17 +517,8 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
       if (s0 > 0.f && s0 < 3.0e38f) v_ref = s0;
     }
   }
-  float inv_vref256 = kInt8 ? 256.f / v_ref : 1.f;
-
-  f32x4 acc[NT][ND];
-  float m_run[NT], l_run[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-#pragma unroll
-    for (int t = 0; t < ND; ++t) acc[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  Rows<KV, D, NT> st;
+  st.reset(v_ref);
 
   // Loads are issued unconditionally: a slot with no block (past the end, or a table
   // entry outside the pool) reads tile (0, g), which is always inside the pool, and is
@@ -402,63 +531,9 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   };
   auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, const Slot& sl) {
     if (sl.ph < 0) return;
-    const int jx = jb + w + W * kidx;
-    float sc = a.scale_log2;
-    float vfac = 1.f;
-    if constexpr (kInt8) {
-      sc *= sl.ks;
-      const float vs = sl.vs;
-      vfac = vs * inv_vref256;
-      if (vfac > 4096.f) {
-        // this block's V scale is far above the reference: move the reference to it so
-        // p * vfac stays well inside the fp16 range
-        const float r = v_ref / vs;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int t = 0; t < ND; ++t) acc[nt][t] *= r;
-        v_ref = vs;
-        inv_vref256 = 256.f / vs;
-        vfac = 256.f;
-      }
-    }
-    const int tok0 = jx * kBlockTokens;
-    const bool need_mask = tok0 + kBlockTokens > lim_min;
-    f32x4 pr[NT];
-    float alpha[NT];
-    const auto& km = KV::k_mat(kk);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 s = KV::qk(km, qop[nt]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = s[e] * sc;
-        if (need_mask && tok0 + 4 * grp + e >= lim[nt]) x = -INFINITY;
-        s[e] = x;
-      }
-      float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      bm = wave_max_across_groups(bm);
-      const float mn = fmaxf(m_run[nt], bm);
-      const float mu = (mn == -INFINITY) ? 0.f : mn;
-      alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - mu);
-      m_run[nt] = mn;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pr[nt][e] = __builtin_amdgcn_exp2f(s[e] - mu);
-      l_run[nt] = l_run[nt] * alpha[nt] + ((pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]));
-    }
-    bool rescale = false;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) rescale |= (alpha[nt] != 1.f);
-    if (__any(rescale)) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int t = 0; t < ND; ++t) acc[nt][t] *= alpha[nt];
-    }
-    if (tok0 + kBlockTokens > hi) KV::mask_v(vv, hi - tok0, grp);
-    const auto& vm = KV::v_mat(vv);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) KV::pv(acc[nt], vm, pr[nt], vfac);
+    const int tok0 = (jb + w + W * kidx) * kBlockTokens;
+    st.update(qop, lim, lim_min, hi, kk, vv, tok0, a.scale_log2 * (kInt8 ? sl.ks : 1.f), sl.vs,
+              grp);
   };
 
   {
@@ -482,17 +557,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
       }
     }
   }
-
-  // ---- per-wave totals ---------------------------------------------------------------
-  const float out_factor = kInt8 ? v_ref * (1.f / 256.f) : 1.f;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    l_run[nt] = wave_sum_across_groups(l_run[nt]);
-    if (kInt8) {
-#pragma unroll
-      for (int t = 0; t < ND; ++t) acc[nt][t] *= out_factor;
-    }
-  }
+  st.totals();
 
   // ---- merge the W waves through LDS (wave 0 finishes) -------------------------------
   if constexpr (W > 1) {
@@ -503,71 +568,40 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         if (grp == 0) {
-          sm_m[w - 1][nt * 16 + row16] = m_run[nt];
-          sm_l[w - 1][nt * 16 + row16] = l_run[nt];
+          sm_m[w - 1][nt * 16 + row16] = st.m[nt];
+          sm_l[w - 1][nt * 16 + row16] = st.l[nt];
         }
 #pragma unroll
-        for (int t = 0; t < ND; ++t) sm_acc[w - 1][nt][t][lane] = acc[nt][t];
+        for (int t = 0; t < ND; ++t) sm_acc[w - 1][nt][t][lane] = st.acc[nt][t];
       }
     }
     __syncthreads();
     if (w == 0) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        float M = m_run[nt];
+        float M = st.m[nt];
 #pragma unroll
         for (int x = 0; x < W - 1; ++x) M = fmaxf(M, sm_m[x][nt * 16 + row16]);
         const float Mu = (M == -INFINITY) ? 0.f : M;
-        const float f0 = __builtin_amdgcn_exp2f(m_run[nt] - Mu);
-        float lsum = l_run[nt] * f0;
+        const float f0 = __builtin_amdgcn_exp2f(st.m[nt] - Mu);
+        float lsum = st.l[nt] * f0;
 #pragma unroll
-        for (int t = 0; t < ND; ++t) acc[nt][t] *= f0;
+        for (int t = 0; t < ND; ++t) st.acc[nt][t] *= f0;
 #pragma unroll
         for (int x = 0; x < W - 1; ++x) {
           const float fx = __builtin_amdgcn_exp2f(sm_m[x][nt * 16 + row16] - Mu);
           lsum += sm_l[x][nt * 16 + row16] * fx;
 #pragma unroll
-          for (int t = 0; t < ND; ++t) acc[nt][t] += sm_acc[x][nt][t][lane] * fx;
+          for (int t = 0; t < ND; ++t) st.acc[nt][t] += sm_acc[x][nt][t][lane] * fx;
         }
-        m_run[nt] = M;
-        l_run[nt] = lsum;
+        st.m[nt] = M;
+        st.l[nt] = lsum;
       }
     }
-    // LDS (merge buffers and the staged table) is reused by the workgroup's next unit
     __syncthreads();
     if (w != 0) return;
   }
-
-  // ---- normalise and write -----------------------------------------------------------
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int rl = nt * 16 + row16;  // row within the row group
-    const int r = row_base + rl;
-    if (r >= a.rows) continue;
-    const int i = r / a.group;
-    const int h = g * a.group + r % a.group;
-    const float lsum = l_run[nt];
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const float lse = lsum > 0.f ? (m_run[nt] + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
-    const int64_t orow = (int64_t)(b * a.num_q_pos + i) * a.num_q_heads + h;
-    float* dst;
-    float* lse_dst = nullptr;
-    if (mode == kDirect) {
-      dst = a.out + orow * D;
-      if (out_lse != nullptr) lse_dst = out_lse + orow;
-    } else if (mode == kSplit) {
-      dst = a.out + (orow * a.max_parts + slot) * D;
-      lse_dst = a.part_lse + orow * a.max_parts + slot;
-    } else {
-      dst = a.ws_out + (slot * 16 * NT + rl) * D;
-      lse_dst = a.ws_lse + slot * 16 * NT + rl;
-    }
-#pragma unroll
-    for (int t = 0; t < ND; ++t) {
-      *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * grp) = acc[nt][t] * inv;
-    }
-    if (lse_dst != nullptr && grp == 0) *lse_dst = lse;
-  }
+  write_rows<KV, D, NT>(a, st, mode, b, g, rg, slot, nullptr, row16, grp);
 }
 
 __device__ __forceinline__ int clamp_len(int L, int max_blocks) {
@@ -617,19 +651,32 @@ void paged_attn_kernel(AttnArgs a) {
 
 // Balanced mode.  All (segment, block) pairs of the batch are laid out in one flat list --
 // segment j = (KV head g, row group rg, sequence b) in order j = (g * nrg + rg) * B + b,
-// holding ceil(L_b / 16) blocks -- and workgroup w takes the contiguous slice
-// [w * per, (w + 1) * per) with per = ceil(total / num_workgroups).  Every workgroup
-// therefore streams the same number of blocks whatever the spread of sequence lengths.
-// A segment that lies wholly inside one slice is written out directly; otherwise each
-// piece becomes a partial result at partial id w + j (unique: along the slices both w and
-// j only grow) and a merge kernel combines the pieces of each cut segment.
+// holding ceil(L_b / 16) blocks -- and wave v (of num_workgroups * W) takes the contiguous
+// slice [v * per, (v + 1) * per) with per = ceil(total / waves).  Every wave therefore
+// streams the same number of blocks whatever the spread of sequence lengths, and it
+// streams them without a break: its ring of tile loads runs on across segment boundaries,
+// and the next segment's query rows are loaded while the current segment's last blocks
+// are still being consumed.  A segment that lies wholly inside one slice is written out
+// directly; otherwise each piece becomes a partial result at partial id v + j (unique:
+// along the slices both v and j only grow) and the merge kernel combines the pieces.
+// s_waitcnt immediate for vmcnt(0) with the other counters left open (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmem0 = 0x0F70;
+
 template <class KV, int D, int NT, int W, int NBUF>
 __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(WavesPerEU<KV, NT>::value)))
 void paged_attn_balanced_kernel(AttnArgs a) {
+  constexpr bool kInt8 = IsInt8<KV>::value;
+  constexpr int kStage = 64;
   __shared__ int s_pref[kMaxBalancedSeqs + 1];
   const int64_t wid = xcd_logical_id();
   if (wid >= a.num_workgroups) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int row16 = lane & 15;
+  const int grp = lane >> 4;
   const int B = a.num_seqs;
+
   // prefix over sequences of their block counts, by the whole workgroup
   __shared__ int s_scan[kWave * W];
   int carry = 0;
@@ -652,41 +699,201 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   if (wid == 0) {
     for (int k = threadIdx.x; k <= B; k += kWave * W) a.ws_prefix[k] = s_pref[k];
   }
+  // (no barrier below this point: the waves are independent)
+
+  // (the host keeps B * max_blocks * Hkv * nrg below 2^31, so flat positions are int32)
   const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
-  const int64_t T = s_pref[B];
-  const int64_t total = T * a.num_kv_heads * nrg;
-  const int64_t per = (total + a.num_workgroups - 1) / a.num_workgroups;
-  int64_t x = wid * per;
-  const int64_t x1 = x + per < total ? x + per : total;
-  while (x < x1) {
-    const int64_t gr = x / T;
-    const int r = (int)(x - gr * T);
-    // sequence holding flat block r: largest b with s_pref[b] <= r (then r < s_pref[b + 1])
-    int lo_b = 0, hi_b = B - 1;
+  const int T = __builtin_amdgcn_readfirstlane(s_pref[B]);
+  const int total = T * a.num_kv_heads * nrg;
+  const int per = (int)(((int64_t)total + a.num_workers - 1) / a.num_workers);
+  const int64_t v = wid * W + w;
+  if (v * per >= total) return;
+  const int x0 = (int)(v * per);
+  const int x1 = total - x0 > per ? x0 + per : total;
+  const int n = x1 - x0;  // blocks of this wave
+
+  // segment of flat position x (uniform in the wave)
+  struct Seg {
+    int j, start, end;
+    int b, g, rg;
+  };
+  auto locate = [&](int x) -> Seg {
+    Seg sg;
+    const int gr = x / T;
+    const int r = x - gr * T;
+    int lo_b = 0, hi_b = B - 1;  // largest b with s_pref[b] <= r
     while (lo_b < hi_b) {
       const int mid = (lo_b + hi_b + 1) >> 1;
-      if (s_pref[mid] <= r) lo_b = mid; else hi_b = mid - 1;
+      if (__builtin_amdgcn_readfirstlane(s_pref[mid]) <= r) lo_b = mid; else hi_b = mid - 1;
     }
-    const int b = lo_b;
-    const int64_t seg_end = gr * T + s_pref[b + 1];
-    const int64_t xe = seg_end < x1 ? seg_end : x1;
-    const int g = (int)(gr / nrg);
-    const int rg = (int)(gr % nrg);
-    const int L = clamp_len(a.seq_lens[b], a.max_blocks);
-    const int lb = r - s_pref[b];
-    const int lo = lb * kBlockTokens;
-    const int hi_t = (lb + (int)(xe - x)) * kBlockTokens;
-    const int hi = hi_t < L ? hi_t : L;
-    const int64_t j = gr * B + b;
-    const int64_t s0 = gr * T + s_pref[b];
-    if (x == s0 && xe == seg_end) {
-      // the whole segment lies in this slice: write the final rows directly
-      attend_unit<KV, D, NT, W, NBUF>(a, kDirect, b, g, rg, L, lo, hi, 0, a.ws_out_lse);
-    } else {
-      attend_unit<KV, D, NT, W, NBUF>(a, kBalanced, b, g, rg, L, lo, hi, wid + j);
+    sg.b = lo_b;
+    sg.g = gr / nrg;
+    sg.rg = gr % nrg;
+    sg.j = gr * B + lo_b;
+    sg.start = gr * T + __builtin_amdgcn_readfirstlane(s_pref[lo_b]);
+    sg.end = gr * T + __builtin_amdgcn_readfirstlane(s_pref[lo_b + 1]);
+    return sg;
+  };
+
+  const size_t tile_bytes = (size_t)kBlockTokens * D * KV::kElem;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache);
+
+  // ---- per-wave LDS staging: tile index (physical block * Hkv + g, -1 = none) and int8
+  // scales of this wave's blocks k0 .. k0 + 63; lane i resolves its own block's segment.
+  __shared__ int s_tile[W][kStage];
+  __shared__ float s_ks[W][kInt8 ? kStage : 1];
+  __shared__ float s_vs[W][kInt8 ? kStage : 1];
+  auto stage = [&](int k0) {
+    const int k = k0 + lane;
+    int tile = -1;
+    float ks = 0.f, vs = 0.f;
+    if (k < n) {
+      const int x = x0 + k;
+      const int gr = x / T;
+      const int r = x - gr * T;
+      int lo_b = 0, hi_b = B - 1;
+      while (lo_b < hi_b) {
+        const int mid = (lo_b + hi_b + 1) >> 1;
+        if (s_pref[mid] <= r) lo_b = mid; else hi_b = mid - 1;
+      }
+      const int g = gr / nrg;
+      const int ph = a.block_tables[(int64_t)lo_b * a.max_blocks + (r - s_pref[lo_b])];
+      if (ph >= 0 && (int64_t)ph < a.num_blocks) {
+        tile = (int)kv_tile(ph, g, a.num_kv_heads);
+        if constexpr (kInt8) {
+          ks = a.k_scale[tile];
+          vs = a.v_scale[tile];
+        }
+      }
     }
-    x = xe;
+    s_tile[w][lane] = tile;
+    if constexpr (kInt8) {
+      s_ks[w][lane] = ks;
+      s_vs[w][lane] = vs;
+    }
+  };
+  auto lds_uniform_f = [](const float& x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+  };
+  struct Slot {
+    int tile;
+    float ks, vs;
+  };
+  auto slot_at = [&](int k) -> Slot {
+    Slot sl{-1, 0.f, 0.f};
+    if (k < n) {
+      const int si = k & (kStage - 1);
+      sl.tile = __builtin_amdgcn_readfirstlane(s_tile[w][si]);
+      if constexpr (kInt8) {
+        sl.ks = lds_uniform_f(s_ks[w][si]);
+        sl.vs = lds_uniform_f(s_vs[w][si]);
+      }
+    }
+    return sl;
+  };
+  stage(0);
+
+  // ---- current segment (being consumed) and the prefetched next one -----------------
+  Seg cur;
+  cur.end = x0;  // nothing consumed yet
+  cur.j = -1;
+  int L = 0, lim_min = 0, lim[NT];
+  typename KV::Q qop[NT], qnext[NT];
+  int lim_next[NT], lim_min_next = 0;
+  Seg nxt;                 // segment whose rows sit in qnext (valid while nxt.j >= 0)
+  nxt.j = -1;
+  int iss_end = x0;        // end of the segment of the newest issued block
+  Rows<KV, D, NT> st;
+  st.reset(1.f);
+
+  auto rows_hi = [&](const Seg& sg, int Ls) {
+    // tokens this wave may read in the segment: up to the end of its slice or the sequence
+    const int last = sg.end < x1 ? sg.end : x1;
+    const int hi_t = (last - sg.start) * kBlockTokens;
+    return hi_t < Ls ? hi_t : Ls;
+  };
+  auto finish = [&]() {
+    st.totals();
+    const bool whole = cur.start >= x0 && cur.end <= x1;
+    write_rows<KV, D, NT>(a, st, whole ? kDirect : kBalanced, cur.b, cur.g, cur.rg, v + cur.j,
+                          a.ws_out_lse, row16, grp);
+  };
+  auto issue = [&](typename KV::K& kk, typename KV::V& vv, int kn, const Slot& sl) {
+    const int x = x0 + kn;
+    if (kn < n && x >= iss_end) {
+      // first block of a new segment: fetch its query rows ahead of time
+      const Seg sg = locate(x);
+      iss_end = sg.end;
+      if (nxt.j < 0) {
+        nxt = sg;
+        const int Ls = clamp_len(a.seq_lens[sg.b], a.max_blocks);
+        lim_min_next = load_rows<KV, D, NT>(a, sg.b, sg.g, sg.rg, Ls, rows_hi(sg, Ls), qnext,
+                                            lim_next, row16, grp);
+      }
+    }
+    const int64_t tl = sl.tile >= 0 ? sl.tile : 0;
+    KV::load_k(kk, kbase + tl * tile_bytes, lane);
+    KV::load_v(vv, vbase + tl * tile_bytes, row16, grp);
+  };
+  auto consume = [&](typename KV::K& kk, typename KV::V& vv, int k, const Slot& sl) {
+    if (k >= n) return;
+    const int x = x0 + k;
+    if (x >= cur.end) {
+      if (cur.j >= 0) finish();
+      const bool pre = nxt.j >= 0 && x >= nxt.start && x < nxt.end;
+      cur = pre ? nxt : locate(x);
+      L = clamp_len(a.seq_lens[cur.b], a.max_blocks);
+      const int hi = rows_hi(cur, L);
+      if (pre) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          qop[nt] = qnext[nt];
+          lim[nt] = lim_next[nt];
+        }
+        lim_min = lim_min_next;
+        nxt.j = -1;
+      } else {
+        // (rare: two segments began within the blocks in flight) load the rows now and
+        // wait for them here, so that no later wait has to allow for a pending query load
+        lim_min = load_rows<KV, D, NT>(a, cur.b, cur.g, cur.rg, L, hi, qop, lim, row16, grp);
+        __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+        if (nxt.j >= 0 && nxt.j <= cur.j) nxt.j = -1;
+      }
+      float vref = 1.f;
+      if constexpr (kInt8) {
+        if (sl.tile >= 0 && sl.vs > 0.f && sl.vs < 3.0e38f) vref = sl.vs;
+      }
+      st.reset(vref);
+    }
+    if (sl.tile < 0) return;
+    const int tok0 = (x - cur.start) * kBlockTokens;
+    st.update(qop, lim, lim_min, rows_hi(cur, L), kk, vv, tok0,
+              a.scale_log2 * (kInt8 ? sl.ks : 1.f), sl.vs, grp);
+  };
+
+  {
+    typename KV::K kb[NBUF];
+    typename KV::V vb[NBUF];
+    Slot sb[NBUF];
+#pragma unroll
+    for (int s = 0; s < NBUF - 1; ++s) {
+      sb[s] = slot_at(s);
+      issue(kb[s], vb[s], s, sb[s]);
+    }
+    for (int k = 0; k < n; k += NBUF) {
+#pragma unroll
+      for (int s = 0; s < NBUF; ++s) {
+        const int kn = k + s + NBUF - 1;  // block issued now, consumed NBUF - 1 steps later
+        const int sn = (s + NBUF - 1) % NBUF;
+        if ((kn & (kStage - 1)) == 0 && kn < n) stage(kn);
+        sb[sn] = slot_at(kn);
+        issue(kb[sn], vb[sn], kn, sb[sn]);
+        consume(kb[s], vb[s], k + s, sb[s]);
+      }
+    }
   }
+  if (cur.j >= 0) finish();
 }
 
 template <class KV, int D, int NT, int W, int NBUF>
@@ -771,6 +978,8 @@ int launch_attention(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream)
 }
 
 int balanced_row_tile(int32_t rows) { return rows <= 16 ? 16 : 32; }
+
+int balanced_waves() { return PA_WAVES; }
 
 int balanced_workgroups(int q_dtype, int kv_dtype, int head_dim, int32_t rows) {
   AttnArgs a{};

@@ -25,9 +25,10 @@ struct AttnArgs {
   int32_t split;            // 0: direct, 1: write partials
   float scale_log2;         // sm_scale * log2(e)
   // balanced mode
-  int32_t num_workgroups;   // workgroups the flat block list is dealt to
-  float* ws_out;            // partial rows  [num_workgroups + segments][row tile][head_dim]
-  float* ws_lse;            // partial lse   [num_workgroups + segments][row tile]
+  int32_t num_workgroups;   // workgroups launched
+  int32_t num_workers;      // waves the flat block list is dealt to (workgroups * waves)
+  float* ws_out;            // partial rows  [num_workers + segments][row tile][head_dim]
+  float* ws_lse;            // partial lse   [num_workers + segments][row tile]
   int32_t* ws_prefix;       // block-count prefix over sequences [num_seqs + 1]
   float* ws_out_lse;        // final lse [B][nq][Hq] for whole segments, or null
 };
@@ -39,6 +40,8 @@ int launch_attention(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream)
 
 // rows of one partial (16 or 32): the row tile the kernel uses for `rows` query rows
 int balanced_row_tile(int32_t rows);
+// waves per workgroup of the balanced kernel
+int balanced_waves();
 // workgroups that fit on the current device at once for the balanced kernel (< 0: error)
 int balanced_workgroups(int q_dtype, int kv_dtype, int head_dim, int32_t rows);
 // balanced attention on `stream`; the AttnArgs workspace pointers must be set

@@ -63,8 +63,8 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
 
 
 // Balanced mode: segment j (KV head g, row group rg, sequence b) occupies flat blocks
-// [S_j, S_{j+1}) with S_j = (g * nrg + rg) * T + prefix[b]; workgroup w covered
-// [w * per, (w + 1) * per), so the workgroups that wrote a partial for segment j are
+// [S_j, S_{j+1}) with S_j = (g * nrg + rg) * T + prefix[b]; attention wave w covered
+// [w * per, (w + 1) * per), so the waves that wrote a partial for segment j are
 // w = S_j / per .. (S_{j+1} - 1) / per, at partial ids w + j.  A segment inside one slice
 // was written out by the attention kernel and is skipped here; an empty segment gets zeros.
 // One workgroup per segment, one wave per query row of its row tile.
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
 
   const int64_t T = a.ws_prefix[B];
   const int64_t total = T * a.num_kv_heads * nrg;
-  const int64_t per = (total + a.num_workgroups - 1) / a.num_workgroups;
+  const int64_t per = (total + a.num_workers - 1) / a.num_workers;
   const int64_t s0 = gr * T + a.ws_prefix[b];
   const int64_t s1 = gr * T + a.ws_prefix[b + 1];
   const int64_t w0 = s1 > s0 ? s0 / per : 0;

@@ -110,14 +110,20 @@ def test_balanced_checks_and_sizes():
     d = _dims()
     f = ctypes.c_void_p(FAKE)
     n = P.paged_attn_balanced_workspace_bytes(d, 1, 8)
-    # prefix (3 ints -> 256 B) | lse (8 + 2*1*2 partials x 16 rows) | rows (x 64 dims)
-    npid = 8 + 2 * 2
+    # prefix (3 ints -> 256 B) | lse (8 workgroups x 4 waves + 2*1*2 segments partials
+    # x 16 rows) | rows (x 64 dims)
+    npid = 8 * 4 + 2 * 2
     assert n == 256 + ((npid * 16 * 4 + 255) // 256) * 256 + npid * 16 * 64 * 4
     assert P.paged_attn_balanced_workspace_bytes(d, 6, 8) > n          # 24 rows -> 32-row tile
     assert P.paged_attn_balanced_workspace_bytes(d, 0, 8) == 0
     assert P.paged_attn_balanced_workspace_bytes(d, 1, 0) == 0
     big = _dims(num_seqs=4096)
     assert P.paged_attn_balanced_workspace_bytes(big, 1, 8) == 0       # more than 2048 sequences
+    # flat block positions and tile indices must stay int32
+    assert P.paged_attn_balanced_workspace_bytes(_dims(num_seqs=2048, max_blocks_per_seq=1 << 19),
+                                                 1, 8) == 0
+    assert P.paged_attn_balanced_workspace_bytes(_dims(num_blocks=1 << 30), 1, 8) == 0
+    assert P.paged_attn_balanced_workspace_bytes(_dims(num_blocks=1 << 29), 1, 8) > 0
     call = P.lib.paged_attn_balanced
     assert call(ctypes.byref(d), 1, f, f, f, None, None, f, f, 0.1, 8, f, n - 1, f, None,
                 None) == -8
