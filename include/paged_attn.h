@@ -24,6 +24,11 @@
  *   v_cache[num_blocks][num_kv_heads][head_dim][16]
  *
  * so one (block, KV head) tile of K or V is one contiguous 16 x head_dim piece of memory.
+ * Tile (block n, head g) starts kv_tile_stride * (n * num_kv_heads + g) elements into its
+ * cache; kv_tile_stride = 16 * head_dim packs the tiles densely (the shapes above), and
+ * kv_tile_stride = 32 * head_dim with v_cache = k_cache + 16 * head_dim lays K and V of one
+ * (block, head) side by side in a single allocation [num_blocks][num_kv_heads][2][tile],
+ * which HBM streams faster than two separate pools (each tile read becomes one 2-tile run).
  * Inside a K tile, element k of the token at offset o sits at [k / x][o][k % x]: each
  * 16-byte column of the 16 tokens' K rows is contiguous.  Inside a V tile, element k of
  * that token sits at [k][o].
@@ -40,6 +45,7 @@
  *  - Return value: PA_OK (0) or a negative PA_ERR_* code.  Every argument check runs on
  *    the host before any HIP call, so a rejected call touches no GPU state.
  *    PA_ERR_LAUNCH reports a failed kernel launch (hipGetLastError).
+ *  - q, k_cache, v_cache and out must be 16-byte aligned (PA_ERR_ALIGN otherwise).
  *  - Device-side contract: table entries for logical blocks < ceil(seq_len/16) name
  *    physical blocks in [0, num_blocks).  An entry outside that range is not read: its
  *    tokens are skipped.  seq_lens[b] larger than 16 * max_blocks_per_seq is cut to that
@@ -69,7 +75,8 @@ enum {
   PA_ERR_PARTITION = -6,  /* partition_tokens not a positive multiple of 16, or
                              max_partitions < 1                                            */
   PA_ERR_LAUNCH = -7,     /* a kernel launch failed (or a device query failed)             */
-  PA_ERR_WORKSPACE = -8   /* workspace smaller than the size query returns, or misaligned  */
+  PA_ERR_WORKSPACE = -8,  /* workspace smaller than the size query returns, or misaligned  */
+  PA_ERR_ALIGN = -9       /* q, k_cache, v_cache or out not 16-byte aligned                */
 };
 
 /* Shapes and element types shared by every call. */
@@ -83,6 +90,10 @@ typedef struct pa_dims {
   int64_t num_blocks;         /* physical blocks in each of k_cache / v_cache (>= 1)       */
   int32_t q_dtype;            /* PA_F32 or PA_BF16                                         */
   int32_t kv_dtype;           /* PA_F32, PA_BF16 or PA_I8                                  */
+  int64_t kv_tile_stride;     /* elements from one (block, KV head) tile to the next in
+                                 k_cache and in v_cache; 0 means 16 * head_dim (dense).
+                                 Otherwise >= 16 * head_dim and a multiple of 16 bytes
+                                 (PA_ERR_DIMS)                                             */
 } pa_dims;
 /* Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, I8). */
 

@@ -17,6 +17,7 @@ PA_F32, PA_BF16, PA_I8 = 0, 1, 2
 PA_OK = 0
 PA_ERR_NULL, PA_ERR_DIMS, PA_ERR_DTYPE, PA_ERR_HEAD_DIM = -1, -2, -3, -4
 PA_ERR_BLOCK_SIZE, PA_ERR_PARTITION, PA_ERR_LAUNCH, PA_ERR_WORKSPACE = -5, -6, -7, -8
+PA_ERR_ALIGN = -9
 
 _DTYPE_CODE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8,
                "f32": PA_F32, "bf16": PA_BF16, "i8": PA_I8}
@@ -33,7 +34,7 @@ class pa_dims(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int64), ("q_dtype", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32)]
+                ("kv_dtype", ctypes.c_int32), ("kv_tile_stride", ctypes.c_int64)]
 
 
 def _load(path=_LIB_PATH):
@@ -71,9 +72,11 @@ LIB_PATH = _LIB_PATH
 
 
 def make_dims(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
-              q_dtype, kv_dtype, block_size=16):
+              q_dtype, kv_dtype, block_size=16, kv_tile_stride=0):
+    """kv_tile_stride: elements between consecutive (block, KV head) tiles (0 = dense)."""
     return pa_dims(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                   max_blocks_per_seq, num_blocks, _DTYPE_CODE[q_dtype], _DTYPE_CODE[kv_dtype])
+                   max_blocks_per_seq, num_blocks, _DTYPE_CODE[q_dtype], _DTYPE_CODE[kv_dtype],
+                   kv_tile_stride)
 
 
 def _p(x):

@@ -12,6 +12,8 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_BF16 ? 2 : 1); }
+
 int check_dims(const pa_dims* d) {
   if (d == nullptr) return PA_ERR_NULL;
   if (d->block_size != 16) return PA_ERR_BLOCK_SIZE;
@@ -22,8 +24,21 @@ int check_dims(const pa_dims* d) {
   if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_DIMS;
   // token positions are int32 inside the kernels
   if ((int64_t)d->max_blocks_per_seq * 16 > INT_MAX) return PA_ERR_DIMS;
+  if (d->kv_tile_stride != 0) {
+    const int eb = d->kv_dtype == PA_F32 ? 4 : (d->kv_dtype == PA_BF16 ? 2 : 1);
+    if (d->kv_tile_stride < 16 * (int64_t)d->head_dim || d->kv_tile_stride > (INT64_MAX >> 40) ||
+        (d->kv_tile_stride * eb) % 16 != 0)
+      return PA_ERR_DIMS;
+  }
   return PA_OK;
 }
+
+// elements from one (block, KV head) tile to the next
+int64_t tile_stride(const pa_dims* d) {
+  return d->kv_tile_stride != 0 ? d->kv_tile_stride : 16 * (int64_t)d->head_dim;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int check_attn_types(const pa_dims* d) {
   if (d->q_dtype == PA_F32 && d->kv_dtype == PA_F32) return PA_OK;
@@ -40,6 +55,7 @@ int check_attn_inputs(const pa_dims* d, const void* q, const void* k, const void
   if (st != PA_OK) return st;
   if (!q || !k || !v || !tables || !lens) return PA_ERR_NULL;
   if (d->kv_dtype == PA_I8 && (!ks || !vs)) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return PA_ERR_ALIGN;
   return PA_OK;
 }
 
@@ -61,6 +77,7 @@ pa::AttnArgs make_args(const pa_dims* d, int32_t nq, const void* q, const void* 
   a.head_dim = d->head_dim;
   a.max_blocks = d->max_blocks_per_seq;
   a.num_blocks = d->num_blocks;
+  a.tile_stride = tile_stride(d) * elem_bytes(d->kv_dtype);
   a.num_q_pos = nq;
   a.rows = nq * a.group;
   a.scale_log2 = sm_scale * kLog2e;
@@ -69,8 +86,6 @@ pa::AttnArgs make_args(const pa_dims* d, int32_t nq, const void* q, const void* 
   a.split = 0;
   return a;
 }
-
-int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_BF16 ? 2 : 1); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -123,8 +138,8 @@ int kv_append(const pa_dims* dims, const void* k_new, const void* v_new,
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
   return pa::launch_append(k_new, v_new, slot_mapping, num_tokens, dims->num_kv_heads,
-                           dims->head_dim, dims->num_blocks, elem_bytes(dims->kv_dtype), k_cache,
-                           v_cache, stream);
+                           dims->head_dim, dims->num_blocks, tile_stride(dims),
+                           elem_bytes(dims->kv_dtype), k_cache, v_cache, stream);
 }
 
 int paged_verify_attn(const pa_dims* dims, int32_t num_q_pos, const void* q,
@@ -134,6 +149,7 @@ int paged_verify_attn(const pa_dims* dims, int32_t num_q_pos, const void* q,
   int st = check_attn_inputs(dims, q, k_cache, v_cache, k_scale, v_scale, block_tables, seq_lens);
   if (st != PA_OK) return st;
   if (!out) return PA_ERR_NULL;
+  if (!aligned16(out)) return PA_ERR_ALIGN;
   if (num_q_pos < 1 || (int64_t)num_q_pos * (dims->num_q_heads / dims->num_kv_heads) > INT_MAX)
     return PA_ERR_DIMS;
   pa::AttnArgs a = make_args(dims, num_q_pos, q, k_cache, v_cache, k_scale, v_scale,
@@ -160,6 +176,7 @@ int paged_decode_attn_split(const pa_dims* dims, const void* q, const void* k_ca
   if (partition_tokens <= 0 || partition_tokens % 16 != 0 || max_partitions < 1)
     return PA_ERR_PARTITION;
   if (!part_out || !part_lse) return PA_ERR_NULL;
+  if (!aligned16(part_out)) return PA_ERR_ALIGN;
   pa::AttnArgs a = make_args(dims, 1, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                              seq_lens, sm_scale);
   a.out = part_out;
@@ -201,8 +218,8 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
   if (!k_cache || !v_cache || !block_tables || !seq_lens || !k_out || !v_out) return PA_ERR_NULL;
   return pa::launch_gather(k_cache, v_cache, block_tables, seq_lens, dims->num_seqs,
                            dims->num_kv_heads, dims->head_dim, dims->max_blocks_per_seq,
-                           dims->num_blocks, max_len, elem_bytes(dims->kv_dtype), k_out, v_out,
-                           stream);
+                           dims->num_blocks, tile_stride(dims), max_len,
+                           elem_bytes(dims->kv_dtype), k_out, v_out, stream);
 }
 
 int paged_attn_balanced_workgroups(const pa_dims* dims, int32_t num_q_pos) {
@@ -249,6 +266,7 @@ int paged_attn_balanced(const pa_dims* dims, int32_t num_q_pos, const void* q,
   st = check_balanced(dims, num_q_pos, num_workgroups);
   if (st != PA_OK) return st;
   if (!out || !workspace) return PA_ERR_NULL;
+  if (!aligned16(out)) return PA_ERR_ALIGN;
   pa::AttnArgs a = make_args(dims, num_q_pos, q, k_cache, v_cache, k_scale, v_scale,
                              block_tables, seq_lens, sm_scale);
   st = balanced_args(dims, num_q_pos, num_workgroups, workspace, workspace_bytes, out, out_lse, &a);
@@ -286,6 +304,7 @@ const char* paged_status_string(int status) {
     case PA_ERR_PARTITION: return "partition_tokens must be a positive multiple of 16 and max_partitions >= 1";
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_WORKSPACE: return "workspace too small or not 16-byte aligned";
+    case PA_ERR_ALIGN: return "q, k_cache, v_cache or out not 16-byte aligned";
     default: return "unknown status";
   }
 }

@@ -23,7 +23,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const T* __restrict__ k_new, const T* __restrict__ v_new,
     const int64_t* __restrict__ slot_mapping, int64_t total, int32_t num_kv_heads,
-    int32_t head_dim, int64_t num_blocks, T* __restrict__ k_cache, T* __restrict__ v_cache) {
+    int32_t head_dim, int64_t num_blocks, int64_t tile_stride, T* __restrict__ k_cache,
+    T* __restrict__ v_cache) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int k = (int)(idx % head_dim);
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   if (slot < 0 || slot >= num_blocks * kBlockTokens) return;
   const int64_t blk = slot / kBlockTokens;
   const int off = (int)(slot % kBlockTokens);
-  const int64_t tile = kv_tile(blk, g, num_kv_heads) * (int64_t)kBlockTokens * head_dim;
+  const int64_t tile = kv_tile(blk, g, num_kv_heads) * tile_stride;
   k_cache[tile + k_elem<sizeof(T)>(off, k)] = k_new[idx];
   v_cache[tile + v_elem(off, k)] = v_new[idx];
 }
@@ -43,7 +44,8 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     int64_t total, int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks,
-    int64_t num_blocks, int32_t max_len, T* __restrict__ k_out, T* __restrict__ v_out) {
+    int64_t num_blocks, int64_t tile_stride, int32_t max_len, T* __restrict__ k_out,
+    T* __restrict__ v_out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   // idx enumerates [B][Hkv][max_len][head_dim]
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(
   const int32_t phys = block_tables[(int64_t)b * max_blocks + tpos / kBlockTokens];
   if (phys < 0 || phys >= num_blocks) return;
   const int off = tpos % kBlockTokens;
-  const int64_t tile = kv_tile(phys, g, num_kv_heads) * (int64_t)kBlockTokens * head_dim;
+  const int64_t tile = kv_tile(phys, g, num_kv_heads) * tile_stride;
   k_out[idx] = k_cache[tile + k_elem<sizeof(T)>(off, k)];
   v_out[idx] = v_cache[tile + v_elem(off, k)];
 }
@@ -66,29 +68,30 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(
 template <typename T>
 int append_t(const void* k_new, const void* v_new, const int64_t* slot_mapping,
              int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
-             void* k_cache, void* v_cache, hipStream_t s) {
+             int64_t tile_stride, void* k_cache, void* v_cache, hipStream_t s) {
   const int64_t total = (int64_t)num_tokens * num_kv_heads * head_dim;
   const int64_t grid = (total + 255) / 256;
   if (grid > 0x7fffffff) return PA_ERR_DIMS;
   hipLaunchKernelGGL(kv_append_kernel<T>, dim3((unsigned)grid), dim3(256), 0, s,
                      static_cast<const T*>(k_new), static_cast<const T*>(v_new), slot_mapping,
-                     total, num_kv_heads, head_dim, num_blocks, static_cast<T*>(k_cache),
-                     static_cast<T*>(v_cache));
+                     total, num_kv_heads, head_dim, num_blocks, tile_stride,
+                     static_cast<T*>(k_cache), static_cast<T*>(v_cache));
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 template <typename T>
 int gather_t(const void* k_cache, const void* v_cache, const int32_t* block_tables,
              const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-             int32_t max_blocks, int64_t num_blocks, int32_t max_len, void* k_out, void* v_out,
-             hipStream_t s) {
+             int32_t max_blocks, int64_t num_blocks, int64_t tile_stride, int32_t max_len,
+             void* k_out, void* v_out, hipStream_t s) {
   const int64_t total = (int64_t)num_seqs * num_kv_heads * max_len * head_dim;
   const int64_t grid = (total + 255) / 256;
   if (grid > 0x7fffffff) return PA_ERR_DIMS;
   hipLaunchKernelGGL(kv_gather_kernel<T>, dim3((unsigned)grid), dim3(256), 0, s,
                      static_cast<const T*>(k_cache), static_cast<const T*>(v_cache),
                      block_tables, seq_lens, total, num_kv_heads, head_dim, max_blocks,
-                     num_blocks, max_len, static_cast<T*>(k_out), static_cast<T*>(v_out));
+                     num_blocks, tile_stride, max_len, static_cast<T*>(k_out),
+                     static_cast<T*>(v_out));
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -96,29 +99,32 @@ int gather_t(const void* k_cache, const void* v_cache, const int32_t* block_tabl
 
 int launch_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                  int64_t num_blocks, int elem_bytes, void* k_cache, void* v_cache,
-                  void* stream) {
+                  int64_t num_blocks, int64_t tile_stride, int elem_bytes, void* k_cache,
+                  void* v_cache, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (elem_bytes == 4)
     return append_t<uint32_t>(k_new, v_new, slot_mapping, num_tokens, num_kv_heads, head_dim,
-                              num_blocks, k_cache, v_cache, s);
+                              num_blocks, tile_stride, k_cache, v_cache, s);
   return append_t<uint16_t>(k_new, v_new, slot_mapping, num_tokens, num_kv_heads, head_dim,
-                            num_blocks, k_cache, v_cache, s);
+                            num_blocks, tile_stride, k_cache, v_cache, s);
 }
 
 int launch_gather(const void* k_cache, const void* v_cache, const int32_t* block_tables,
                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
-                  int32_t head_dim, int32_t max_blocks, int64_t num_blocks, int32_t max_len,
-                  int elem_bytes, void* k_out, void* v_out, void* stream) {
+                  int32_t head_dim, int32_t max_blocks, int64_t num_blocks, int64_t tile_stride,
+                  int32_t max_len, int elem_bytes, void* k_out, void* v_out, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (elem_bytes == 4)
     return gather_t<uint32_t>(k_cache, v_cache, block_tables, seq_lens, num_seqs, num_kv_heads,
-                              head_dim, max_blocks, num_blocks, max_len, k_out, v_out, s);
+                              head_dim, max_blocks, num_blocks, tile_stride, max_len, k_out,
+                              v_out, s);
   if (elem_bytes == 2)
     return gather_t<uint16_t>(k_cache, v_cache, block_tables, seq_lens, num_seqs, num_kv_heads,
-                              head_dim, max_blocks, num_blocks, max_len, k_out, v_out, s);
+                              head_dim, max_blocks, num_blocks, tile_stride, max_len, k_out,
+                              v_out, s);
   return gather_t<uint8_t>(k_cache, v_cache, block_tables, seq_lens, num_seqs, num_kv_heads,
-                           head_dim, max_blocks, num_blocks, max_len, k_out, v_out, s);
+                           head_dim, max_blocks, num_blocks, tile_stride, max_len, k_out,
+                              v_out, s);
 }
 
 }  // namespace pa

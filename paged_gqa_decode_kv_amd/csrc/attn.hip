@@ -458,7 +458,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   int lim[NT];
   const int lim_min = load_rows<KV, D, NT>(a, b, g, rg, L, hi, qop, lim, row16, grp);
 
-  const size_t tile_bytes = (size_t)kBlockTokens * D * KV::kElem;
+  const int64_t tile_bytes = a.tile_stride;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache);
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
@@ -663,8 +663,21 @@ void paged_attn_kernel(AttnArgs a) {
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmem0 = 0x0F70;
 
+// The balanced kernel runs at most two workgroups of W = 4 waves per compute unit (two
+// waves per SIMD), so it may use the registers of two waves (fp32 with two row tiles:
+// of one).
+#ifndef PA_BAL_WAVES_PER_EU
+#define PA_BAL_WAVES_PER_EU 2
+#endif
+template <class KV, int NT> struct BalancedWavesPerEU {
+  static constexpr int value = WavesPerEU<KV, NT>::value < PA_BAL_WAVES_PER_EU
+                                   ? WavesPerEU<KV, NT>::value
+                                   : PA_BAL_WAVES_PER_EU;
+};
+
 template <class KV, int D, int NT, int W, int NBUF>
-__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(WavesPerEU<KV, NT>::value)))
+__global__ __launch_bounds__(kWave* W)
+__attribute__((amdgpu_waves_per_eu(BalancedWavesPerEU<KV, NT>::value)))
 void paged_attn_balanced_kernel(AttnArgs a) {
   constexpr bool kInt8 = IsInt8<KV>::value;
   constexpr int kStage = 64;
@@ -735,7 +748,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     return sg;
   };
 
-  const size_t tile_bytes = (size_t)kBlockTokens * D * KV::kElem;
+  const int64_t tile_bytes = a.tile_stride;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache);
 

@@ -18,6 +18,7 @@ struct AttnArgs {
   float* part_lse;   // split only: per-partition log-sum-exp
   int32_t num_seqs, num_q_heads, num_kv_heads, group, head_dim, max_blocks;
   int64_t num_blocks;
+  int64_t tile_stride;      // bytes from one (block, KV head) tile to the next in each cache
   int32_t num_q_pos;        // query positions per sequence
   int32_t rows;             // query rows per (sequence, KV head) = num_q_pos * group
   int32_t part_tokens;      // split: tokens per partition
@@ -55,14 +56,15 @@ int launch_merge(const float* part_out, const float* part_lse, const int32_t* se
                  int32_t part_tokens, int32_t max_parts, float* out, float* out_lse,
                  void* stream);
 
+// tile_stride in elements
 int launch_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                  int64_t num_blocks, int elem_bytes, void* k_cache, void* v_cache,
-                  void* stream);
+                  int64_t num_blocks, int64_t tile_stride, int elem_bytes, void* k_cache,
+                  void* v_cache, void* stream);
 
 int launch_gather(const void* k_cache, const void* v_cache, const int32_t* block_tables,
                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
-                  int32_t head_dim, int32_t max_blocks, int64_t num_blocks, int32_t max_len,
-                  int elem_bytes, void* k_out, void* v_out, void* stream);
+                  int32_t head_dim, int32_t max_blocks, int64_t num_blocks, int64_t tile_stride,
+                  int32_t max_len, int elem_bytes, void* k_out, void* v_out, void* stream);
 
 }  // namespace pa

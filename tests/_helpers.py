@@ -25,20 +25,36 @@ def raw(x):
     return x.view(torch.int16).numpy() if x.dtype == torch.bfloat16 else x.numpy()
 
 
-def dims_of(P, wl):
+def dims_of(P, wl, dv=None):
     c = wl.cfg
     return P.make_dims(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
-                       wl.block_tables.shape[1], wl.k_cache.shape[0], c.q_dtype, c.kv_dtype)
+                       wl.block_tables.shape[1], wl.k_cache.shape[0], c.q_dtype, c.kv_dtype,
+                       kv_tile_stride=0 if dv is None else dv.stride)
 
 
 class Dev:
-    """Device copies of a workload's tensors."""
+    """Device copies of a workload's tensors.  With interleave=True the K and V tiles of
+    each (block, KV head) sit side by side in one allocation [NB][Hkv][2][tile] (tile
+    stride 2 * tile); k_cache is then that allocation and v_cache the address of its
+    first V tile."""
 
-    def __init__(self, wl):
+    def __init__(self, wl, interleave=False):
         dev = torch.device("cuda:0")
         self.q = wl.q.to(dev)
-        self.k_cache = wl.k_cache.to(dev)
-        self.v_cache = wl.v_cache.to(dev)
+        self.shape_k, self.shape_v = wl.k_cache.shape, wl.v_cache.shape
+        self.stride = 0
+        if interleave:
+            nb, h = wl.k_cache.shape[:2]
+            tile = wl.k_cache[0, 0].numel()
+            self.comb = torch.empty((nb, h, 2, tile), dtype=wl.k_cache.dtype, device=dev)
+            self.comb[:, :, 0] = wl.k_cache.reshape(nb, h, tile).to(dev)
+            self.comb[:, :, 1] = wl.v_cache.reshape(nb, h, tile).to(dev)
+            self.k_cache = self.comb
+            self.v_cache = self.comb.data_ptr() + tile * self.comb.element_size()
+            self.stride = 2 * tile
+        else:
+            self.k_cache = wl.k_cache.to(dev)
+            self.v_cache = wl.v_cache.to(dev)
         self.k_scale = None if wl.k_scale is None else wl.k_scale.to(dev)
         self.v_scale = None if wl.v_scale is None else wl.v_scale.to(dev)
         self.block_tables = wl.block_tables.to(dev)
@@ -47,9 +63,17 @@ class Dev:
         self.k_new = None if wl.k_new is None else wl.k_new.to(dev)
         self.v_new = None if wl.v_new is None else wl.v_new.to(dev)
 
+    def caches_host(self):
+        """(K, V) on the host in the dense layout."""
+        if self.stride:
+            nb, h = self.shape_k[:2]
+            return (self.comb[:, :, 0].reshape(self.shape_k).cpu(),
+                    self.comb[:, :, 1].reshape(self.shape_v).cpu())
+        return self.k_cache.cpu(), self.v_cache.cpu()
+
 
 def gpu_append(P, wl, dv):
-    d = dims_of(P, wl)
+    d = dims_of(P, wl, dv)
     P.kv_append(d, dv.k_new, dv.v_new, dv.slot_mapping, wl.cfg.batch, dv.k_cache, dv.v_cache)
 
 
@@ -58,7 +82,7 @@ def gpu_attention(P, wl, dv, seq_lens=None, split=None, balanced=None):
     or the balanced mode with `balanced` workgroups, 0 = the library's resident count).
     Returns (out, partials or None, out_lse or None)."""
     c = wl.cfg
-    d = dims_of(P, wl)
+    d = dims_of(P, wl, dv)
     lens = dv.seq_lens if seq_lens is None else seq_lens
     sm = float(np.float32(wl.sm_scale))
     out = torch.full((c.batch, c.num_q_pos, c.num_q_heads, c.head_dim), float("nan"),

@@ -69,6 +69,21 @@ def test_decode_dimension_and_type_checks(change, status):
     assert _decode(d) == status
 
 
+def test_tile_stride_and_alignment_checks():
+    for stride, status in [(16 * 64, 0), (32 * 64, 0), (16 * 64 - 8, -2), (16 * 64 + 4, -2),
+                           (16 * 64 + 8, 0), (-1, -2)]:
+        d = _dims(kv_tile_stride=stride)
+        st = P.lib.kv_gather(ctypes.byref(d), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                             ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 0, ctypes.c_void_p(FAKE),
+                             ctypes.c_void_p(FAKE), None)
+        assert st == status, (stride, st)        # max_len 0: checks only, nothing launched
+    d = _dims()
+    assert _decode(d, q=FAKE + 8) == -9
+    assert _decode(d, k=FAKE + 4) == -9
+    assert _decode(d, v=FAKE + 2) == -9
+    assert _decode(d, out=FAKE + 8) == -9
+
+
 def test_null_pointer_checks():
     d = _dims()
     assert P.lib.paged_decode_attn(None, None, None, None, None, None, None, None, 0.1, None,
@@ -135,7 +150,7 @@ def test_balanced_checks_and_sizes():
 
 
 def test_status_strings():
-    for st in range(0, -9, -1):
+    for st in range(0, -10, -1):
         assert P.paged_status_string(st) and P.paged_status_string(st) != "unknown status"
     assert P.paged_status_string(-99) == "unknown status"
 

@@ -36,13 +36,14 @@ def _small(name, spare=7, **kw):
     return W.generate(W.scaled(name, **base), spare_blocks=spare)
 
 
-def _check_attention(P, wl, tol=None, split=None, pairs=None, append=True, balanced=None):
+def _check_attention(P, wl, tol=None, split=None, pairs=None, append=True, balanced=None,
+                     interleave=False):
     c = wl.cfg
     tol = TOL[c.kv_dtype] if tol is None else tol
     say(f"[case] {c.name} B={c.batch} Hq={c.num_q_heads} Hkv={c.num_kv_heads} d={c.head_dim} "
         f"nq={c.num_q_pos} kv={c.kv_dtype} split={split} balanced={balanced} "
-        f"seed={wl.meta['seed']}")
-    dv = Dev(wl)
+        f"interleave={interleave} seed={wl.meta['seed']}")
+    dv = Dev(wl, interleave)
     if append and wl.slot_mapping is not None:
         gpu_append(P, wl, dv)
     out, parts, out_lse = gpu_attention(P, wl, dv, split=split, balanced=balanced)
@@ -69,17 +70,19 @@ def _check_attention(P, wl, tol=None, split=None, pairs=None, append=True, balan
 
 
 # ---- append and gather: bit exact -------------------------------------------------
+@pytest.mark.parametrize("interleave", [False, True])
 @pytest.mark.parametrize("name,kw", [("tiny_fp32", {}),
                                      ("llama3_8b", dict(batch=9, length_range=(1, 300)))])
-def test_kv_append_bit_exact(P, name, kw):
+def test_kv_append_bit_exact(P, name, kw, interleave):
     wl = W.generate(W.scaled(name, **kw), spare_blocks=3) if kw else W.generate(name)
-    say(f"[case] append {wl.cfg.name}")
-    dv = Dev(wl)
+    say(f"[case] append {wl.cfg.name} interleave={interleave}")
+    dv = Dev(wl, interleave)
     gpu_append(P, wl, dv)
     torch.cuda.synchronize()
     kc, vc = oracle_caches(wl, appended=True)
-    assert np.array_equal(raw(dv.k_cache.cpu()).view(np.uint8), kc.view(np.uint8))
-    assert np.array_equal(raw(dv.v_cache.cpu()).view(np.uint8), vc.view(np.uint8))
+    gk, gv = dv.caches_host()
+    assert np.array_equal(raw(gk).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(raw(gv).view(np.uint8), vc.view(np.uint8))
 
 
 def test_kv_append_skips_negative_and_out_of_pool_slots(P):
@@ -100,17 +103,18 @@ def test_kv_append_skips_negative_and_out_of_pool_slots(P):
     assert np.array_equal(raw(dv.v_cache.cpu()).view(np.uint8), vc.view(np.uint8))
 
 
+@pytest.mark.parametrize("interleave", [False, True])
 @pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b", "verify_int8"])
-def test_kv_gather_bit_exact(P, name):
+def test_kv_gather_bit_exact(P, name, interleave):
     wl = _small(name, batch=5, length_range=(0, 333), append=False)
-    say(f"[case] gather {name}")
-    dv = Dev(wl)
+    say(f"[case] gather {name} interleave={interleave}")
+    dv = Dev(wl, interleave)
     c = wl.cfg
     maxL = int(wl.seq_lens.max()) + 3
     fill = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}[c.kv_dtype]
     k_out = torch.full((c.batch, c.num_kv_heads, maxL, c.head_dim), 7, dtype=fill, device="cuda:0")
     v_out = k_out.clone()
-    P.kv_gather(dims_of(P, wl), dv.k_cache, dv.v_cache, dv.block_tables, dv.seq_lens, maxL,
+    P.kv_gather(dims_of(P, wl, dv), dv.k_cache, dv.v_cache, dv.block_tables, dv.seq_lens, maxL,
                 k_out, v_out)
     torch.cuda.synchronize()
     ko, vo = paging.gather(raw(wl.k_cache), raw(wl.v_cache), wl.block_tables.numpy(),
@@ -157,6 +161,17 @@ CASES = [
 def test_attention_small(P, name, kw):
     wl = _small(name, **kw)
     _check_attention(P, wl)
+
+
+# K and V tiles of one (block, head) side by side in one allocation (tile stride 2 tiles)
+@pytest.mark.parametrize("name,kw", [CASES[0], CASES[2], CASES[6], CASES[8], CASES[12]])
+def test_attention_small_interleaved(P, name, kw):
+    wl = _small(name, **kw)
+    _check_attention(P, wl, interleave=True)
+    _check_attention(P, wl, interleave=True, balanced=0)
+    _check_attention(P, wl, interleave=True, balanced=7)
+    if wl.cfg.num_q_pos == 1:
+        _check_attention(P, wl, interleave=True, split=(64, 16))
 
 
 def test_empty_and_short_sequences(P):
@@ -266,6 +281,7 @@ def test_full_llama3_8b(P):
     _check_attention(P, wl)
     _check_attention(P, wl, split=(512, 8))
     _check_attention(P, wl, balanced=0)
+    _check_attention(P, wl, balanced=0, interleave=True)
 
 
 def test_full_llama2_70b_shared_prefix(P):
