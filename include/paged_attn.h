@@ -219,6 +219,30 @@ int paged_attn_balanced(const pa_dims* dims, int32_t num_q_pos, const void* q,
                         void* workspace, size_t workspace_bytes, float* out, float* out_lse,
                         void* stream);
 
+/*
+ * paged_decode_step -- one decode step in one launch: kv_append of every sequence's new
+ * token followed by paged_attn_balanced with nq = 1 (tutorial section 2 / lecture 10 "KV
+ * Cache 原理": a step writes the new token's K and V into the cache, then its query attends
+ * to all cached tokens including itself).  Sequence b's new token is its token
+ * L - 1, L = seq_lens[b] (which counts it); its slot comes from the block table,
+ * block_tables[b][(L - 1) / 16] * 16 + (L - 1) % 16 (tutorial section 7), so no slot
+ * mapping is passed.
+ *   k_new, v_new   device, [B][Hkv][head_dim] in kv_dtype (PA_F32 or PA_BF16; PA_I8 gives
+ *                  PA_ERR_DTYPE); k_new 16-byte aligned
+ *   k_cache, v_cache device, read and written: the new token lands in its slot bit for bit
+ *   other arguments as paged_attn_balanced with num_q_pos = 1; complete the step with
+ *   paged_attn_balanced_merge (num_q_pos = 1) on the same stream.
+ * The result equals kv_append (a sequence with seq_lens[b] <= 0 appends nothing; a table
+ * entry outside the pool is skipped) followed by paged_attn_balanced, provided no other
+ * sequence of the batch reads a block that receives a new token -- a block being written
+ * belongs to one sequence, as under copy-on-write block sharing.
+ */
+int paged_decode_step(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
+                      void* k_cache, void* v_cache, const int32_t* block_tables,
+                      const int32_t* seq_lens, float sm_scale, int32_t num_workgroups,
+                      void* workspace, size_t workspace_bytes, float* out, float* out_lse,
+                      void* stream);
+
 /* Second half of paged_attn_balanced: writes the rows of cut segments (and of empty
  * sequences: zeros, lse -inf) from the partials the attention call left in the workspace.
  * dims, num_q_pos, num_workgroups, workspace, out and out_lse as in that call. */

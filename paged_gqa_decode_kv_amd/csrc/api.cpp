@@ -274,6 +274,29 @@ int paged_attn_balanced(const pa_dims* dims, int32_t num_q_pos, const void* q,
   return pa::launch_balanced(a, dims->q_dtype, dims->kv_dtype, stream);
 }
 
+int paged_decode_step(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
+                      void* k_cache, void* v_cache, const int32_t* block_tables,
+                      const int32_t* seq_lens, float sm_scale, int32_t num_workgroups,
+                      void* workspace, size_t workspace_bytes, float* out, float* out_lse,
+                      void* stream) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->kv_dtype != PA_F32 && dims->kv_dtype != PA_BF16) return PA_ERR_DTYPE;
+  st = check_attn_inputs(dims, q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens);
+  if (st != PA_OK) return st;
+  st = check_balanced(dims, 1, num_workgroups);
+  if (st != PA_OK) return st;
+  if (!k_new || !v_new || !out || !workspace) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(k_new)) return PA_ERR_ALIGN;
+  pa::AttnArgs a = make_args(dims, 1, q, k_cache, v_cache, nullptr, nullptr, block_tables,
+                             seq_lens, sm_scale);
+  st = balanced_args(dims, 1, num_workgroups, workspace, workspace_bytes, out, out_lse, &a);
+  if (st != PA_OK) return st;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  return pa::launch_balanced_append(a, dims->q_dtype, dims->kv_dtype, stream);
+}
+
 int paged_attn_balanced_merge(const pa_dims* dims, int32_t num_q_pos, int32_t num_workgroups,
                               void* workspace, size_t workspace_bytes, float* out,
                               float* out_lse, void* stream) {

@@ -115,6 +115,47 @@ struct Bf16Kv {
       v.v[t].y &= m1;
     }
   }
+  // Decode-step append: the new token's K and V as this lane needs them to patch a tile --
+  // the 16-byte K chunk of column 4u + grp (the lane's chunk at every step u) and V[16t +
+  // row16] -- and the patch itself (token `off` of the tile) and its store into the cache.
+  struct NewTok { u32x4 k[NK]; uint32_t v[ND]; };
+  __device__ static void load_new(NewTok& n, const void* krow, const void* vrow, int row16,
+                                  int grp) {
+    const uint8_t* kp = static_cast<const uint8_t*>(krow) + 16 * grp;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) n.k[kk] = *reinterpret_cast<const u32x4*>(kp + 64 * kk);
+    const uint16_t* vp = static_cast<const uint16_t*>(vrow) + row16;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) n.v[t] = vp[16 * t];
+  }
+  __device__ static void patch(K& k, V& v, const NewTok& n, int off, int row16, int grp) {
+    if (row16 == off) {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) k.v[kk] = n.k[kk];
+    }
+    if (grp == (off >> 2)) {
+      const bool hi_half = off & 1;
+#pragma unroll
+      for (int t = 0; t < ND; ++t) {
+        uint32_t w = (off & 2) ? v.v[t].y : v.v[t].x;
+        w = hi_half ? ((w & 0x0000FFFFu) | (n.v[t] << 16)) : ((w & 0xFFFF0000u) | n.v[t]);
+        if (off & 2) v.v[t].y = w; else v.v[t].x = w;
+      }
+    }
+  }
+  __device__ static void store_new(void* ktile, void* vtile, const NewTok& n, int off, int lane,
+                                   int row16, int grp) {
+    if (row16 == off) {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(ktile) + 1024 * kk + lane * 16) = n.k[kk];
+    }
+    if (grp == (off >> 2)) {
+#pragma unroll
+      for (int t = 0; t < ND; ++t)
+        static_cast<uint16_t*>(vtile)[t * 256 + row16 * 16 + off] = (uint16_t)n.v[t];
+    }
+  }
   __device__ static void pv(f32x4* acc, const V& v, f32x4 p, float /*vfac*/) {
     bf16x4 hi, lo;
 #pragma unroll
@@ -186,6 +227,48 @@ struct F32Kv {
       for (int e = 0; e < 4; ++e)
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.v[t][e], p[e], acc[t], 0, 0, 0);
   }
+  // decode-step append (as in Bf16Kv): K chunk of column 4u + grp, V[16t + row16]
+  struct NewTok { f32x4 k[NU]; float v[ND]; };
+  __device__ static void load_new(NewTok& n, const void* krow, const void* vrow, int row16,
+                                  int grp) {
+    const uint8_t* kp = static_cast<const uint8_t*>(krow) + 16 * grp;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) n.k[u] = *reinterpret_cast<const f32x4*>(kp + 64 * u);
+    const float* vp = static_cast<const float*>(vrow) + row16;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) n.v[t] = vp[16 * t];
+  }
+  __device__ static void patch(K& k, V& v, const NewTok& n, int off, int row16, int grp) {
+    if (row16 == off) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) k.v[u] = n.k[u];
+    }
+    if (grp == (off >> 2)) {
+      const int e = off & 3;
+#pragma unroll
+      for (int t = 0; t < ND; ++t) {
+        f32x4 x = v.v[t];
+        x[0] = e == 0 ? n.v[t] : x[0];
+        x[1] = e == 1 ? n.v[t] : x[1];
+        x[2] = e == 2 ? n.v[t] : x[2];
+        x[3] = e == 3 ? n.v[t] : x[3];
+        v.v[t] = x;
+      }
+    }
+  }
+  __device__ static void store_new(void* ktile, void* vtile, const NewTok& n, int off, int lane,
+                                   int row16, int grp) {
+    if (row16 == off) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        *reinterpret_cast<f32x4*>(static_cast<uint8_t*>(ktile) + 1024 * u + lane * 16) = n.k[u];
+    }
+    if (grp == (off >> 2)) {
+#pragma unroll
+      for (int t = 0; t < ND; ++t)
+        static_cast<float*>(vtile)[t * 256 + row16 * 16 + off] = n.v[t];
+    }
+  }
 };
 
 template <int D>
@@ -252,6 +335,11 @@ struct I8Kv {
     return c;
   }
   __device__ static void mask_v(V&, int, int) {}  // codes are finite; P = 0 removes them
+  // (no decode-step append into int8 caches: never instantiated)
+  struct NewTok {};
+  __device__ static void load_new(NewTok&, const void*, const void*, int, int) {}
+  __device__ static void patch(K&, V&, const NewTok&, int, int, int) {}
+  __device__ static void store_new(void*, void*, const NewTok&, int, int, int, int) {}
   // p is scaled by vfac = 256 * v_scale(block) / v_ref and rounded once to fp16 (relative
   // error <= 2^-11 per weight, so |error of out| <= 2^-11 * max|V|, inside the int8
   // tolerance); the factor 256 keeps small weights out of the fp16 subnormal range.
@@ -659,6 +747,13 @@ void paged_attn_kernel(AttnArgs a) {
 // are still being consumed.  A segment that lies wholly inside one slice is written out
 // directly; otherwise each piece becomes a partial result at partial id v + j (unique:
 // along the slices both v and j only grow) and the merge kernel combines the pieces.
+//
+// APP (decode step, nq = 1): the token at position L_b - 1 of every sequence is new this
+// step.  Its K and V come from a.k_new / a.v_new [B][Hkv][d] rather than from the cache:
+// the wave that consumes the tile holding it patches the token into the tile registers
+// before the MFMAs and (row group 0) stores it into its cache slot, so one launch does
+// the append and the attention.  The new-token rows are fetched together with the
+// segment's query rows.
 // s_waitcnt immediate for vmcnt(0) with the other counters left open (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmem0 = 0x0F70;
@@ -675,7 +770,7 @@ template <class KV, int NT> struct BalancedWavesPerEU {
                                    : PA_BAL_WAVES_PER_EU;
 };
 
-template <class KV, int D, int NT, int W, int NBUF>
+template <class KV, int D, int NT, int W, int NBUF, bool APP>
 __global__ __launch_bounds__(kWave* W)
 __attribute__((amdgpu_waves_per_eu(BalancedWavesPerEU<KV, NT>::value)))
 void paged_attn_balanced_kernel(AttnArgs a) {
@@ -814,6 +909,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   int L = 0, lim_min = 0, lim[NT];
   typename KV::Q qop[NT], qnext[NT];
   int lim_next[NT], lim_min_next = 0;
+  typename KV::NewTok tok, tok_next;  // APP: the new token of the current / next segment
   Seg nxt;                 // segment whose rows sit in qnext (valid while nxt.j >= 0)
   nxt.j = -1;
   int iss_end = x0;        // end of the segment of the newest issued block
@@ -843,6 +939,11 @@ void paged_attn_balanced_kernel(AttnArgs a) {
         const int Ls = clamp_len(a.seq_lens[sg.b], a.max_blocks);
         lim_min_next = load_rows<KV, D, NT>(a, sg.b, sg.g, sg.rg, Ls, rows_hi(sg, Ls), qnext,
                                             lim_next, row16, grp);
+        if constexpr (APP) {
+          const int64_t nrow = ((int64_t)sg.b * a.num_kv_heads + sg.g) * D * KV::kElem;
+          KV::load_new(tok_next, static_cast<const uint8_t*>(a.k_new) + nrow,
+                       static_cast<const uint8_t*>(a.v_new) + nrow, row16, grp);
+        }
       }
     }
     const int64_t tl = sl.tile >= 0 ? sl.tile : 0;
@@ -865,11 +966,17 @@ void paged_attn_balanced_kernel(AttnArgs a) {
           lim[nt] = lim_next[nt];
         }
         lim_min = lim_min_next;
+        if constexpr (APP) tok = tok_next;
         nxt.j = -1;
       } else {
         // (rare: two segments began within the blocks in flight) load the rows now and
         // wait for them here, so that no later wait has to allow for a pending query load
         lim_min = load_rows<KV, D, NT>(a, cur.b, cur.g, cur.rg, L, hi, qop, lim, row16, grp);
+        if constexpr (APP) {
+          const int64_t nrow = ((int64_t)cur.b * a.num_kv_heads + cur.g) * D * KV::kElem;
+          KV::load_new(tok, static_cast<const uint8_t*>(a.k_new) + nrow,
+                       static_cast<const uint8_t*>(a.v_new) + nrow, row16, grp);
+        }
         __builtin_amdgcn_s_waitcnt(kWaitVmem0);
         if (nxt.j >= 0 && nxt.j <= cur.j) nxt.j = -1;
       }
@@ -881,8 +988,22 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     }
     if (sl.tile < 0) return;
     const int tok0 = (x - cur.start) * kBlockTokens;
+    const bool new_tok = APP && tok0 + kBlockTokens >= L;  // the tile holding token L - 1
+    const int off = L - 1 - tok0;
+    if constexpr (APP) {
+      if (new_tok) KV::patch(kk, vv, tok, off, row16, grp);
+    }
     st.update(qop, lim, lim_min, rows_hi(cur, L), kk, vv, tok0,
               a.scale_log2 * (kInt8 ? sl.ks : 1.f), sl.vs, grp);
+    if constexpr (APP) {
+      // stored only now: issued before this block's wait, the stores would make that wait
+      // (whose count assumes no stores) also drain the next block's loads
+      if (new_tok && cur.rg == 0) {
+        uint8_t* kt = const_cast<uint8_t*>(kbase) + (int64_t)sl.tile * tile_bytes;
+        uint8_t* vt = const_cast<uint8_t*>(vbase) + (int64_t)sl.tile * tile_bytes;
+        KV::store_new(kt, vt, tok, off, lane, row16, grp);
+      }
+    }
   };
 
   {
@@ -920,10 +1041,10 @@ int launch_one(const AttnArgs& a, void* stream) {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-template <class KV, int D, int NT, int W, int NBUF>
+template <class KV, int D, int NT, int W, int NBUF, bool APP>
 int launch_balanced_one(const AttnArgs& a, void* stream) {
   const int64_t grid = ((int64_t)a.num_workgroups + 7) / 8 * 8;
-  hipLaunchKernelGGL((paged_attn_balanced_kernel<KV, D, NT, W, NBUF>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((paged_attn_balanced_kernel<KV, D, NT, W, NBUF, APP>), dim3((unsigned)grid),
                      dim3(kWave * W), 0, static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -935,7 +1056,8 @@ int occupancy_one() {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return PA_ERR_LAUNCH;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&paged_attn_balanced_kernel<KV, D, NT, W, NBUF>),
+          &per_cu,
+          reinterpret_cast<const void*>(&paged_attn_balanced_kernel<KV, D, NT, W, NBUF, false>),
           kWave * W, 0) != hipSuccess)
     return PA_ERR_LAUNCH;
   // two workgroups per compute unit measured best on MI355X for all four workloads
@@ -955,20 +1077,28 @@ int occupancy_one() {
 #define PA_NBUF_2 2
 #endif
 
-enum Op { kLaunch, kLaunchBalanced, kOccupancy };
+enum Op { kLaunch, kLaunchBalanced, kLaunchBalancedAppend, kOccupancy };
 
 template <template <int> class KVT, int D>
 int dispatch_dim(const AttnArgs& a, Op op, void* stream) {
   constexpr int W = PA_WAVES;
+  using KV = KVT<D>;
+  constexpr bool kCanAppend = !IsInt8<KV>::value;
   if (a.rows <= 16) {
-    using KV = KVT<D>;
     if (op == kLaunch) return launch_one<KV, D, 1, W, PA_NBUF_1>(a, stream);
-    if (op == kLaunchBalanced) return launch_balanced_one<KV, D, 1, W, PA_NBUF_1>(a, stream);
+    if (op == kLaunchBalanced) return launch_balanced_one<KV, D, 1, W, PA_NBUF_1, false>(a, stream);
+    if (op == kLaunchBalancedAppend) {
+      if constexpr (kCanAppend) return launch_balanced_one<KV, D, 1, W, PA_NBUF_1, true>(a, stream);
+      return PA_ERR_DTYPE;
+    }
     return occupancy_one<KV, D, 1, W, PA_NBUF_1>();
   }
-  using KV = KVT<D>;
   if (op == kLaunch) return launch_one<KV, D, 2, W, PA_NBUF_2>(a, stream);
-  if (op == kLaunchBalanced) return launch_balanced_one<KV, D, 2, W, PA_NBUF_2>(a, stream);
+  if (op == kLaunchBalanced) return launch_balanced_one<KV, D, 2, W, PA_NBUF_2, false>(a, stream);
+  if (op == kLaunchBalancedAppend) {
+    if constexpr (kCanAppend) return launch_balanced_one<KV, D, 2, W, PA_NBUF_2, true>(a, stream);
+    return PA_ERR_DTYPE;
+  }
   return occupancy_one<KV, D, 2, W, PA_NBUF_2>();
 }
 
@@ -1003,6 +1133,10 @@ int balanced_workgroups(int q_dtype, int kv_dtype, int head_dim, int32_t rows) {
 
 int launch_balanced(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream) {
   return dispatch(a, q_dtype, kv_dtype, kLaunchBalanced, stream);
+}
+
+int launch_balanced_append(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream) {
+  return dispatch(a, q_dtype, kv_dtype, kLaunchBalancedAppend, stream);
 }
 
 }  // namespace pa

@@ -32,6 +32,10 @@ struct AttnArgs {
   float* ws_lse;            // partial lse   [num_workers + segments][row tile]
   int32_t* ws_prefix;       // block-count prefix over sequences [num_seqs + 1]
   float* ws_out_lse;        // final lse [B][nq][Hq] for whole segments, or null
+  // decode step (balanced mode with the append folded in): the new token of every
+  // sequence, [B][Hkv][head_dim] in the cache's element type
+  const void* k_new;
+  const void* v_new;
 };
 
 // most sequences the balanced mode accepts in one call (its prefix lives in LDS)
@@ -47,6 +51,9 @@ int balanced_waves();
 int balanced_workgroups(int q_dtype, int kv_dtype, int head_dim, int32_t rows);
 // balanced attention on `stream`; the AttnArgs workspace pointers must be set
 int launch_balanced(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream);
+// the same with the decode step's append folded in (a.k_new / a.v_new set, nq = 1,
+// fp32 or bf16 caches); k_cache / v_cache are written
+int launch_balanced_append(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream);
 
 // merge of the balanced mode's partials into out [B][nq][Hq][d] (and out_lse, if given)
 int launch_balanced_merge(const AttnArgs& a, float* out, float* out_lse, void* stream);

@@ -115,6 +115,23 @@ def gpu_attention(P, wl, dv, seq_lens=None, split=None, balanced=None):
     return out, (part_out, part_lse), out_lse
 
 
+def gpu_decode_step(P, wl, dv, G=0, seq_lens=None):
+    """paged_decode_step + paged_attn_balanced_merge: append and decode attention in one
+    attention launch.  Returns (out, out_lse)."""
+    c = wl.cfg
+    d = dims_of(P, wl, dv)
+    lens = dv.seq_lens if seq_lens is None else seq_lens
+    G = G or P.paged_attn_balanced_workgroups(d, 1)
+    nbytes = P.paged_attn_balanced_workspace_bytes(d, 1, G)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    out = torch.full((c.batch, 1, c.num_q_heads, c.head_dim), float("nan"), device="cuda:0")
+    out_lse = torch.full((c.batch, 1, c.num_q_heads), float("nan"), device="cuda:0")
+    P.paged_decode_step(d, dv.q, dv.k_new, dv.v_new, dv.k_cache, dv.v_cache, dv.block_tables,
+                        lens, float(np.float32(wl.sm_scale)), G, ws, out, out_lse)
+    P.paged_attn_balanced_merge(d, 1, G, ws, out, out_lse)
+    return out, out_lse
+
+
 def oracle_caches(wl, appended=True):
     """Host caches as the oracle sees them (after the step's append, by the oracle's own
     scatter)."""

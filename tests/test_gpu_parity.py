@@ -7,8 +7,8 @@ import torch
 
 import workloads as W
 from oracle import attention, paging
-from _helpers import (TOL, Dev, dims_of, gpu_append, gpu_attention, max_err, oracle_attention,
-                      oracle_caches, raw, say)
+from _helpers import (TOL, Dev, dims_of, gpu_append, gpu_attention, gpu_decode_step, max_err,
+                      oracle_attention, oracle_caches, raw, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -247,6 +247,80 @@ def test_balanced_workspace_errors(P):
     assert e.value.status == -8
 
 
+# ---- decode step: the append folded into the balanced attention launch ----------------
+def _check_decode_step(P, wl, G=0, interleave=False, zero_lens=(), pairs=None):
+    c = wl.cfg
+    say(f"[case] decode step {c.name} B={c.batch} Hq={c.num_q_heads} Hkv={c.num_kv_heads} "
+        f"d={c.head_dim} kv={c.kv_dtype} G={G} interleave={interleave} zero={zero_lens} "
+        f"seed={wl.meta['seed']}")
+    lens = wl.seq_lens.clone()
+    slots = wl.slot_mapping.numpy().copy()
+    tables = wl.block_tables.numpy()
+    for b, L in enumerate(lens.tolist()):      # the slot the kernel derives from the table
+        assert slots[b] == paging.slot_of(tables[b], L - 1)
+    for b in zero_lens:
+        lens[b] = 0
+        slots[b] = -1
+    dv = Dev(wl, interleave)
+    out, out_lse = gpu_decode_step(P, wl, dv, G, seq_lens=lens.cuda())
+    torch.cuda.synchronize()
+    kc, vc = paging.append(raw(wl.k_cache), raw(wl.v_cache), raw(wl.k_new), raw(wl.v_new), slots)
+    gk, gv = dv.caches_host()
+    assert np.array_equal(raw(gk).view(np.uint8), kc.view(np.uint8)), "K cache after the step"
+    assert np.array_equal(raw(gv).view(np.uint8), vc.view(np.uint8)), "V cache after the step"
+    ref, ref_lse = oracle_attention(wl, kc, vc, seq_lens=lens.numpy(), pairs=pairs)
+    err = max_err(out, ref, pairs, c.group_size)
+    say(f"  max abs err {err:.3e} (tol {TOL[c.kv_dtype]:.0e})")
+    assert err <= TOL[c.kv_dtype]
+    g = out_lse.cpu().numpy().reshape(ref_lse.shape)
+    sel = np.isfinite(ref_lse)
+    if pairs is not None:
+        m = np.zeros(ref_lse.shape, bool)
+        for b, kv in pairs:
+            m[b, ..., kv * c.group_size:(kv + 1) * c.group_size] = True
+        sel &= m
+    assert np.all(np.abs(g[sel] - ref_lse[sel]) <= 1e-3 * np.maximum(1, np.abs(ref_lse[sel])))
+    for b in zero_lens:
+        assert (out[b] == 0).all() and (out_lse[b] == -np.inf).all()
+
+
+@pytest.mark.parametrize("G", [0, 5])
+@pytest.mark.parametrize("name,kw", [
+    ("llama3_8b", dict(batch=6, length_range=(1, 700))),
+    ("llama3_8b", dict(batch=5, length_range=(1, 300), head_dim=64, num_q_heads=16, num_kv_heads=2)),
+    ("llama3_8b", dict(batch=3, length_range=(40, 400), num_q_heads=32, num_kv_heads=1)),   # 32 rows
+    ("llama3_8b", dict(batch=2, length_range=(100, 300), num_q_heads=64, num_kv_heads=1)),  # 2 row tiles
+    ("llama2_70b_prefix", dict(batch=4, length_range=(17, 520))),
+    ("tiny_fp32", dict(batch=5, length_range=(1, 400), head_dim=128)),
+    ("tiny_fp32", dict(batch=4, length_range=(1, 200), num_q_heads=12, num_kv_heads=4)),
+])
+def test_decode_step_small(P, name, kw, G):
+    wl = _small(name, **kw)
+    _check_decode_step(P, wl, G)
+    _check_decode_step(P, wl, G, interleave=True)
+
+
+def test_decode_step_lengths_at_block_edges(P):
+    # new token at offsets 0, 15 and 1 of a block; a sequence of one token; sequences of
+    # length 0 append nothing and read nothing
+    wl = _small("llama3_8b", batch=7, lengths=(1, 16, 17, 32, 33, 5, 200))
+    _check_decode_step(P, wl, 0)
+    _check_decode_step(P, wl, 3, zero_lens=(1, 5))
+
+
+def test_decode_step_int8_rejected(P):
+    wl = _small("verify_int8", batch=2, length_range=(1, 50), num_q_pos=1)
+    d = dims_of(P, wl)
+    dv = Dev(wl)
+    ws = torch.empty(P.paged_attn_balanced_workspace_bytes(d, 1, 4), dtype=torch.uint8,
+                     device="cuda:0")
+    out = torch.empty((2, 1, wl.cfg.num_q_heads, wl.cfg.head_dim), device="cuda:0")
+    with pytest.raises(P.PagedAttnError) as e:
+        P.paged_decode_step(d, dv.q, dv.q, dv.q, dv.k_cache, dv.v_cache, dv.block_tables,
+                            dv.seq_lens, 0.1, 4, ws, out)
+    assert e.value.status == -3
+
+
 # ---- invariances, bit for bit --------------------------------------------------------
 def test_block_relabel_and_batch_order_bit_identical(P):
     wl = _small("llama3_8b", batch=6, length_range=(1, 500), append=False)
@@ -276,6 +350,12 @@ def test_split_count_invariance(P):
 
 
 # ---- full-size configurations ---------------------------------------------------------
+def test_full_llama3_8b_decode_step(P):
+    wl = W.generate("llama3_8b")
+    _check_decode_step(P, wl, 0)
+    _check_decode_step(P, wl, 0, interleave=True)
+
+
 def test_full_llama3_8b(P):
     wl = W.generate("llama3_8b")
     _check_attention(P, wl)
@@ -286,6 +366,7 @@ def test_full_llama3_8b(P):
 
 def test_full_llama2_70b_shared_prefix(P):
     wl = W.generate("llama2_70b_prefix")
+    _check_decode_step(P, wl, 0)
     _check_attention(P, wl)
     _check_attention(P, wl, balanced=0)
     wl2 = W.generate("llama2_70b_prefix", shuffle_batch=True)
