@@ -1,21 +1,32 @@
 """Benchmark: paged GQA decode attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--path split|direct]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--path step|balanced|split|direct]
+                    [--layout interleaved|separate]
 
 One step is one decode step of one attention layer of the Llama-3-8B-shaped workload
 (batch 64, 32 query / 8 KV heads, head_dim 128, bf16 KV, contexts U[512, 4096], seed
-1001): kv_append of the 64 new tokens followed by paged decode attention -- by default
-the balanced kernel (the batch's blocks dealt evenly over the workgroups) and its merge;
---path split / direct time the fixed-partition split + merge or the single-pass kernel.
-Inputs are resident in HBM before the timed region; two copies of the KV pool are used in
-turn so that consecutive steps do not find the previous step's KV in the 256 MB Infinity
-Cache.
+1001): the append of the 64 new tokens and paged decode attention over the cache that
+includes them.  Paths:
+  step      (default) paged_decode_step + paged_attn_balanced_merge: the append folded
+            into the balanced attention kernel, then the merge of cut segments
+  balanced  kv_append, paged_attn_balanced, paged_attn_balanced_merge
+  split     kv_append, fixed-partition split attention, lse_merge
+  direct    kv_append, the single-pass kernel
+--layout: K and V tiles of one (block, head) side by side in one pool (interleaved,
+default) or two separate pools.  Inputs are resident in HBM before the timed region;
+two copies of the KV pool are used in turn so that consecutive steps do not find the
+previous step's KV in the 256 MB Infinity Cache.
 
 Printed: ONE JSON line.  value = algorithmic KV bytes per step / step time (GB/s);
 roofline.achieved = the same bytes / the attention kernel's mean duration, timed with
 HIP events on the stream the kernels run on.  The other workloads (Llama-2-70B shared
 prefix, 128K context, int8 verify) are timed the same way and reported under "others".
 cpu_baseline times the fp64 oracle on a bounded sample of the same workload.
+
+    python bench.py --pmc-summary FETCH_DIR WRITE_DIR
+
+writes the HBM-traffic summary of the attention kernel (profiles/) from two rocprofv3
+--pmc runs of this script with --calibrate (FETCH_SIZE, then WRITE_SIZE).
 """
 import argparse
 import json
@@ -41,21 +52,29 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--path", choices=["balanced", "split", "direct"], default="balanced")
+    ap.add_argument("--path", choices=["step", "balanced", "split", "direct"], default="step")
+    ap.add_argument("--layout", choices=["interleaved", "separate"], default="interleaved")
     ap.add_argument("--workgroups", type=int, default=0, help="balanced path; 0 = library default")
     ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="bracket the attention kernel with HIP events on every n-th timed step")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs into the traffic file and exit")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="summarise a rocprofv3 --kernel-trace run of this script (profiles/) "
+                         "and exit")
     return ap.parse_args()
 
 
 class Runner:
     """Device-resident inputs of one workload and one decode step through the C ABI."""
 
-    def __init__(self, P, wl, path, partition, copies=2, workgroups=0):
+    def __init__(self, P, wl, path, partition, copies=2, workgroups=0, layout="interleaved"):
         import torch
         self.P, self.wl, self.torch = P, wl, torch
         c = wl.cfg
@@ -64,20 +83,34 @@ class Runner:
         self.tables = wl.block_tables.to(dev)
         self.lens = wl.seq_lens.to(dev)
         self.pools = []
+        self.keep = []
+        tile = wl.k_cache[0, 0].numel()
         for _ in range(copies):
-            self.pools.append((wl.k_cache.to(dev), wl.v_cache.to(dev),
-                               None if wl.k_scale is None else wl.k_scale.to(dev),
-                               None if wl.v_scale is None else wl.v_scale.to(dev)))
+            ks = None if wl.k_scale is None else wl.k_scale.to(dev)
+            vs = None if wl.v_scale is None else wl.v_scale.to(dev)
+            if layout == "interleaved":
+                # [NB][Hkv][2][tile]: K then V tile of each (block, head), tile stride 2 tiles
+                nb, h = wl.k_cache.shape[:2]
+                comb = torch.empty((nb, h, 2, tile), dtype=wl.k_cache.dtype, device=dev)
+                comb[:, :, 0] = wl.k_cache.reshape(nb, h, tile).to(dev)
+                comb[:, :, 1] = wl.v_cache.reshape(nb, h, tile).to(dev)
+                self.keep.append(comb)
+                self.pools.append((comb, comb.data_ptr() + tile * comb.element_size(), ks, vs))
+            else:
+                self.pools.append((wl.k_cache.to(dev), wl.v_cache.to(dev), ks, vs))
         self.append = wl.slot_mapping is not None
         if self.append:
             self.k_new, self.v_new = wl.k_new.to(dev), wl.v_new.to(dev)
             self.slots = wl.slot_mapping.to(dev)
         self.dims = P.make_dims(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
                                 wl.block_tables.shape[1], wl.k_cache.shape[0], c.q_dtype,
-                                c.kv_dtype)
+                                c.kv_dtype,
+                                kv_tile_stride=2 * tile if layout == "interleaved" else 0)
         self.sm = float(np.float32(c.sm_scale))
         self.out = torch.empty((c.batch, c.num_q_pos, c.num_q_heads, c.head_dim),
                                dtype=torch.float32, device=dev)
+        if path == "step" and not (self.append and c.num_q_pos == 1):
+            path = "balanced"        # the fused step is the decode step with an append
         self.path = path
         self.split = path == "split" and c.num_q_pos == 1 and partition
         if path == "split" and not self.split:
@@ -89,60 +122,61 @@ class Runner:
                                         dtype=torch.float32, device=dev)
             self.part_lse = torch.empty((c.batch, c.num_q_heads, self.maxp),
                                         dtype=torch.float32, device=dev)
-        if path == "balanced":
+        if path in ("balanced", "step"):
             self.G = workgroups or P.paged_attn_balanced_workgroups(self.dims, c.num_q_pos)
             nbytes = P.paged_attn_balanced_workspace_bytes(self.dims, c.num_q_pos, self.G)
             self.ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
 
     def step(self, i, ev=None):
+        """One decode step.  With ev, HIP events bracket the attention kernel only (each
+        event record costs the stream a few microseconds, so append and merge are left
+        unbracketed; rocprofv3 gives their durations)."""
         P, c = self.P, self.wl.cfg
         kc, vc, ks, vs = self.pools[i % len(self.pools)]
-        if ev is not None:
-            ev[0].record()
-        if self.append:
+        if self.append and self.path != "step":
             P.kv_append(self.dims, self.k_new, self.v_new, self.slots, c.batch, kc, vc)
         if ev is not None:
-            ev[1].record()
-        if self.path == "balanced":
+            ev[0].record()
+        if self.path == "step":
+            P.paged_decode_step(self.dims, self.q, self.k_new, self.v_new, kc, vc, self.tables,
+                                self.lens, self.sm, self.G, self.ws, self.out)
+        elif self.path == "balanced":
             P.paged_attn_balanced(self.dims, c.num_q_pos, self.q, kc, vc, ks, vs, self.tables,
                                   self.lens, self.sm, self.G, self.ws, self.out)
-            if ev is not None:
-                ev[2].record()
-            P.paged_attn_balanced_merge(self.dims, c.num_q_pos, self.G, self.ws, self.out)
         elif self.split:
             P.paged_decode_attn_split(self.dims, self.q, kc, vc, ks, vs, self.tables, self.lens,
                                       self.sm, self.pt, self.maxp, self.part_out, self.part_lse)
-            if ev is not None:
-                ev[2].record()
-            P.lse_merge(self.dims, self.part_out, self.part_lse, self.lens, self.pt, self.maxp,
-                        self.out)
         else:
             P.paged_verify_attn(self.dims, c.num_q_pos, self.q, kc, vc, ks, vs, self.tables,
                                 self.lens, self.sm, self.out)
-            if ev is not None:
-                ev[2].record()
         if ev is not None:
-            ev[3].record()
+            ev[1].record()
+        if self.path in ("step", "balanced"):
+            P.paged_attn_balanced_merge(self.dims, c.num_q_pos, self.G, self.ws, self.out)
+        elif self.split:
+            P.lse_merge(self.dims, self.part_out, self.part_lse, self.lens, self.pt, self.maxp,
+                        self.out)
 
-    def measure(self, steps, warmup):
+    def measure(self, steps, warmup, every=4):
+        """Wall time of `steps` steps; the attention kernel is bracketed by HIP events on
+        every `every`-th step of the same timed region (steps 0, every, 2 every, ...)."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for i in range(0, steps, every)}
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.step(i, evs[i])
+            self.step(i, evs.get(i))
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        app = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]     # us
-        attn = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
-        merge = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
-        return wall, np.array(app), np.array(attn), np.array(merge)
+        attn = [e[0].elapsed_time(e[1]) * 1e3 for e in evs.values()]     # us
+        return wall, np.array(attn)
 
 
-def summarize(wl, wall, steps, app, attn, merge):
+def summarize(wl, wall, steps, attn):
     kv = wl.kv_bytes()
     us_step = wall / steps * 1e6
     srt = np.sort(attn)
@@ -154,8 +188,7 @@ def summarize(wl, wall, steps, app, attn, merge):
         "attn_kernel_us_median": float(np.median(attn)),
         "attn_kernel_us_p95": float(srt[int((len(srt) - 1) * 0.95)]),
         "attn_kernel_GBps": kv / (attn.mean() * 1e-6) / 1e9,
-        "append_us_mean": float(app.mean()),
-        "merge_us_mean": float(merge.mean()),
+        "attn_kernel_samples": len(attn),
     }
 
 
@@ -208,7 +241,10 @@ def cpu_baseline(wl, seconds):
 
 
 KERNEL_SOURCES = ["paged_gqa_decode_kv_amd/csrc/attn.hip", "paged_gqa_decode_kv_amd/csrc/pa_common.hpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama3_8b_balanced_traffic.json")
+
+
+def traffic_file(path, layout):
+    return os.path.join(ROOT, "profiles", f"llama3_8b_{path}_{layout}_traffic.json")
 
 
 def kernel_source_hash():
@@ -220,11 +256,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(path, layout):
     """HBM bytes per launch of the attention kernel from the committed counter summary,
     or None if there is none or the kernel source changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(traffic_file(path, layout)) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -243,8 +279,113 @@ def calibration_copy(torch, nbytes=1 << 30):
     del a, b
 
 
+KERNEL_NAME = {"step": "paged_attn_balanced_kernel (decode step: append folded in)",
+               "balanced": "paged_attn_balanced_kernel",
+               "split": "paged_attn_kernel (split)", "direct": "paged_attn_kernel (direct)"}
+
+
+def pmc_summary(args, fetch_dir, write_dir):
+    """Traffic file from two rocprofv3 --pmc runs of this script (--calibrate): the
+    attention kernel's per-dispatch FETCH_SIZE / WRITE_SIZE (KiB), each scaled by what the
+    same counter reads for the 1 GiB calibration copy (copy bytes / counter bytes)."""
+    import sqlite3
+    copy_bytes = 1 << 30
+
+    def load(d, counter):
+        db = sqlite3.connect(os.path.join(d, "run_results.db"))
+        rows = db.execute("select kernel_name, value from counters_collection "
+                          "where counter_name=? order by dispatch_id", (counter,)).fetchall()
+        cal = [v for k, v in rows if "copyBuffer" in k][:3]
+        att = [v for k, v in rows if "paged_attn_balanced_kernel" in k or
+               ("paged_attn_kernel" in k and "balanced" not in k)]
+        return float(np.mean(cal)), float(np.mean(att)), len(att)
+    cf, fetch, n = load(fetch_dir, "FETCH_SIZE")
+    cw, write, _ = load(write_dir, "WRITE_SIZE")
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    import workloads as W
+    wl = W.generate("llama3_8b", poison=False)
+    out = {
+        "kernel": KERNEL_NAME[args.path],
+        "workload": "llama3_8b_layer_decode (batch 64, 32q/8kv, d128, bf16, contexts "
+                    "U[512,4096] seed 1001), library-default workgroups",
+        "path": args.path, "layout": args.layout,
+        "kernel_source_sha": kernel_source_hash(), "kernel_sources": KERNEL_SOURCES,
+        "algorithmic_bytes_per_launch": wl.kv_bytes(),
+        "fetch_bytes_per_launch": round(fetch * 1024 * fs),
+        "write_bytes_per_launch": round(write * 1024 * ws),
+        "traffic_bytes_per_launch": round(fetch * 1024 * fs + write * 1024 * ws),
+        "calibration": {"copy_bytes": copy_bytes, "FETCH_SIZE_KiB": round(cf, 1),
+                        "WRITE_SIZE_KiB": round(cw, 1), "fetch_scale": round(fs, 5),
+                        "write_scale": round(ws, 5)},
+        "raw_KiB_per_dispatch": {"FETCH_SIZE": round(fetch, 2), "WRITE_SIZE": round(write, 2),
+                                 "dispatches": n},
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run -- python bench.py --steps 10 "
+            f"--warmup 2 --no-others --no-cpu --calibrate --path {args.path} --layout {args.layout}",
+            f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run -- python bench.py --steps 10 "
+            f"--warmup 2 --no-others --no-cpu --calibrate --path {args.path} --layout {args.layout}",
+            f"python bench.py --path {args.path} --layout {args.layout} --pmc-summary "
+            f"{fetch_dir} {write_dir}"],
+    }
+    with open(traffic_file(args.path, args.layout), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def trace_summary(args, trace_dir):
+    """Markdown summary of a rocprofv3 --kernel-trace run of this script: per kernel and
+    workload, calls and mean / median duration (the first 3 calls of each workload, the
+    warm-up, are left out)."""
+    import re
+    import sqlite3
+    db = sqlite3.connect(os.path.join(trace_dir, "run_results.db"))
+    rows = db.execute("select name, start, end from kernels order by start").fetchall()
+
+    def short(n):
+        n = n.replace("(anonymous namespace)::", "")
+        m = re.match(r"void pa::(\w+)<(.*)>\(", n)
+        return f"{m.group(1)}<{m.group(2)}>" if m else n.split("(")[0][:60]
+    # the attention kernels start a new workload whenever their instantiation changes or
+    # a run of calls ends with a copy (the next workload's uploads)
+    groups, cur, last = [], None, None
+    for n, s0, e in rows:
+        k = short(n)
+        if "copyBuffer" in k or "elementwise" in k or "fill" in k.lower():
+            last = "copy"
+            continue
+        if k.startswith("paged_attn") and (cur is None or last == "copy"):
+            cur = {}
+            groups.append(cur)
+        last = k
+        if cur is not None:
+            cur.setdefault(k, []).append((e - s0) / 1000)
+    names = ["llama3_8b", "llama2_70b_prefix", "long_128k", "verify_int8"]
+    lines = [f"# rocprofv3 kernel trace: bench.py --path {args.path} --layout {args.layout}", "",
+             "Command (MI355X, one GPU):", "",
+             f"    rocprofv3 --kernel-trace --stats -d {trace_dir} -o run -- python bench.py "
+             f"--steps 20 --warmup 3 --no-cpu --path {args.path} --layout {args.layout}",
+             f"    python bench.py --path {args.path} --layout {args.layout} --trace-summary "
+             f"{trace_dir}", "",
+             f"Kernel sources sha: {kernel_source_hash()}", "",
+             "| workload | kernel | calls | mean us | median us |", "|---|---|---|---|---|"]
+    for name, g in zip(names, groups):
+        for k, v in g.items():
+            v = v[3:] if len(v) > 3 else v
+            lines.append(f"| {name} | `{k}` | {len(v)} | {np.mean(v):.2f} | {np.median(v):.2f} |")
+    out = os.path.join(ROOT, "profiles", f"{args.path}_{args.layout}_kernel_trace.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args, *args.pmc_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args, args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path is single-GPU); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -261,7 +402,7 @@ def main():
     main_name = "llama3_8b"
     wl = W.generate(main_name, poison=False)
     part = args.partition or PARTITION[main_name]
-    r = Runner(P, wl, args.path, part, workgroups=args.workgroups)
+    r = Runner(P, wl, args.path, part, workgroups=args.workgroups, layout=args.layout)
     res = summarize(wl, *_m(r, args))
     G = getattr(r, "G", None)
     del r
@@ -272,9 +413,10 @@ def main():
         for name in ("llama2_70b_prefix", "long_128k", "verify_int8"):
             w2 = W.generate(name, poison=False)
             copies = 1 if name == "long_128k" else 2
-            r2 = Runner(P, w2, "balanced", None, copies=copies)
+            r2 = Runner(P, w2, "step", None, copies=copies, layout=args.layout)
             s = summarize(w2, *_m(r2, args, steps=min(args.steps, 20), warmup=3))
-            s["path"] = "balanced"
+            s["path"] = r2.path
+            s["layout"] = args.layout
             s["workgroups"] = r2.G
             s["pct_hbm_peak"] = s["kv_GBps"] / HBM_PEAK_GBS * 100
             s["attn_kernel_frac_of_peak"] = s["attn_kernel_GBps"] / HBM_PEAK_GBS
@@ -283,8 +425,7 @@ def main():
             torch.cuda.empty_cache()
 
     achieved = res["attn_kernel_GBps"]
-    kernel = {"balanced": "paged_attn_balanced_kernel", "split": "paged_attn_kernel (split)",
-              "direct": "paged_attn_kernel (direct)"}[args.path]
+    kernel = KERNEL_NAME[args.path]
     line = {
         "metric": METRIC,
         "value": round(res["kv_GBps"], 2),
@@ -301,18 +442,20 @@ def main():
         "config": {"workload": "llama3_8b_layer_decode", "batch": 64, "q_heads": 32,
                    "kv_heads": 8, "head_dim": 128, "block_size": 16, "kv_dtype": "bf16",
                    "context": "uniform [512, 4096] (+ the appended token)", "seed": 1001,
-                   "path": args.path, "workgroups": G,
+                   "path": args.path, "layout": args.layout, "workgroups": G,
                    "partition_tokens": part if args.path == "split" else None,
                    "kv_bytes_per_step": res["kv_bytes"]},
         "us_per_step": round(res["us_per_step"], 2),
         "pct_hbm_peak": round(res["kv_GBps"] / HBM_PEAK_GBS * 100, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic() if args.path == "balanced" else None,
+                     "traffic": measured_traffic(args.path, args.layout),
                      "kernel": kernel, "kernel_us_mean": round(res["attn_kernel_us_mean"], 2),
                      "bytes_per_launch": res["kv_bytes"]},
-        "timing": {k: round(v, 3) for k, v in res.items() if k.endswith("_us_mean") or
-                   k.endswith("_us_median") or k.endswith("_us_p95")},
+        "timing": dict({k: round(v, 3) for k, v in res.items() if k.endswith("_us_mean") or
+                        k.endswith("_us_median") or k.endswith("_us_p95")},
+                       attn_kernel_samples=res["attn_kernel_samples"],
+                       event_every=args.event_every),
         "others": others,
     }
     if not args.no_cpu:
@@ -323,8 +466,8 @@ def main():
 def _m(r, args, steps=None, warmup=None):
     steps = args.steps if steps is None else steps
     warmup = args.warmup if warmup is None else warmup
-    wall, app, attn, merge = r.measure(steps, warmup)
-    return (wall, steps, app, attn, merge)
+    wall, attn = r.measure(steps, warmup, args.event_every)
+    return (wall, steps, attn)
 
 
 if __name__ == "__main__":

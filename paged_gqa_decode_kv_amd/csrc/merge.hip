@@ -72,7 +72,6 @@ template <int D>
 __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int row_tile,
                                                               float* __restrict__ out,
                                                               float* __restrict__ out_lse) {
-  constexpr int PER = D / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int nwv = blockDim.x / kWave;
@@ -93,6 +92,13 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
   const int64_t w1 = s1 > s0 ? (s1 - 1) / per : -1;
   if (s1 > s0 && w0 == w1) return;   // written by the attention kernel
 
+  // Within a row's wave the lanes split into PG groups of D / 4 lanes: each group takes one
+  // piece per step, each lane four dims of it; U steps are in flight at once.
+  constexpr int LPR = D / 4;
+  constexpr int PG = kWave / LPR;
+  constexpr int U = 8;
+  const int pg = lane / LPR, dl = lane % LPR;
+  const int64_t npc = w1 - w0 + 1;  // pieces (0 for an empty segment)
   for (int rl = wv; rl < row_tile; rl += nwv) {
     const int r = rg * row_tile + rl;
     if (r >= a.rows) break;
@@ -100,54 +106,42 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
     const int h = g * a.group + r % a.group;
     const int64_t orow = (int64_t)(b * a.num_q_pos + i) * a.num_q_heads + h;
     // max lse over the pieces: lanes take pieces, then a wave reduction
-    const int64_t npc = w1 - w0 + 1;
     float M = -INFINITY;
     for (int64_t q = lane; q < npc; q += kWave)
       M = fmaxf(M, a.ws_lse[(w0 + q + j) * row_tile + rl]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float acc[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (M != -INFINITY) {
-      for (int64_t q0 = 0; q0 < npc; q0 += kWave) {
-        // lane q holds the weight of piece q0 + q
-        float wl = 0.f;
-        if (q0 + lane < npc) {
-          const float lp = a.ws_lse[(w0 + q0 + lane + j) * row_tile + rl];
-          wl = lp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lp - M) * kLog2e);
+      for (int64_t q0 = 0; q0 < npc; q0 += PG * U) {
+        float lp[U];
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t q = q0 + u * PG + pg;
+          const int64_t pid = w0 + (q < npc ? q : 0) + j;
+          lp[u] = a.ws_lse[pid * row_tile + rl];
+          v[u] = *reinterpret_cast<const f32x4*>(a.ws_out + (pid * row_tile + rl) * D + 4 * dl);
+          if (q >= npc) lp[u] = -INFINITY;
         }
-        float ws = wl;
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) ws += __shfl_xor(ws, off);
-        wsum += ws;
-        const int nq = (int)(npc - q0 < kWave ? npc - q0 : kWave);
-        // four pieces per step so their row loads are in flight together
-        for (int q = 0; q < nq; q += 4) {
-          float wq[4];
-          const float* o[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int qq = q + u < nq ? q + u : q;
-            wq[u] = q + u < nq ? __shfl(wl, qq) : 0.f;
-            o[u] = a.ws_out + ((w0 + q0 + qq + j) * row_tile + rl) * D;
-          }
-          float v[4][PER];
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int k = 0; k < PER; ++k) v[u][k] = o[u][lane + k * kWave];
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int k = 0; k < PER; ++k) acc[k] += wq[u] == 0.f ? 0.f : wq[u] * v[u][k];
+        for (int u = 0; u < U; ++u) {
+          const float wq = lp[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lp[u] - M) * kLog2e);
+          if (wq != 0.f) acc += wq * v[u];
+          wsum += wq;
         }
+      }
+      // the PG groups' partial sums
+#pragma unroll
+      for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off);
+        wsum += __shfl_xor(wsum, off);
       }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) out[orow * D + lane + k * kWave] = acc[k] * inv;
+    if (pg == 0) *reinterpret_cast<f32x4*>(out + orow * D + 4 * dl) = acc * inv;
     if (out_lse != nullptr && lane == 0)
       out_lse[orow] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
   }
