@@ -203,7 +203,7 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
  *   out_lse      device, [B][nq][Hq] fp32 (natural log; -inf for a row that sees no token),
  *                or NULL
  *   num_workgroups >= 1; paged_attn_balanced_workgroups gives a good value for the current
- *                device (twice its compute units)
+ *                device (one or two per compute unit)
  *   workspace    device, >= paged_attn_balanced_workspace_bytes(dims, nq, num_workgroups)
  *                bytes, 16-byte aligned; contents need no initialisation and are scratch
  *                from this call to the end of the merge (calls sharing one workspace must be
@@ -254,9 +254,10 @@ int paged_attn_balanced_merge(const pa_dims* dims, int32_t num_q_pos, int32_t nu
 size_t paged_attn_balanced_workspace_bytes(const pa_dims* dims, int32_t num_q_pos,
                                            int32_t num_workgroups);
 
-/* A good num_workgroups for paged_attn_balanced on the current HIP device: two per compute
- * unit, or fewer if the kernel cannot keep two resident per unit; a negative PA_ERR_* code
- * on failure.  This call queries the device (HIP calls), unlike the argument checks. */
+/* A good num_workgroups for paged_attn_balanced on the current HIP device: one per compute
+ * unit for up to 16 query rows per KV head (nq * Hq / Hkv), two per unit for more (fewer if
+ * the kernel cannot keep two resident); a negative PA_ERR_* code on failure.  This call
+ * queries the device (HIP calls), unlike the argument checks. */
 int paged_attn_balanced_workgroups(const pa_dims* dims, int32_t num_q_pos);
 
 /* Text for a status code (static storage). */

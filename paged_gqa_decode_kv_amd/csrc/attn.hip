@@ -22,9 +22,10 @@
 //    (11 bits) and the fp32 path uses fp32 MFMA directly.
 //  * int8 K/V are decoded to exact fp16 in registers; the per-(block, head) K scale
 //    multiplies the scores and the V scale is folded into P.
-//  * A workgroup of W waves owns one (sequence, KV head, row group, partition); its waves
-//    take interleaved blocks and are merged through LDS at the end (same LSE identity as
-//    the cross-workgroup split).
+//  * Direct / split modes: a workgroup of W waves owns one (sequence, KV head, row group,
+//    partition); its waves take interleaved blocks and are merged through LDS at the end
+//    (same LSE identity as the cross-workgroup split).  Balanced mode: every wave streams
+//    its own equal slice of the batch's flat block list (see paged_attn_balanced_kernel).
 //  * Workgroup ids are remapped so that consecutive units (same KV head, neighbouring
 //    sequences -- e.g. sequences sharing a prefix) land on the same XCD and its L2.
 #include <hip/hip_runtime.h>
@@ -1090,9 +1091,12 @@ int occupancy_one() {
           reinterpret_cast<const void*>(&paged_attn_balanced_kernel<KV, D, NT, W, NBUF, false>),
           kWave * W, 0) != hipSuccess)
     return PA_ERR_LAUNCH;
-  // two workgroups per compute unit measured best on MI355X for all four workloads
-  // (three per unit make the slices, and so the per-piece start-up, more numerous)
-  const int64_t n = (int64_t)cus * (per_cu >= 2 ? 2 : 1);
+  // Measured on MI355X (Llama-3-8B decode, shared-prefix and 128K bf16 workloads; int8
+  // verify): with one row tile a wave per SIMD (one workgroup per unit) streams fastest
+  // (108 / 66 / 326 us against 110 / 73 / 347 us with two per unit); with two row tiles
+  // (more compute per byte) two workgroups per unit hide it better (85 against 95 us).
+  const int want = NT == 1 ? 1 : 2;
+  const int64_t n = (int64_t)cus * (per_cu >= want ? want : (per_cu > 0 ? per_cu : 1));
   return n > 0x7fffffff ? 0x7fffffff : (int)n;
 }
 
