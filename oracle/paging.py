@@ -122,3 +122,29 @@ def gather(k_cache, v_cache, block_tables, seq_lens, k_out, v_out, block_size=BL
                 ko[b, g, t, :] = k_row(k_cache, blk, g, off)
                 vo[b, g, t, :] = v_cache[blk, g, :, off]
     return ko, vo
+
+
+def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None):
+    """Copies of the caches (and int8 scales) after copying physical block ``src`` to
+    ``dst`` for every pair: all KV heads' K and V of the block, bit for bit.
+
+    This is the copy-on-write step of block sharing (devpress tutorial §7: blocks shared
+    between sequences carry reference counts; a shared block that one sharer must write is
+    first copied to a block of its own).  Pairs with a block outside the pool, or with
+    src == dst, are skipped; every copy reads the pool as it was before the call (the
+    destinations are fresh blocks that no pair reads).
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    ks = None if k_scale is None else np.array(k_scale, copy=True)
+    vs = None if v_scale is None else np.array(v_scale, copy=True)
+    nb = kc.shape[0]
+    for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
+        if not (0 <= src < nb and 0 <= dst < nb) or src == dst:
+            continue
+        kc[dst] = k_cache[src]
+        vc[dst] = v_cache[src]
+        if ks is not None:
+            ks[dst] = k_scale[src]
+            vs[dst] = v_scale[src]
+    return kc, vc, ks, vs

@@ -59,6 +59,12 @@ MUTATIONS = [
      "test_oracle_paging.py"),
     ("KV-size factor 2 dropped", "oracle/kvsize.py", "return 2 * n_layers * batch",
      "return n_layers * batch", "test_oracle_kvsize.py"),
+    ("copy direction swapped", "oracle/paging.py", "kc[dst] = k_cache[src]",
+     "kc[src] = k_cache[dst]", "test_oracle_paging.py"),
+    ("copy skips V", "oracle/paging.py", "vc[dst] = v_cache[src]", "pass",
+     "test_oracle_paging.py"),
+    ("copy skips scales", "oracle/paging.py", "ks[dst] = k_scale[src]", "pass",
+     "test_oracle_paging.py"),
 ]
 
 

@@ -146,3 +146,45 @@ def test_gather_equals_depage():
             assert np.array_equal(ko2[b, g, : lens[b]], K.astype(np.float32))
             assert np.array_equal(vo2[b, g, : lens[b]], V.astype(np.float32))
             assert (ko2[b, g, lens[b]:] == 7.0).all()
+
+
+def test_copy_blocks_copies_whole_blocks_and_nothing_else():
+    # closed form on the labelled pool: after copying 3 -> 10 and 7 -> 11, de-paging a
+    # table that names block 10 (11) returns the labels of block 3 (7); skipped pairs
+    # (out of the pool, src == dst) change nothing
+    NB, H, d = 24, 3, 8
+    kc, vc = _labelled_pool(NB, H, d, "f32")
+    ks = np.arange(NB * H, dtype=np.float32).reshape(NB, H) + 0.25
+    vs = -ks
+    pairs = np.array([[3, 10], [7, 11], [-1, 5], [2, 99], [4, 4]], dtype=np.int32)
+    kc2, vc2, ks2, vs2 = paging.copy_blocks(kc, vc, pairs, ks, vs)
+    for dst, src in ((10, 3), (11, 7)):
+        for g in range(H):
+            K, V = paging.depage(kc2, vc2, "f32", [dst], 16, g)
+            for t in range(16):
+                label = ((src * 8 + g) * 16 + t) * 64.0
+                assert K[t].tolist() == [label + k for k in range(d)]
+                assert V[t].tolist() == [-(label + k) for k in range(d)]
+        assert ks2[dst].tolist() == ks[src].tolist() and vs2[dst].tolist() == vs[src].tolist()
+    keep = np.ones(NB, bool)
+    keep[[10, 11]] = False
+    assert np.array_equal(kc2[keep], kc[keep]) and np.array_equal(vc2[keep], vc[keep])
+    assert np.array_equal(ks2[keep], ks[keep]) and np.array_equal(vs2[keep], vs[keep])
+
+
+def test_copy_on_write_keeps_the_other_sharer_intact():
+    # two sequences share a partly filled block; the writer gets a private copy first,
+    # then appends into it: the other sharer still reads the old contents, the writer
+    # reads the old tokens followed by its new one
+    NB, H, d = 12, 2, 8
+    kc, vc = _labelled_pool(NB, H, d, "f32")
+    shared, private = 5, 9
+    kc2, vc2, _, _ = paging.copy_blocks(kc, vc, [[shared, private]])
+    k_new = np.full((1, H, d), 0.5, np.float32)
+    kc3, vc3 = paging.append(kc2, vc2, k_new, -k_new, [private * 16 + 7])
+    for g in range(H):
+        Ka, _ = paging.depage(kc3, vc3, "f32", [shared], 8, g)    # the reader
+        Kb, _ = paging.depage(kc3, vc3, "f32", [private], 8, g)   # the writer
+        K0, _ = paging.depage(kc, vc, "f32", [shared], 8, g)
+        assert np.array_equal(Ka, K0)
+        assert np.array_equal(Kb[:7], K0[:7]) and (Kb[7] == 0.5).all()
