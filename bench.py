@@ -176,6 +176,48 @@ class Runner:
         return wall, np.array(attn)
 
 
+def copy_blocks_bench(P, torch, W, steps):
+    """kv_copy_blocks on the Llama-3-8B pool (interleaved layout): a bulk copy of 2048
+    blocks and the copy-on-write of one block per sequence (64 pairs).  Two disjoint pair
+    sets alternate so a launch does not find the previous one's blocks in the Infinity
+    Cache.  Bytes = pairs * Hkv * (K + V tile) * 2 (read and write).  The launches run
+    back to back between two HIP events on the stream they run on (one event pair per
+    launch would add its own idle gap to a launch this short)."""
+    wl = W.generate(W.scaled("llama3_8b", append=False), poison=False, spare_blocks=4096)
+    c = wl.cfg
+    dev = torch.device("cuda:0")
+    nb, h = wl.k_cache.shape[:2]
+    tile = wl.k_cache[0, 0].numel()
+    comb = torch.empty((nb, h, 2, tile), dtype=wl.k_cache.dtype, device=dev)
+    comb[:, :, 0] = wl.k_cache.reshape(nb, h, tile).to(dev)
+    comb[:, :, 1] = wl.v_cache.reshape(nb, h, tile).to(dev)
+    vptr = comb.data_ptr() + tile * comb.element_size()
+    dims = P.make_dims(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                       wl.block_tables.shape[1], nb, c.q_dtype, c.kv_dtype,
+                       kv_tile_stride=2 * tile)
+    pairs = W.copy_pairs(wl, 4096, seed=3).to(dev)
+    res = {}
+    for label, n in (("bulk", 2048), ("cow_step", c.batch)):
+        sets = [pairs[:n].contiguous(), pairs[2048:2048 + n].contiguous()]
+        for i in range(4):
+            P.kv_copy_blocks(dims, sets[i % 2], n, comb, vptr)
+        torch.cuda.synchronize()
+        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        e0.record()
+        for i in range(steps):
+            P.kv_copy_blocks(dims, sets[i % 2], n, comb, vptr)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        nbytes = n * h * 2 * tile * comb.element_size() * 2
+        res[label] = {"pairs": n, "bytes": nbytes, "us_mean": round(us, 2),
+                      "GBps": round(nbytes / us / 1e3, 1),
+                      "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del comb
+    torch.cuda.empty_cache()
+    return res
+
+
 def summarize(wl, wall, steps, attn):
     kv = wl.kv_bytes()
     us_step = wall / steps * 1e6
@@ -348,8 +390,12 @@ def trace_summary(args, trace_dir):
     # the attention kernels start a new workload whenever their instantiation changes or
     # a run of calls ends with a copy (the next workload's uploads)
     groups, cur, last = [], None, None
+    copies = []
     for n, s0, e in rows:
         k = short(n)
+        if "kv_copy_blocks" in k:
+            copies.append((e - s0) / 1000)
+            continue
         if "copyBuffer" in k or "elementwise" in k or "fill" in k.lower():
             last = "copy"
             continue
@@ -372,6 +418,15 @@ def trace_summary(args, trace_dir):
         for k, v in g.items():
             v = v[3:] if len(v) > 3 else v
             lines.append(f"| {name} | `{k}` | {len(v)} | {np.mean(v):.2f} | {np.median(v):.2f} |")
+    if copies:
+        # copy_blocks_bench: 4 warm-up + n bulk launches (2048 pairs), then the same for
+        # the 64-pair copy-on-write step
+        half = len(copies) // 2
+        for label, v in (("kv_copy_blocks 2048 pairs", copies[4:half]),
+                         ("kv_copy_blocks 64 pairs", copies[half + 4:])):
+            if v:
+                lines.append(f"| llama3_8b pool | `{label}` | {len(v)} | {np.mean(v):.2f} | "
+                             f"{np.median(v):.2f} |")
     out = os.path.join(ROOT, "profiles", f"{args.path}_{args.layout}_kernel_trace.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -423,6 +478,8 @@ def main():
             others[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in s.items()}
             del r2, w2
             torch.cuda.empty_cache()
+
+        others["kv_copy_blocks"] = copy_blocks_bench(P, torch, W, min(args.steps, 40))
 
     achieved = res["attn_kernel_GBps"]
     kernel = KERNEL_NAME[args.path]

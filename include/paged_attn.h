@@ -188,6 +188,24 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
               void* k_out, void* v_out, void* stream);
 
 /*
+ * kv_copy_blocks -- copy whole physical blocks: for each pair (src, dst), every KV head's K
+ * and V of block src (and, for int8, its k_scale / v_scale) is copied to block dst, bit
+ * for bit.  This is the copy-on-write step of block sharing (tutorial section 7: shared
+ * blocks carry reference counts; a sequence about to write into a shared, partly filled
+ * block first gets a private copy of it).
+ *   block_pairs  device, [num_pairs][2] int32 (src, dst); a pair with a block outside
+ *                [0, num_blocks) or src == dst is skipped
+ *   k_cache, v_cache device, written in place (either layout, kv_tile_stride honoured)
+ *   k_scale, v_scale device, [num_blocks][Hkv] fp32, written; required for PA_I8,
+ *                ignored otherwise
+ * Copies run concurrently: no destination may also be a source or appear twice (a
+ * destination is a freshly allocated block).  num_pairs may be 0 (nothing is launched).
+ */
+int kv_copy_blocks(const pa_dims* dims, const int32_t* block_pairs, int32_t num_pairs,
+                   void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                   void* stream);
+
+/*
  * paged_attn_balanced -- decode (nq = 1) or causal verify (nq > 1) attention with the work
  * dealt evenly over the waves of num_workgroups workgroups (four waves each), whatever the
  * spread of sequence lengths.  Every (KV head, query-row tile, sequence) segment of the

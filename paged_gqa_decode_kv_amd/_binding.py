@@ -54,6 +54,7 @@ def _load(path=_LIB_PATH):
         "paged_attn_balanced_workgroups": [D, I32],
         "paged_attn_balanced_merge": [D, I32, I32, P, ctypes.c_size_t, P, P, P],
         "paged_decode_step": [D, P, P, P, P, P, P, P, F32, I32, P, ctypes.c_size_t, P, P, P],
+        "kv_copy_blocks": [D, P, I32, P, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -170,6 +171,13 @@ def paged_attn_balanced(dims, num_q_pos, q, k_cache, v_cache, k_scale, v_scale, 
         ctypes.byref(dims), num_q_pos, _p(q), _p(k_cache), _p(v_cache), _p(k_scale), _p(v_scale),
         _p(block_tables), _p(seq_lens), sm_scale, num_workgroups, _p(workspace), nbytes, _p(out),
         _p(out_lse), _stream(stream)))
+
+
+def kv_copy_blocks(dims, block_pairs, num_pairs, k_cache, v_cache, k_scale=None, v_scale=None,
+                   stream=None):
+    _check("kv_copy_blocks", lib.kv_copy_blocks(
+        ctypes.byref(dims), _p(block_pairs), num_pairs, _p(k_cache), _p(v_cache), _p(k_scale),
+        _p(v_scale), _stream(stream)))
 
 
 def paged_decode_step(dims, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, sm_scale,

@@ -222,6 +222,24 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
                            elem_bytes(dims->kv_dtype), k_out, v_out, stream);
 }
 
+int kv_copy_blocks(const pa_dims* dims, const int32_t* block_pairs, int32_t num_pairs,
+                   void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                   void* stream) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->kv_dtype != PA_F32 && dims->kv_dtype != PA_BF16 && dims->kv_dtype != PA_I8)
+    return PA_ERR_DTYPE;
+  if (num_pairs < 0) return PA_ERR_DIMS;
+  if (num_pairs == 0) return PA_OK;
+  if (!block_pairs || !k_cache || !v_cache) return PA_ERR_NULL;
+  if (dims->kv_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+  return pa::launch_copy_blocks(block_pairs, num_pairs, dims->num_kv_heads, dims->head_dim,
+                                dims->num_blocks, tile_stride(dims), elem_bytes(dims->kv_dtype),
+                                k_cache, v_cache, dims->kv_dtype == PA_I8 ? k_scale : nullptr,
+                                dims->kv_dtype == PA_I8 ? v_scale : nullptr, stream);
+}
+
 int paged_attn_balanced_workgroups(const pa_dims* dims, int32_t num_q_pos) {
   int st = check_balanced(dims, num_q_pos, 1);
   if (st != PA_OK) return st;

@@ -10,6 +10,10 @@
 // Gather copies every sequence's tokens out of the pool in logical order through the same
 // tile addressing the attention kernels use, so its output checks that translation
 // bit for bit.
+//
+// Block copy (copy-on-write of shared blocks, tutorial section 7): for each (src, dst)
+// pair every KV head's K and V tile of block src is copied to block dst (and the int8
+// scales).  Each thread moves one 16-byte piece of one pair.
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
@@ -95,7 +99,58 @@ int gather_t(const void* k_cache, const void* v_cache, const int32_t* block_tabl
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+// A pair's data is 2 * Hkv tiles (K and V of every KV head), taken as 16-byte pieces in
+// the order K(g = 0), V(0), K(1), ... (ascending addresses in the interleaved layout).
+// Workgroup (pair, part) moves pieces [part * 256, (part + 1) * 256), one per thread, with
+// non-temporal loads and stores: copied blocks are not read again by this launch, and
+// keeping them out of the caches measured faster than plain accesses and than several
+// pieces in flight per thread.
+__global__ __launch_bounds__(256) void kv_copy_blocks_kernel(
+    const int32_t* __restrict__ pairs, int32_t num_kv_heads, int64_t num_blocks,
+    int32_t tile_shift, int32_t parts, int64_t tile_stride_bytes, uint8_t* k_cache,
+    uint8_t* v_cache, float* k_scale, float* v_scale) {
+  const int64_t p = blockIdx.x / parts;
+  const int part = (int)(blockIdx.x % parts);
+  const int32_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+  const int total = (2 * num_kv_heads) << tile_shift;
+  const int c = part * 256 + (int)threadIdx.x;
+  if (c < total) {
+    const int t = c >> tile_shift;
+    uint8_t* base = (t & 1) ? v_cache : k_cache;
+    const int64_t off = (int64_t)(c & ((1 << tile_shift) - 1)) * 16;
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        base + kv_tile(src, t >> 1, num_kv_heads) * tile_stride_bytes + off));
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(
+        base + kv_tile(dst, t >> 1, num_kv_heads) * tile_stride_bytes + off));
+  }
+  if (k_scale != nullptr && part == 0) {
+    for (int g = threadIdx.x; g < num_kv_heads; g += 256) {
+      k_scale[kv_tile(dst, g, num_kv_heads)] = k_scale[kv_tile(src, g, num_kv_heads)];
+      v_scale[kv_tile(dst, g, num_kv_heads)] = v_scale[kv_tile(src, g, num_kv_heads)];
+    }
+  }
+}
+
 }  // namespace
+
+int launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, int32_t num_kv_heads,
+                       int32_t head_dim, int64_t num_blocks, int64_t tile_stride,
+                       int elem_bytes, void* k_cache, void* v_cache, float* k_scale,
+                       float* v_scale, void* stream) {
+  // pieces per tile = head_dim * elem_bytes (a power of two: 64 or 128 dims, 1/2/4 bytes)
+  int shift = 0;
+  while ((1 << shift) < head_dim * elem_bytes) ++shift;
+  const int64_t total = (int64_t)(2 * num_kv_heads) << shift;
+  const int64_t parts = (total + 255) / 256;
+  const int64_t grid = (int64_t)num_pairs * parts;
+  if (grid > 0x7fffffff || total > 0x7fffffff) return PA_ERR_DIMS;
+  hipLaunchKernelGGL(kv_copy_blocks_kernel, dim3((unsigned)grid), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), pairs, num_kv_heads, num_blocks, shift,
+                     (int32_t)parts, tile_stride * elem_bytes, static_cast<uint8_t*>(k_cache),
+                     static_cast<uint8_t*>(v_cache), k_scale, v_scale);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
 
 int launch_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,

@@ -69,6 +69,12 @@ int launch_append(const void* k_new, const void* v_new, const int64_t* slot_mapp
                   int64_t num_blocks, int64_t tile_stride, int elem_bytes, void* k_cache,
                   void* v_cache, void* stream);
 
+// tile_stride in elements; scales may be null (non-int8 caches)
+int launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, int32_t num_kv_heads,
+                       int32_t head_dim, int64_t num_blocks, int64_t tile_stride,
+                       int elem_bytes, void* k_cache, void* v_cache, float* k_scale,
+                       float* v_scale, void* stream);
+
 int launch_gather(const void* k_cache, const void* v_cache, const int32_t* block_tables,
                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
                   int32_t head_dim, int32_t max_blocks, int64_t num_blocks, int64_t tile_stride,

@@ -25,7 +25,8 @@ def test_header_declares_the_entry_points():
     for n in ["kv_append", "paged_decode_attn", "paged_verify_attn", "paged_decode_attn_split",
               "lse_merge", "paged_attn_balanced", "paged_attn_balanced_merge",
               "paged_attn_balanced_workspace_bytes", "paged_attn_balanced_workgroups",
-              "paged_split_workspace_bytes", "kv_gather", "paged_status_string"]:
+              "paged_split_workspace_bytes", "kv_gather", "paged_status_string",
+              "paged_decode_step", "kv_copy_blocks"]:
         assert n in names
 
 
@@ -82,6 +83,18 @@ def test_tile_stride_and_alignment_checks():
     assert _decode(d, k=FAKE + 4) == -9
     assert _decode(d, v=FAKE + 2) == -9
     assert _decode(d, out=FAKE + 8) == -9
+
+
+def test_copy_blocks_checks():
+    d = _dims()
+    f = ctypes.c_void_p(FAKE)
+    assert P.lib.kv_copy_blocks(ctypes.byref(d), f, -1, f, f, None, None, None) == -2
+    assert P.lib.kv_copy_blocks(ctypes.byref(d), f, 0, f, f, None, None, None) == 0
+    assert P.lib.kv_copy_blocks(ctypes.byref(d), None, 3, f, f, None, None, None) == -1
+    di8 = _dims(kv_dtype="i8")
+    assert P.lib.kv_copy_blocks(ctypes.byref(di8), f, 3, f, f, None, None, None) == -1
+    assert P.lib.kv_copy_blocks(ctypes.byref(d), f, 3, ctypes.c_void_p(FAKE + 4), f, None, None,
+                                None) == -9
 
 
 def test_null_pointer_checks():

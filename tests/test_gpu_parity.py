@@ -123,6 +123,110 @@ def test_kv_gather_bit_exact(P, name, interleave):
     assert np.array_equal(raw(v_out.cpu()).view(np.uint8), vo.view(np.uint8))
 
 
+# ---- block copy (copy-on-write): bit exact ---------------------------------------------
+def _gpu_copy(P, wl, dv, pairs):
+    pd = pairs.to("cuda:0")
+    P.kv_copy_blocks(dims_of(P, wl, dv), pd, pairs.shape[0], dv.k_cache, dv.v_cache,
+                     dv.k_scale, dv.v_scale)
+    torch.cuda.synchronize()
+
+
+def _check_pool(dv, kc, vc, ks=None, vs=None):
+    gk, gv = dv.caches_host()
+    assert np.array_equal(raw(gk).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(raw(gv).view(np.uint8), vc.view(np.uint8))
+    if ks is not None:
+        assert np.array_equal(raw(dv.k_scale).view(np.uint8), ks.view(np.uint8))
+        assert np.array_equal(raw(dv.v_scale).view(np.uint8), vs.view(np.uint8))
+
+
+@pytest.mark.parametrize("interleave", [False, True])
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b", "verify_int8"])
+def test_kv_copy_blocks_bit_exact(P, name, interleave):
+    wl = _small(name, spare=12, batch=6, length_range=(1, 200), append=False)
+    nb = wl.k_cache.shape[0]
+    pairs = W.copy_pairs(wl, 9, seed=5)
+    free = sorted(set((wl.occupancy == 0).nonzero().flatten().tolist()) -
+                  set(pairs[:, 1].tolist()))
+    skip = torch.tensor([[-1, free[0]], [int(pairs[0, 0]), nb], [free[1], free[1]],
+                         [nb + 5, free[2]], [int(pairs[1, 0]), -7]], dtype=torch.int32)
+    allp = torch.cat([pairs[:4], skip, pairs[4:]]).contiguous()
+    say(f"[case] copy_blocks {name} interleave={interleave} pairs={allp.shape[0]} NB={nb}")
+    dv = Dev(wl, interleave)
+    _gpu_copy(P, wl, dv, allp)
+    kc, vc, ks, vs = paging.copy_blocks(raw(wl.k_cache), raw(wl.v_cache), allp.numpy(),
+                                        raw(wl.k_scale), raw(wl.v_scale))
+    _check_pool(dv, kc, vc, ks, vs)
+    # no pairs: nothing launched, nothing changed
+    P.kv_copy_blocks(dims_of(P, wl, dv), allp.cuda(), 0, dv.k_cache, dv.v_cache, dv.k_scale,
+                     dv.v_scale)
+    torch.cuda.synchronize()
+    _check_pool(dv, kc, vc, ks, vs)
+
+
+@pytest.mark.parametrize("interleave", [False, True])
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b"])
+def test_copy_on_write_then_decode(P, name, interleave):
+    """Parallel sampling: sequences fork with every block shared (the partly filled last
+    one too); on the next token each writer of a still-shared block gets a private copy.
+    GPU: block copy, append, decode attention; oracle: the same three steps."""
+    from dataclasses import replace
+    wl = _small(name, spare=16, lengths=[37, 50, 16, 129, 3], batch=5, append=False)
+    c = wl.cfg
+    alloc = wl.meta["allocator"]
+    for parent, child in [(0, 5), (3, 6), (4, 7), (4, 8)]:
+        alloc.fork_all(parent, child)
+    B = 9
+    slots, pairs = [0] * B, []
+    for i in [5, 0, 6, 3, 7, 8, 4, 1, 2]:          # children write first: they copy
+        slots[i], cp = alloc.append_token(i)
+        if cp is not None:
+            pairs.append(cp)
+    assert len(pairs) == 4
+    rows = [alloc.block_tables[i] for i in range(B)]
+    tables = torch.full((B, max(map(len, rows))), -1, dtype=torch.int32)
+    for i, r in enumerate(rows):
+        tables[i, :len(r)] = torch.tensor(r, dtype=torch.int32)
+    gen = torch.Generator().manual_seed(77)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    q = torch.randn((B, 1, c.num_q_heads, c.head_dim), generator=gen).to(dt[c.q_dtype])
+    kn = torch.randn((B, c.num_kv_heads, c.head_dim), generator=gen).to(dt[c.kv_dtype])
+    vn = torch.randn((B, c.num_kv_heads, c.head_dim), generator=gen).to(dt[c.kv_dtype])
+    wl2 = replace(wl, cfg=replace(c, batch=B, lengths=None), q=q, block_tables=tables,
+                  seq_lens=torch.tensor([alloc.token_counts[i] for i in range(B)],
+                                        dtype=torch.int32),
+                  slot_mapping=torch.tensor(slots, dtype=torch.int64), k_new=kn, v_new=vn)
+    pt = torch.tensor(pairs, dtype=torch.int32)
+    say(f"[case] copy-on-write {name} interleave={interleave} pairs={pairs}")
+    dv = Dev(wl2, interleave)
+    _gpu_copy(P, wl2, dv, pt)
+    gpu_append(P, wl2, dv)
+    out, _, _ = gpu_attention(P, wl2, dv)
+    out_b, _, _ = gpu_attention(P, wl2, dv, balanced=0)
+    torch.cuda.synchronize()
+    kc, vc, _, _ = paging.copy_blocks(raw(wl.k_cache), raw(wl.v_cache), pt.numpy())
+    kc, vc = paging.append(kc, vc, raw(kn), raw(vn), np.array(slots))
+    _check_pool(dv, kc, vc)
+    ref, _ = oracle_attention(wl2, kc, vc)
+    for o in (out, out_b):
+        err = max_err(o, ref)
+        say(f"  max abs err {err:.3e}")
+        assert err <= TOL[c.kv_dtype]
+    # a child and its parent share every block but the last
+    assert rows[5][:-1] == rows[0][:-1] and rows[5][-1] != rows[0][-1]
+
+
+def test_kv_copy_blocks_full_llama3_8b_pool(P):
+    """The benchmark's bulk copy: 2048 pairs on the Llama-3-8B pool, whole pool compared."""
+    wl = W.generate(W.scaled("llama3_8b", append=False), spare_blocks=2048)
+    pairs = W.copy_pairs(wl, 2048, seed=3)
+    say(f"[case] copy_blocks full llama3_8b pairs=2048 NB={wl.k_cache.shape[0]}")
+    dv = Dev(wl, True)
+    _gpu_copy(P, wl, dv, pairs)
+    kc, vc, _, _ = paging.copy_blocks(raw(wl.k_cache), raw(wl.v_cache), pairs.numpy())
+    _check_pool(dv, kc, vc)
+
+
 # ---- attention, small shapes (several tiles, ragged tails, edge cases) ---------------
 def test_tiny_fp32_config(P):
     wl = W.generate("tiny_fp32")

@@ -37,6 +37,32 @@ def test_fork_shares_prefix_refcounted():
     assert sorted(a.free_blocks) == list(range(20))
 
 
+def test_copy_on_write_on_the_first_write_into_a_shared_block():
+    a = W.BlockAllocator(12, 16, free_order=list(range(12)))
+    a.allocate(0, 37)                                 # blocks 11, 10, 9; 5 tokens in block 9
+    a.fork_all(0, 1)
+    assert a.block_tables[1] == [11, 10, 9] and a.refcount[9] == 2
+    slot, copy = a.append_token(1)                    # writes position 37 into shared block 9
+    assert copy == (9, 8) and a.block_tables[1] == [11, 10, 8]
+    assert slot == 8 * 16 + 5
+    assert a.refcount[9] == 1 and a.refcount[8] == 1 and a.refcount[11] == 2
+    slot, copy = a.append_token(0)                    # block 9 is now the parent's alone
+    assert copy is None and slot == 9 * 16 + 5
+    for _ in range(10):                               # positions 38..47 stay in block 8
+        assert a.append_token(1)[1] is None
+    slot, copy = a.append_token(1)                    # position 48: a new block, no copy
+    assert copy is None and a.block_tables[1] == [11, 10, 8, 7] and slot == 7 * 16
+    a.release(0)
+    assert a.refcount[11] == 1 and 9 in a.free_blocks and 11 not in a.free_blocks
+    a.release(1)
+    assert sorted(a.free_blocks) == list(range(12))
+    b = W.BlockAllocator(8, 16)
+    b.allocate(0, 32)                                  # two full blocks
+    b.fork_all(0, 1)
+    slot, copy = b.append_token(1)                     # full shared block: new block, no copy
+    assert copy is None and b.block_tables[1][:2] == b.block_tables[0]
+
+
 @pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b", "verify_int8"])
 def test_tables_distinct_and_sized(name):
     wl = W.generate(name)

@@ -77,13 +77,34 @@ class BlockAllocator:
         self.token_counts[child_id] = total_tokens
         return self.block_tables[child_id]
 
+    def fork_all(self, parent_id, child_id):
+        """Child shares every block of the parent, the partly filled last one included
+        (parallel sampling from one prompt); the first of them to write into a shared
+        block copies it (``append_token``)."""
+        blocks = self.block_tables[parent_id]
+        for blk in blocks:
+            self.refcount[blk] += 1
+        self.block_tables[child_id] = list(blocks)
+        self.token_counts[child_id] = self.token_counts[parent_id]
+        return self.block_tables[child_id]
+
     def append_token(self, request_id):
-        """Account one more token; takes a new block when the last one is full."""
+        """Account one more token and return its pool slot plus the block copy it needs:
+        (slot, None), or (slot, (src, dst)) when the token lands in a block that other
+        sequences still share, which the sequence first replaces by a private copy (the
+        copy-on-write of devpress tutorial §7).  A full last block gets a new block."""
         blocks = self.block_tables[request_id]
         used = self.token_counts[request_id]
+        copy = None
         if used >= len(blocks) * self.block_size:
             blocks.append(self._take())
+        elif self.refcount[blocks[-1]] > 1:
+            old = blocks[-1]
+            blocks[-1] = self._take()
+            self.refcount[old] -= 1
+            copy = (old, blocks[-1])
         self.token_counts[request_id] = used + 1
+        return blocks[used // self.block_size] * self.block_size + used % self.block_size, copy
 
     def release(self, request_id):
         for blk in self.block_tables.pop(request_id, []):
@@ -306,7 +327,8 @@ def generate(cfg, seed=None, *, poison=True, spare_blocks=0, shuffle_batch=False
 
     wl = Workload(cfg, q, k_cache, v_cache, k_scale, v_scale, tables,
                   torch.tensor(lens, dtype=torch.int32), slot_mapping, k_new, v_new, occ,
-                  meta={"seed": seed, "num_blocks": NB, "max_blocks": max_blocks})
+                  meta={"seed": seed, "num_blocks": NB, "max_blocks": max_blocks,
+                        "allocator": alloc})
     if shuffle_batch:
         perm = torch.randperm(B, generator=gen)
         wl = permute_batch(wl, perm)
@@ -322,7 +344,8 @@ def permute_batch(wl: Workload, perm):
         slot_mapping=None if wl.slot_mapping is None else wl.slot_mapping[p].contiguous(),
         k_new=None if wl.k_new is None else wl.k_new[p].contiguous(),
         v_new=None if wl.v_new is None else wl.v_new[p].contiguous(),
-        meta=dict(wl.meta, batch_perm=p.tolist()))
+        meta=dict({k: v for k, v in wl.meta.items() if k != "allocator"},
+                  batch_perm=p.tolist()))
 
 
 def relabel_blocks(wl: Workload, perm):
@@ -341,7 +364,22 @@ def relabel_blocks(wl: Workload, perm):
         sm = perm[s // BLOCK_SIZE] * BLOCK_SIZE + s % BLOCK_SIZE
     return replace(wl, k_cache=mv(wl.k_cache), v_cache=mv(wl.v_cache), k_scale=mv(wl.k_scale),
                    v_scale=mv(wl.v_scale), block_tables=nt, slot_mapping=sm,
-                   occupancy=mv(wl.occupancy))
+                   occupancy=mv(wl.occupancy),
+                   meta={k: v for k, v in wl.meta.items() if k != "allocator"})
+
+
+def copy_pairs(wl: Workload, n: int, seed: int = 0):
+    """[n, 2] int32 (src, dst) block pairs for a block copy: distinct sources drawn from the
+    blocks that hold live tokens, distinct destinations from the blocks that hold none (so
+    no destination is a source), as copy-on-write produces them."""
+    gen = torch.Generator().manual_seed(seed)
+    used = (wl.occupancy > 0).nonzero().flatten()
+    free = (wl.occupancy == 0).nonzero().flatten()
+    if n > used.numel() or n > free.numel():
+        raise ValueError("not enough used or free blocks for the requested pairs")
+    src = used[torch.randperm(used.numel(), generator=gen)[:n]]
+    dst = free[torch.randperm(free.numel(), generator=gen)[:n]]
+    return torch.stack([src, dst], dim=1).to(torch.int32).contiguous()
 
 
 def _quantise_int8(x32, live):
