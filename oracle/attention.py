@@ -23,6 +23,11 @@ those nq = K + 1 positions, query position i (0 <= i < nq) sits at absolute
 position L - nq + i and, being causal, sees tokens t <= L - nq + i, that is the
 first lam_i = L - nq + 1 + i tokens.  Decode is nq = 1, lam = L.
 
+Sliding window (in-depth guide §2.3, "稀疏注意力与窗口化的工程取舍": each token attends
+only to the most recent W tokens).  Reading taken: the W tokens end at and include the
+row's own position p, so a row sees tokens max(0, p - W + 1) .. p; W = 0 means no window
+(the whole causal prefix).
+
 Context split (not on the pages; stated by the benchmark spec): the tokens visible to a row
 are cut into partitions, attention is taken over each (o_p, lse_p), and the
 partials are recombined with the log-sum-exp identity
@@ -39,22 +44,24 @@ import numpy as np
 from . import paging, storage
 
 
-def attend(q_rows, K, V, sigma, limits):
-    """fp64 attention of each row of ``q_rows`` ([R, d]) over the first
-    ``limits[r]`` rows of K and V ([L, d]).  Returns (out [R, d], lse [R])."""
+def attend(q_rows, K, V, sigma, limits, starts=None):
+    """fp64 attention of each row of ``q_rows`` ([R, d]) over rows
+    [starts[r], limits[r]) of K and V ([L, d]) (starts default to 0).
+    Returns (out [R, d], lse [R])."""
     q_rows = np.asarray(q_rows, dtype=np.float64)
     R, d = q_rows.shape
     out = np.zeros((R, d), dtype=np.float64)
     lse = np.full((R,), -np.inf, dtype=np.float64)
     for r in range(R):
         lam = int(limits[r])
-        if lam <= 0:
+        lo = 0 if starts is None else max(0, int(starts[r]))
+        if lam <= lo:
             continue
-        s = sigma * (K[:lam] @ q_rows[r])
+        s = sigma * (K[lo:lam] @ q_rows[r])
         m = s.max()
         e = np.exp(s - m)
         l = e.sum()
-        out[r] = (e @ V[:lam]) / l
+        out[r] = (e @ V[lo:lam]) / l
         lse[r] = m + np.log(l)
     return out, lse
 
@@ -62,6 +69,14 @@ def attend(q_rows, K, V, sigma, limits):
 def row_limits(seq_len, num_q_pos):
     """Visible-token count of each query position (causal verify rows)."""
     return [max(0, seq_len - num_q_pos + 1 + i) for i in range(num_q_pos)]
+
+
+def row_starts(seq_len, num_q_pos, window):
+    """First visible token of each query position: with a sliding window of W > 0 tokens
+    the row at position p starts at max(0, p - W + 1); with W = 0 at token 0."""
+    if window <= 0:
+        return [0] * num_q_pos
+    return [max(0, lam - window) for lam in row_limits(seq_len, num_q_pos)]
 
 
 def _group_rows(q_dec, b, g, G, num_q_pos):
@@ -76,14 +91,15 @@ def _group_rows(q_dec, b, g, G, num_q_pos):
 
 
 def paged_attention(q, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens, sigma,
-                    num_q_pos=1, k_scale=None, v_scale=None, pairs=None, fast=True):
+                    num_q_pos=1, k_scale=None, v_scale=None, pairs=None, fast=True, window=0):
     """Attention of every query row against its sequence's paged cache.
 
     q: [B, nq, Hq, d] stored as ``q_kind``; caches in the project format (see
     ``paging``).  Returns (out [B, nq, Hq, d], lse [B, nq, Hq]) in fp64.  With
     ``pairs`` (a list of (b, g)) only those sequence/KV-head pairs are computed and
     every other entry is NaN.  ``sigma`` is used as given (pass the fp32 value the
-    kernel receives, widened).
+    kernel receives, widened).  ``window`` > 0: sliding-window attention over the
+    ``window`` most recent tokens of each row (``row_starts``).
     """
     qd = storage.decode(q, q_kind)
     B, nq, Hq, d = qd.shape
@@ -100,7 +116,8 @@ def paged_attention(q, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens
         K, V = dep(k_cache, v_cache, kv_kind, block_tables[b], L, g, k_scale, v_scale)
         rows, idx = _group_rows(qd, b, g, G, nq)
         lim = row_limits(L, nq)
-        o, ls = attend(rows, K, V, sigma, [lim[i] for i, _ in idx])
+        lo = row_starts(L, nq, window)
+        o, ls = attend(rows, K, V, sigma, [lim[i] for i, _ in idx], [lo[i] for i, _ in idx])
         for r, (i, h) in enumerate(idx):
             out[b, i, h] = o[r]
             lse[b, i, h] = ls[r]

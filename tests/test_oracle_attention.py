@@ -205,3 +205,89 @@ def test_verify_causal_closed_form():
         assert np.allclose(out[0, i], p / 2, atol=1e-12)
         # lse of p+1 equal scores s = 0.5 * d
         assert abs(lse[0, i, 0] - (0.5 * d + math.log(p + 1))) < 1e-12
+
+
+def test_sliding_window_closed_form():
+    # Uniform attention over V[t] = t with a window of W tokens: the row at absolute
+    # position p sees tokens max(0, p - W + 1) .. p, so its output is their mean
+    # (lo + p) / 2 and its lse is s + log(p - lo + 1).
+    L, nq, d, G = 37, 6, 4, 2
+    tables = np.array([[2, 0, 1]], dtype=np.int32)
+    kc = np.ones((3, 1, d // 4, 16, 4), np.float32)
+    vc = np.zeros((3, 1, d, 16), np.float32)
+    for t in range(48):
+        vc[tables[0, t // 16], 0, :, t % 16] = t
+    q = np.ones((1, nq, G, d), np.float32)
+    for Wn in (1, 2, 5, 16, 17, 33, 34, 100):
+        out, lse = attention.paged_attention(q, "f32", kc, vc, "f32", tables, np.array([L]),
+                                             0.5, nq, window=Wn)
+        for i in range(nq):
+            p = L - nq + i
+            lo = max(0, p - Wn + 1)
+            assert np.allclose(out[0, i], (lo + p) / 2, atol=1e-12), (Wn, i)
+            assert abs(lse[0, i, 0] - (0.5 * d + math.log(p - lo + 1))) < 1e-12
+
+
+def test_sliding_window_of_one_is_own_value():
+    wl = _small("tiny_fp32", head_dim=16, length_range=(1, 60))
+    out, lse = _paged(wl, window=1)
+    Kt = W.k_token_rows(wl.k_cache).numpy()              # [NB, Hkv, 16, d], by the generator
+    q = wl.q.float().numpy().astype(np.float64)
+    sig = float(np.float32(wl.sm_scale))
+    G = wl.cfg.group_size
+    for b in range(wl.cfg.batch):
+        L = int(wl.seq_lens[b])
+        blk = int(wl.block_tables[b, (L - 1) // 16])
+        for h in range(wl.cfg.num_q_heads):
+            v = wl.v_cache[blk, h // G, :, (L - 1) % 16].numpy()
+            assert np.array_equal(out[b, 0, h], v.astype(np.float64))
+            k = Kt[blk, h // G, (L - 1) % 16].astype(np.float64)
+            assert abs(lse[b, 0, h] - sig * (q[b, 0, h] @ k)) < 1e-12
+
+
+@pytest.mark.parametrize("Wn", [3, 16, 40])
+def test_sliding_window_equals_full_attention_over_the_recent_tokens(Wn):
+    """Brute force through another cache: each row's windowed result equals full attention
+    over a fresh one-sequence pool that holds only that row's last Wn tokens, built from
+    the generator's token-major values and re-encoded by it."""
+    wl = _small("verify_int8", kv_dtype="bf16", head_dim=32, num_q_heads=4, num_kv_heads=2,
+                length_range=(1, 80))
+    c = wl.cfg
+    nq = c.num_q_pos
+    out, lse = _paged(wl, window=Wn)
+    Kt = W.k_token_rows(wl.k_cache)                      # [NB, Hkv, 16, d] bf16
+    Vt = wl.v_cache.transpose(2, 3)                      # [NB, Hkv, 16, d]
+    raw = lambda x: x.view(torch.int16).numpy()
+    for b in range(c.batch):
+        L = int(wl.seq_lens[b])
+        for i in range(nq):
+            p = L - nq + i
+            if p < 0:
+                assert np.all(lse[b, i] == -np.inf)
+                continue
+            toks = list(range(max(0, p - Wn + 1), p + 1))
+            nb = -(-len(toks) // 16)
+            kt = torch.zeros((nb, c.num_kv_heads, 16, c.head_dim), dtype=torch.bfloat16)
+            vt = torch.zeros_like(kt)
+            for n, t in enumerate(toks):
+                blk = int(wl.block_tables[b, t // 16])
+                kt[n // 16, :, n % 16] = Kt[blk, :, t % 16]
+                vt[n // 16, :, n % 16] = Vt[blk, :, t % 16]
+            kc, vc = W.encode_k(kt), W.encode_v(vt)
+            o2, l2 = attention.paged_attention(
+                raw(wl.q[b:b + 1, i:i + 1]), "bf16", raw(kc), raw(vc), "bf16",
+                np.arange(nb, dtype=np.int32)[None], np.array([len(toks)]),
+                float(np.float32(wl.sm_scale)), 1)
+            assert np.allclose(out[b, i], o2[0, 0], rtol=0, atol=1e-13)
+            assert np.allclose(lse[b, i], l2[0, 0], rtol=0, atol=1e-12)
+
+
+def test_sliding_window_at_least_the_context_is_full_attention():
+    wl = _small("verify_int8", head_dim=32, num_q_heads=4, num_kv_heads=2, length_range=(1, 70))
+    out, lse = _paged(wl)
+    for Wn in (70, 71, 1000):
+        o2, l2 = _paged(wl, window=Wn)
+        assert np.array_equal(out, o2) and np.array_equal(lse, l2)
+    assert attention.row_starts(50, 3, 0) == [0, 0, 0]
+    assert attention.row_starts(50, 3, 10) == [38, 39, 40]
+    assert attention.row_starts(5, 3, 10) == [0, 0, 0]

@@ -16,8 +16,8 @@ MUTATIONS = [
      "test_oracle_attention.py"),
     ("verify limit off by one", "oracle/attention.py", "seq_len - num_q_pos + 1 + i",
      "seq_len - num_q_pos + i", "test_oracle_attention.py"),
-    ("softmax scale dropped", "oracle/attention.py", "s = sigma * (K[:lam] @ q_rows[r])",
-     "s = (K[:lam] @ q_rows[r])", "test_oracle_attention.py"),
+    ("softmax scale dropped", "oracle/attention.py", "s = sigma * (K[lo:lam] @ q_rows[r])",
+     "s = (K[lo:lam] @ q_rows[r])", "test_oracle_attention.py"),
     ("lse without the max", "oracle/attention.py", "lse[r] = m + np.log(l)", "lse[r] = np.log(l)",
      "test_oracle_attention.py"),
     ("merge weight sign", "oracle/attention.py", "w = np.exp(lp[live] - M)",
@@ -59,6 +59,15 @@ MUTATIONS = [
      "test_oracle_paging.py"),
     ("KV-size factor 2 dropped", "oracle/kvsize.py", "return 2 * n_layers * batch",
      "return n_layers * batch", "test_oracle_kvsize.py"),
+    ("window one token too wide", "oracle/attention.py",
+     "return [max(0, lam - window) for lam in", "return [max(0, lam - window - 1) for lam in",
+     "test_oracle_attention.py"),
+    ("window start of the last row for every row", "oracle/attention.py",
+     "return [max(0, lam - window) for lam in row_limits(seq_len, num_q_pos)]",
+     "return [max(0, seq_len - window)] * num_q_pos", "test_oracle_attention.py"),
+    ("window start ignored", "oracle/attention.py",
+     "lo = 0 if starts is None else max(0, int(starts[r]))", "lo = 0",
+     "test_oracle_attention.py"),
     ("copy direction swapped", "oracle/paging.py", "kc[dst] = k_cache[src]",
      "kc[src] = k_cache[dst]", "test_oracle_paging.py"),
     ("copy skips V", "oracle/paging.py", "vc[dst] = v_cache[src]", "pass",
