@@ -105,7 +105,8 @@ class Runner:
         self.dims = P.make_dims(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
                                 wl.block_tables.shape[1], wl.k_cache.shape[0], c.q_dtype,
                                 c.kv_dtype,
-                                kv_tile_stride=2 * tile if layout == "interleaved" else 0)
+                                kv_tile_stride=2 * tile if layout == "interleaved" else 0,
+                                sliding_window=c.sliding_window)
         self.sm = float(np.float32(c.sm_scale))
         self.out = torch.empty((c.batch, c.num_q_pos, c.num_q_heads, c.head_dim),
                                dtype=torch.float32, device=dev)
@@ -405,7 +406,7 @@ def trace_summary(args, trace_dir):
         last = k
         if cur is not None:
             cur.setdefault(k, []).append((e - s0) / 1000)
-    names = ["llama3_8b", "llama2_70b_prefix", "long_128k", "verify_int8"]
+    names = ["llama3_8b", "llama2_70b_prefix", "long_128k", "verify_int8", "mistral_7b_window"]
     lines = [f"# rocprofv3 kernel trace: bench.py --path {args.path} --layout {args.layout}", "",
              "Command (MI355X, one GPU):", "",
              f"    rocprofv3 --kernel-trace --stats -d {trace_dir} -o run -- python bench.py "
@@ -465,7 +466,7 @@ def main():
 
     others = {}
     if not args.no_others:
-        for name in ("llama2_70b_prefix", "long_128k", "verify_int8"):
+        for name in ("llama2_70b_prefix", "long_128k", "verify_int8", "mistral_7b_window"):
             w2 = W.generate(name, poison=False)
             copies = 1 if name == "long_128k" else 2
             r2 = Runner(P, w2, "step", None, copies=copies, layout=args.layout)

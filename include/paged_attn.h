@@ -94,6 +94,11 @@ typedef struct pa_dims {
                                  k_cache and in v_cache; 0 means 16 * head_dim (dense).
                                  Otherwise >= 16 * head_dim and a multiple of 16 bytes
                                  (PA_ERR_DIMS)                                             */
+  int32_t sliding_window;     /* W: 0 = every cached token; W > 0 = the row at position p
+                                 attends tokens max(0, p - W + 1) .. p only (sliding-window
+                                 attention, in-depth guide section 2.3).  Every attention
+                                 call honours it; kv_append, kv_gather and kv_copy_blocks
+                                 ignore it.  < 0 is PA_ERR_DIMS                             */
 } pa_dims;
 /* Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, I8). */
 

@@ -34,7 +34,8 @@ class pa_dims(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int64), ("q_dtype", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32), ("kv_tile_stride", ctypes.c_int64)]
+                ("kv_dtype", ctypes.c_int32), ("kv_tile_stride", ctypes.c_int64),
+                ("sliding_window", ctypes.c_int32)]
 
 
 def _load(path=_LIB_PATH):
@@ -74,11 +75,12 @@ LIB_PATH = _LIB_PATH
 
 
 def make_dims(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
-              q_dtype, kv_dtype, block_size=16, kv_tile_stride=0):
-    """kv_tile_stride: elements between consecutive (block, KV head) tiles (0 = dense)."""
+              q_dtype, kv_dtype, block_size=16, kv_tile_stride=0, sliding_window=0):
+    """kv_tile_stride: elements between consecutive (block, KV head) tiles (0 = dense);
+    sliding_window: tokens each row attends, ending at its own position (0 = all)."""
     return pa_dims(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                    max_blocks_per_seq, num_blocks, _DTYPE_CODE[q_dtype], _DTYPE_CODE[kv_dtype],
-                   kv_tile_stride)
+                   kv_tile_stride, sliding_window)
 
 
 def _p(x):

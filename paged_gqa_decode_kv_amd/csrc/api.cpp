@@ -24,6 +24,7 @@ int check_dims(const pa_dims* d) {
   if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_DIMS;
   // token positions are int32 inside the kernels
   if ((int64_t)d->max_blocks_per_seq * 16 > INT_MAX) return PA_ERR_DIMS;
+  if (d->sliding_window < 0) return PA_ERR_DIMS;
   if (d->kv_tile_stride != 0) {
     const int eb = d->kv_dtype == PA_F32 ? 4 : (d->kv_dtype == PA_BF16 ? 2 : 1);
     if (d->kv_tile_stride < 16 * (int64_t)d->head_dim || d->kv_tile_stride > (INT64_MAX >> 40) ||
@@ -84,6 +85,7 @@ pa::AttnArgs make_args(const pa_dims* d, int32_t nq, const void* q, const void* 
   a.part_tokens = 0;
   a.max_parts = 1;
   a.split = 0;
+  a.window = d->sliding_window;
   return a;
 }
 

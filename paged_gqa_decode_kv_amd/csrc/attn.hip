@@ -381,12 +381,13 @@ struct Rows {
     inv_vref256 = kInt8 ? 256.f / vref : 1.f;
   }
 
-  // One 16-token block whose first token is tok0: rows see tokens < lim[nt] (lim_min is
-  // the smallest over the wave's rows); tokens >= hi are past the sequence end and their
-  // V may be poisoned.  sc = softmax scale * log2(e) (times the block's K scale for int8);
+  // One 16-token block whose first token is tok0: rows see tokens in [lo[nt], lim[nt])
+  // (lim_min is the smallest limit over the wave's rows, lo_max the largest start: a
+  // sliding window's); tokens >= hi are past the sequence end and their V may be poisoned.  sc = softmax scale * log2(e) (times the block's K scale for int8);
   // vs = the block's V scale (int8).
   __device__ __forceinline__ void update(const typename KV::Q* qop, const int* lim, int lim_min,
-                                         int hi, typename KV::K& kk, typename KV::V& vv,
+                                         const int* lo, int lo_max, int hi,
+                                         typename KV::K& kk, typename KV::V& vv,
                                          int tok0, float sc, float vs, int grp) {
     float vfac = 1.f;
     if constexpr (kInt8) {
@@ -405,6 +406,7 @@ struct Rows {
       }
     }
     const bool need_mask = tok0 + kBlockTokens > lim_min;
+    const bool need_lo = tok0 < lo_max;
     f32x4 pr[NT];
     float alpha[NT];
     const auto& km = KV::k_mat(kk);
@@ -415,6 +417,7 @@ struct Rows {
       for (int e = 0; e < 4; ++e) {
         float x = sv[e] * sc;
         if (need_mask && tok0 + 4 * grp + e >= lim[nt]) x = -INFINITY;
+        if (need_lo && tok0 + 4 * grp + e < lo[nt]) x = -INFINITY;
         sv[e] = x;
       }
       float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
@@ -456,12 +459,19 @@ struct Rows {
   }
 };
 
+// First token a query row at causal limit lam (it sees tokens < lam) may attend: with a
+// sliding window of W tokens ending at its own position, lam - W.
+__device__ __forceinline__ int window_start(int lam, int window) {
+  return window > 0 && lam > window ? lam - window : 0;
+}
+
 // Query rows of row tile rg for KV head g of sequence b: the MFMA B operand of each 16-row
-// tile and the causal limit of this lane's row (tokens [.., lim) visible; lim capped at
-// hi).  Returns the smallest limit over the tile's rows.
+// tile and the visible range of this lane's row (tokens [lo, lim); lim capped at hi).
+// Returns the smallest limit over the tile's rows; lo_max receives the largest start.
 template <class KV, int D, int NT>
 __device__ __forceinline__ int load_rows(const AttnArgs& a, int b, int g, int rg, int L, int hi,
-                                         typename KV::Q* qop, int* lim, int row16, int grp) {
+                                         typename KV::Q* qop, int* lim, int* lo, int& lo_max,
+                                         int row16, int grp) {
   const int row_base = rg * 16 * NT;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -474,7 +484,14 @@ __device__ __forceinline__ int load_rows(const AttnArgs& a, int b, int g, int rg
     int lam = valid ? L - a.num_q_pos + 1 + i : L;
     lam = lam < 0 ? 0 : lam;
     lim[nt] = lam < hi ? lam : hi;
+    lo[nt] = window_start(lam, a.window);
   }
+  // the tile's last row has the largest start
+  int r_last = row_base + 16 * NT - 1;
+  r_last = r_last < a.rows ? r_last : a.rows - 1;
+  int lam_last = L - a.num_q_pos + 1 + r_last / a.group;
+  lam_last = lam_last < 0 ? 0 : lam_last;
+  lo_max = window_start(lam_last, a.window);
   const int i0 = row_base / a.group;
   int lam0 = L - a.num_q_pos + 1 + i0;
   lam0 = lam0 < 0 ? 0 : lam0;
@@ -540,8 +557,9 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   const int nk = je - jb - w > 0 ? (je - jb - w + W - 1) / W : 0;
 
   typename KV::Q qop[NT];
-  int lim[NT];
-  const int lim_min = load_rows<KV, D, NT>(a, b, g, rg, L, hi, qop, lim, row16, grp);
+  int lim[NT], lo_row[NT], lo_max;
+  const int lim_min = load_rows<KV, D, NT>(a, b, g, rg, L, hi, qop, lim, lo_row, lo_max, row16,
+                                           grp);
 
   const int64_t tile_bytes = a.tile_stride;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache);
@@ -617,8 +635,8 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, const Slot& sl) {
     if (sl.ph < 0) return;
     const int tok0 = (jb + w + W * kidx) * kBlockTokens;
-    st.update(qop, lim, lim_min, hi, kk, vv, tok0, a.scale_log2 * (kInt8 ? sl.ks : 1.f), sl.vs,
-              grp);
+    st.update(qop, lim, lim_min, lo_row, lo_max, hi, kk, vv, tok0,
+              a.scale_log2 * (kInt8 ? sl.ks : 1.f), sl.vs, grp);
   };
 
   {
@@ -731,6 +749,15 @@ void paged_attn_kernel(AttnArgs a) {
     lo = p * a.part_tokens;
     hi = (p == nparts - 1) ? L : lo + a.part_tokens;
   }
+  // sliding window: no row of this sequence sees a block before the first row's window
+  // (a partition wholly before it is left empty: zero rows, lse = -inf)
+  if (a.window > 0) {
+    int lam0 = L - a.num_q_pos + 1;
+    lam0 = lam0 < 0 ? 0 : lam0;
+    const int w0 = window_start(lam0, a.window) / kBlockTokens * kBlockTokens;
+    lo = lo > w0 ? lo : w0;
+    if (hi < lo) hi = lo;  // lo is a multiple of 16 here, so the unit reads no block
+  }
   attend_unit<KV, D, NT, W, NBUF>(a, a.split ? kSplit : kDirect, b, g, rg, L, lo, hi, p);
 }
 
@@ -775,6 +802,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   constexpr bool kInt8 = IsInt8<KV>::value;
   constexpr int kStage = 64;
   __shared__ int s_pref[kMaxBalancedSeqs + 1];
+  __shared__ int s_fb[kMaxBalancedSeqs];  // first block a row of the sequence may see
   const int64_t wid = xcd_logical_id();
   if (wid >= a.num_workgroups) return;
   const int lane = threadIdx.x & (kWave - 1);
@@ -783,13 +811,23 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   const int grp = lane >> 4;
   const int B = a.num_seqs;
 
-  // prefix over sequences of their block counts, by the whole workgroup
+  // prefix over sequences of their block counts, by the whole workgroup.  With a sliding
+  // window a sequence's list starts at the block holding its first row's first visible
+  // token; the blocks before it are not dealt out at all.
   __shared__ int s_scan[kWave * W];
   int carry = 0;
   if (threadIdx.x == 0) s_pref[0] = 0;
   for (int c0 = 0; c0 < B; c0 += kWave * W) {
     const int bb = c0 + (int)threadIdx.x;
-    const int nb = bb < B ? (clamp_len(a.seq_lens[bb], a.max_blocks) + kBlockTokens - 1) / kBlockTokens : 0;
+    int nb = 0;
+    if (bb < B) {
+      const int Lb = clamp_len(a.seq_lens[bb], a.max_blocks);
+      int lam0 = Lb - a.num_q_pos + 1;
+      lam0 = lam0 < 0 ? 0 : lam0;
+      const int fb = window_start(lam0, a.window) / kBlockTokens;
+      s_fb[bb] = fb;
+      nb = (Lb + kBlockTokens - 1) / kBlockTokens - fb;
+    }
     s_scan[threadIdx.x] = nb;
     __syncthreads();
     for (int off = 1; off < kWave * W; off <<= 1) {
@@ -822,6 +860,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   struct Seg {
     int j, start, end;
     int b, g, rg;
+    int fb;  // table index of the segment's first block
   };
   auto locate = [&](int x) -> Seg {
     Seg sg;
@@ -838,6 +877,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     sg.j = gr * B + lo_b;
     sg.start = gr * T + __builtin_amdgcn_readfirstlane(s_pref[lo_b]);
     sg.end = gr * T + __builtin_amdgcn_readfirstlane(s_pref[lo_b + 1]);
+    sg.fb = __builtin_amdgcn_readfirstlane(s_fb[lo_b]);
     return sg;
   };
 
@@ -864,7 +904,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
         if (s_pref[mid] <= r) lo_b = mid; else hi_b = mid - 1;
       }
       const int g = gr / nrg;
-      const int ph = a.block_tables[(int64_t)lo_b * a.max_blocks + (r - s_pref[lo_b])];
+      const int ph = a.block_tables[(int64_t)lo_b * a.max_blocks + (r - s_pref[lo_b]) + s_fb[lo_b]];
       if (ph >= 0 && (int64_t)ph < a.num_blocks) {
         tile = (int)kv_tile(ph, g, a.num_kv_heads);
         if constexpr (kInt8) {
@@ -904,9 +944,9 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   Seg cur;
   cur.end = x0;  // nothing consumed yet
   cur.j = -1;
-  int L = 0, lim_min = 0, lim[NT];
+  int L = 0, lim_min = 0, lim[NT], lo_row[NT], lo_max = 0;
   typename KV::Q qop[NT], qnext[NT];
-  int lim_next[NT], lim_min_next = 0;
+  int lim_next[NT], lim_min_next = 0, lo_next[NT], lo_max_next = 0;
   typename KV::NewTok tok, tok_next;  // APP: the new token of the current / next segment
   Seg nxt;                 // segment whose rows sit in qnext (valid while nxt.j >= 0)
   nxt.j = -1;
@@ -947,7 +987,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   auto rows_hi = [&](const Seg& sg, int Ls) {
     // tokens this wave may read in the segment: up to the end of its slice or the sequence
     const int last = sg.end < x1 ? sg.end : x1;
-    const int hi_t = (last - sg.start) * kBlockTokens;
+    const int hi_t = (last - sg.start + sg.fb) * kBlockTokens;
     return hi_t < Ls ? hi_t : Ls;
   };
   auto finish = [&]() {
@@ -966,7 +1006,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
         nxt = sg;
         const int Ls = clamp_len(a.seq_lens[sg.b], a.max_blocks);
         lim_min_next = load_rows<KV, D, NT>(a, sg.b, sg.g, sg.rg, Ls, rows_hi(sg, Ls), qnext,
-                                            lim_next, row16, grp);
+                                            lim_next, lo_next, lo_max_next, row16, grp);
         if constexpr (APP) {
           const int64_t nrow = ((int64_t)sg.b * a.num_kv_heads + sg.g) * D * KV::kElem;
           KV::load_new(tok_next, static_cast<const uint8_t*>(a.k_new) + nrow,
@@ -992,14 +1032,17 @@ void paged_attn_balanced_kernel(AttnArgs a) {
         for (int nt = 0; nt < NT; ++nt) {
           qop[nt] = qnext[nt];
           lim[nt] = lim_next[nt];
+          lo_row[nt] = lo_next[nt];
         }
         lim_min = lim_min_next;
+        lo_max = lo_max_next;
         if constexpr (APP) tok = tok_next;
         nxt.j = -1;
       } else {
         // (rare: two segments began within the blocks in flight) load the rows now and
         // wait for them here, so that no later wait has to allow for a pending query load
-        lim_min = load_rows<KV, D, NT>(a, cur.b, cur.g, cur.rg, L, hi, qop, lim, row16, grp);
+        lim_min = load_rows<KV, D, NT>(a, cur.b, cur.g, cur.rg, L, hi, qop, lim, lo_row, lo_max,
+                                       row16, grp);
         if constexpr (APP) {
           const int64_t nrow = ((int64_t)cur.b * a.num_kv_heads + cur.g) * D * KV::kElem;
           KV::load_new(tok, static_cast<const uint8_t*>(a.k_new) + nrow,
@@ -1015,13 +1058,13 @@ void paged_attn_balanced_kernel(AttnArgs a) {
       st.reset(vref);
     }
     if (sl.tile < 0) return;
-    const int tok0 = (x - cur.start) * kBlockTokens;
+    const int tok0 = (x - cur.start + cur.fb) * kBlockTokens;
     const bool new_tok = APP && tok0 + kBlockTokens >= L;  // the tile holding token L - 1
     const int off = L - 1 - tok0;
     if constexpr (APP) {
       if (new_tok) KV::patch(kk, vv, tok, off, row16, grp);
     }
-    st.update(qop, lim, lim_min, rows_hi(cur, L), kk, vv, tok0,
+    st.update(qop, lim, lim_min, lo_row, lo_max, rows_hi(cur, L), kk, vv, tok0,
               a.scale_log2 * (kInt8 ? sl.ks : 1.f), sl.vs, grp);
     if constexpr (APP) {
       if (new_tok && cur.rg == 0) {  // keep the token for the store at the end

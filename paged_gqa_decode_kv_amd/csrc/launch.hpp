@@ -25,6 +25,7 @@ struct AttnArgs {
   int32_t max_parts;        // split: partitions per row in the workspace; direct: 1
   int32_t split;            // 0: direct, 1: write partials
   float scale_log2;         // sm_scale * log2(e)
+  int32_t window;           // sliding window in tokens (0 = none)
   // balanced mode
   int32_t num_workgroups;   // workgroups launched
   int32_t num_workers;      // waves the flat block list is dealt to (workgroups * waves)

@@ -29,7 +29,8 @@ def dims_of(P, wl, dv=None):
     c = wl.cfg
     return P.make_dims(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
                        wl.block_tables.shape[1], wl.k_cache.shape[0], c.q_dtype, c.kv_dtype,
-                       kv_tile_stride=0 if dv is None else dv.stride)
+                       kv_tile_stride=0 if dv is None else dv.stride,
+                       sliding_window=c.sliding_window)
 
 
 class Dev:
@@ -146,7 +147,8 @@ def oracle_attention(wl, kc, vc, seq_lens=None, pairs=None):
     lens = wl.seq_lens.numpy() if seq_lens is None else np.asarray(seq_lens)
     return attention.paged_attention(raw(wl.q), c.q_dtype, kc, vc, c.kv_dtype,
                                      wl.block_tables.numpy(), lens, float(np.float32(wl.sm_scale)),
-                                     c.num_q_pos, raw(wl.k_scale), raw(wl.v_scale), pairs=pairs)
+                                     c.num_q_pos, raw(wl.k_scale), raw(wl.v_scale), pairs=pairs,
+                                     window=c.sliding_window)
 
 
 def max_err(gpu_out, ref, pairs=None, group=None):

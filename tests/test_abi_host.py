@@ -60,6 +60,7 @@ def _decode(d, q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, t=FAKE, lens=FAKE, out=
     (dict(num_kv_heads=0), -2),
     (dict(max_blocks_per_seq=0), -2),
     (dict(num_blocks=0), -2),
+    (dict(sliding_window=-1), -2),
     (dict(q_dtype="f32", kv_dtype="bf16"), -3),
     (dict(q_dtype="bf16", kv_dtype="f32"), -3),
 ])

@@ -351,6 +351,84 @@ def test_balanced_workspace_errors(P):
     assert e.value.status == -8
 
 
+# ---- sliding window ------------------------------------------------------------------
+def _poison_before_window(wl):
+    """NaN every block wholly before the window of its sequence's first row (such blocks
+    belong to that sequence only in these workloads): a kernel that reads one shows it."""
+    from dataclasses import replace
+    c = wl.cfg
+    kc, vc = wl.k_cache.clone(), wl.v_cache.clone()
+    ks = None if wl.k_scale is None else wl.k_scale.clone()
+    vs = None if wl.v_scale is None else wl.v_scale.clone()
+    n = 0
+    for b, L in enumerate(wl.seq_lens.tolist()):
+        lo = max(0, L - c.num_q_pos + 1 - c.sliding_window)
+        for j in range(lo // 16):
+            blk = int(wl.block_tables[b, j])
+            if ks is not None:
+                ks[blk] = float("nan")
+                vs[blk] = float("nan")
+            else:
+                kc[blk] = float("nan")
+                vc[blk] = float("nan")
+            n += 1
+    return replace(wl, k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs), n
+
+
+WINDOW_DECODE = [
+    ("tiny_fp32", dict(batch=5, length_range=(1, 520), sliding_window=1)),
+    ("tiny_fp32", dict(batch=5, length_range=(1, 520), sliding_window=100)),
+    ("llama3_8b", dict(batch=7, length_range=(1, 600), sliding_window=16)),
+    ("llama3_8b", dict(batch=7, length_range=(1, 600), sliding_window=37)),
+    ("llama3_8b", dict(batch=6, length_range=(1, 900), sliding_window=256, num_q_heads=64,
+                       num_kv_heads=1)),
+    ("mistral_7b_window", dict(batch=5, length_range=(1, 1200), sliding_window=300)),
+]
+
+
+@pytest.mark.parametrize("mode", ["direct", "split", "balanced", "step"])
+@pytest.mark.parametrize("name,kw", WINDOW_DECODE)
+def test_sliding_window_decode(P, name, kw, mode):
+    wl, npois = _poison_before_window(_small(name, **kw))
+    say(f"[case] window {kw['sliding_window']} {mode} blocks poisoned {npois}")
+    if mode == "direct":
+        _check_attention(P, wl)
+    elif mode == "split":
+        _check_attention(P, wl, split=(64, 40))
+        _check_attention(P, wl, split=(16, 200), interleave=True)
+    elif mode == "balanced":
+        _check_attention(P, wl, balanced=0)
+        _check_attention(P, wl, balanced=5, interleave=True)
+    else:
+        _check_decode_step(P, wl, 0)
+        _check_decode_step(P, wl, 3, interleave=True)
+
+
+@pytest.mark.parametrize("mode", ["direct", "balanced"])
+@pytest.mark.parametrize("name,kw", [
+    ("verify_int8", dict(batch=5, length_range=(1, 500), sliding_window=20)),
+    ("verify_int8", dict(batch=5, length_range=(1, 500), sliding_window=3)),
+    ("verify_int8", dict(batch=4, length_range=(1, 400), sliding_window=64, kv_dtype="bf16")),
+])
+def test_sliding_window_verify(P, name, kw, mode):
+    wl, npois = _poison_before_window(_small(name, **kw))
+    say(f"[case] verify window {kw['sliding_window']} {mode} blocks poisoned {npois}")
+    if mode == "direct":
+        _check_attention(P, wl)
+    else:
+        _check_attention(P, wl, balanced=0)
+        _check_attention(P, wl, balanced=7, interleave=True)
+
+
+def test_sliding_window_full_mistral_7b(P):
+    """The benchmark's sliding-window workload at full size (64 sequences of U[2048, 16384]
+    tokens, window 4096) through the decode step, on sampled (sequence, KV head) pairs."""
+    wl = W.generate("mistral_7b_window")
+    rng = np.random.default_rng(11)
+    pairs = [(int(b), int(g)) for b, g in zip(rng.integers(0, 64, 12), rng.integers(0, 8, 12))]
+    _check_decode_step(P, wl, 0, interleave=True, pairs=pairs)
+
+
 # ---- decode step: the append folded into the balanced attention launch ----------------
 def _check_decode_step(P, wl, G=0, interleave=False, zero_lens=(), pairs=None):
     c = wl.cfg

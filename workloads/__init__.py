@@ -147,6 +147,7 @@ class Config:
     shared_prefix_tokens: int = 0
     peaked_fraction: float = 0.0      # fraction of K slots scaled by peaked_factor
     peaked_factor: float = 8.0
+    sliding_window: int = 0           # 0 = whole context; W = the W most recent tokens
     seed: int = 0
 
     @property
@@ -175,6 +176,10 @@ CONFIGS = {
     # speculative verify: 1 + 5 draft positions, causal, int8 KV, context U[1024, 8192]
     "verify_int8": Config("verify_int8", 32, 32, 8, 128, "bf16", "i8",
                           length_range=(1024, 8192), num_q_pos=6, append=False, seed=1004),
+    # sliding-window decode (Mistral-7B-shaped layer: 32q/8kv, d128, window 4096), batch
+    # 64, context U[2048, 16384] so that most sequences run past the window
+    "mistral_7b_window": Config("mistral_7b_window", 64, 32, 8, 128, "bf16", "bf16",
+                                length_range=(2048, 16384), sliding_window=4096, seed=1005),
 }
 
 
@@ -203,12 +208,23 @@ class Workload:
         each attended token's K and V once (plus the int8 scales of used blocks)."""
         c = self.cfg
         elem = {"f32": 4, "bf16": 2, "i8": 1}[c.kv_dtype]
-        toks = int(self.seq_lens.to(torch.int64).sum())
+        toks = sum(self.visible_range(int(L))[1] - self.visible_range(int(L))[0]
+                   for L in self.seq_lens.tolist())
         nbytes = toks * 2 * c.num_kv_heads * c.head_dim * elem
         if c.kv_dtype == "i8":
-            used = sum(-(-int(L) // BLOCK_SIZE) for L in self.seq_lens.tolist())
+            used = 0
+            for L in self.seq_lens.tolist():
+                lo, hi = self.visible_range(int(L))
+                used += -(-hi // BLOCK_SIZE) - lo // BLOCK_SIZE if hi > lo else 0
             nbytes += used * 2 * c.num_kv_heads * 4
         return nbytes
+
+    def visible_range(self, L):
+        """Tokens [lo, L) that some query row of a sequence of L tokens attends (all of
+        them, or with a sliding window of W the last W + nq - 1)."""
+        c = self.cfg
+        W = c.sliding_window
+        return (max(0, L - W - c.num_q_pos + 1) if W > 0 else 0), L
 
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
