@@ -385,6 +385,8 @@ struct Rows {
   // (lim_min is the smallest limit over the wave's rows, lo_max the largest start: a
   // sliding window's); tokens >= hi are past the sequence end and their V may be poisoned.  sc = softmax scale * log2(e) (times the block's K scale for int8);
   // vs = the block's V scale (int8).
+  // SW: a sliding window is in force (the lower bounds are tested at all).
+  template <bool SW>
   __device__ __forceinline__ void update(const typename KV::Q* qop, const int* lim, int lim_min,
                                          const int* lo, int lo_max, int hi,
                                          typename KV::K& kk, typename KV::V& vv,
@@ -405,8 +407,8 @@ struct Rows {
         vfac = 256.f;
       }
     }
-    const bool need_mask = tok0 + kBlockTokens > lim_min;
-    const bool need_lo = tok0 < lo_max;
+    // (one uniform test: blocks inside every row's range skip the per-token masks)
+    const bool need_mask = tok0 + kBlockTokens > lim_min || (SW && tok0 < lo_max);
     f32x4 pr[NT];
     float alpha[NT];
     const auto& km = KV::k_mat(kk);
@@ -416,8 +418,10 @@ struct Rows {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = sv[e] * sc;
-        if (need_mask && tok0 + 4 * grp + e >= lim[nt]) x = -INFINITY;
-        if (need_lo && tok0 + 4 * grp + e < lo[nt]) x = -INFINITY;
+        if (need_mask) {
+          const int t = tok0 + 4 * grp + e;
+          if (t >= lim[nt] || (SW && t < lo[nt])) x = -INFINITY;
+        }
         sv[e] = x;
       }
       float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
@@ -468,7 +472,7 @@ __device__ __forceinline__ int window_start(int lam, int window) {
 // Query rows of row tile rg for KV head g of sequence b: the MFMA B operand of each 16-row
 // tile and the visible range of this lane's row (tokens [lo, lim); lim capped at hi).
 // Returns the smallest limit over the tile's rows; lo_max receives the largest start.
-template <class KV, int D, int NT>
+template <class KV, int D, int NT, bool SW>
 __device__ __forceinline__ int load_rows(const AttnArgs& a, int b, int g, int rg, int L, int hi,
                                          typename KV::Q* qop, int* lim, int* lo, int& lo_max,
                                          int row16, int grp) {
@@ -484,14 +488,16 @@ __device__ __forceinline__ int load_rows(const AttnArgs& a, int b, int g, int rg
     int lam = valid ? L - a.num_q_pos + 1 + i : L;
     lam = lam < 0 ? 0 : lam;
     lim[nt] = lam < hi ? lam : hi;
-    lo[nt] = window_start(lam, a.window);
+    lo[nt] = SW ? window_start(lam, a.window) : 0;
   }
-  // the tile's last row has the largest start
-  int r_last = row_base + 16 * NT - 1;
-  r_last = r_last < a.rows ? r_last : a.rows - 1;
-  int lam_last = L - a.num_q_pos + 1 + r_last / a.group;
-  lam_last = lam_last < 0 ? 0 : lam_last;
-  lo_max = window_start(lam_last, a.window);
+  lo_max = 0;
+  if constexpr (SW) {  // the tile's last row has the largest start
+    int r_last = row_base + 16 * NT - 1;
+    r_last = r_last < a.rows ? r_last : a.rows - 1;
+    int lam_last = L - a.num_q_pos + 1 + r_last / a.group;
+    lam_last = lam_last < 0 ? 0 : lam_last;
+    lo_max = window_start(lam_last, a.window);
+  }
   const int i0 = row_base / a.group;
   int lam0 = L - a.num_q_pos + 1 + i0;
   lam0 = lam0 < 0 ? 0 : lam0;
@@ -538,9 +544,10 @@ __device__ __forceinline__ void write_rows(const AttnArgs& a, const Rows<KV, D, 
 // that sequence's tokens [lo, hi) (lo a multiple of 16).  The W waves of the workgroup
 // take interleaved blocks; their partial results are merged through LDS and wave 0
 // writes the normalised rows (and, except in direct mode, their log-sum-exp).
-// `slot` is the partition index (split mode).  Every wave of the workgroup must call this
-// together (it contains barriers).
-template <class KV, int D, int NT, int W, int NBUF>
+// `slot` is the partition index (split mode).  SW: a sliding window is in force (each row
+// also has a first visible token).  Every wave of the workgroup must call this together
+// (it contains barriers).
+template <class KV, int D, int NT, int W, int NBUF, bool SW>
 __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int b, int g, int rg,
                                             int L, int lo, int hi, int64_t slot) {
   constexpr int ND = D / 16;
@@ -558,8 +565,8 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
 
   typename KV::Q qop[NT];
   int lim[NT], lo_row[NT], lo_max;
-  const int lim_min = load_rows<KV, D, NT>(a, b, g, rg, L, hi, qop, lim, lo_row, lo_max, row16,
-                                           grp);
+  const int lim_min = load_rows<KV, D, NT, SW>(a, b, g, rg, L, hi, qop, lim, lo_row, lo_max,
+                                               row16, grp);
 
   const int64_t tile_bytes = a.tile_stride;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache);
@@ -635,7 +642,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, const Slot& sl) {
     if (sl.ph < 0) return;
     const int tok0 = (jb + w + W * kidx) * kBlockTokens;
-    st.update(qop, lim, lim_min, lo_row, lo_max, hi, kk, vv, tok0,
+    st.template update<SW>(qop, lim, lim_min, lo_row, lo_max, hi, kk, vv, tok0,
               a.scale_log2 * (kInt8 ? sl.ks : 1.f), sl.vs, grp);
   };
 
@@ -727,7 +734,7 @@ template <class KV, int NT> struct WavesPerEU {
 };
 
 // Direct and split modes: one unit per (KV head, sequence, row group, partition).
-template <class KV, int D, int NT, int W, int NBUF>
+template <class KV, int D, int NT, int W, int NBUF, bool SW>
 __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(WavesPerEU<KV, NT>::value)))
 void paged_attn_kernel(AttnArgs a) {
   const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
@@ -751,14 +758,14 @@ void paged_attn_kernel(AttnArgs a) {
   }
   // sliding window: no row of this sequence sees a block before the first row's window
   // (a partition wholly before it is left empty: zero rows, lse = -inf)
-  if (a.window > 0) {
+  if (SW) {
     int lam0 = L - a.num_q_pos + 1;
     lam0 = lam0 < 0 ? 0 : lam0;
     const int w0 = window_start(lam0, a.window) / kBlockTokens * kBlockTokens;
     lo = lo > w0 ? lo : w0;
     if (hi < lo) hi = lo;  // lo is a multiple of 16 here, so the unit reads no block
   }
-  attend_unit<KV, D, NT, W, NBUF>(a, a.split ? kSplit : kDirect, b, g, rg, L, lo, hi, p);
+  attend_unit<KV, D, NT, W, NBUF, SW>(a, a.split ? kSplit : kDirect, b, g, rg, L, lo, hi, p);
 }
 
 // Balanced mode.  All (segment, block) pairs of the batch are laid out in one flat list --
@@ -779,6 +786,10 @@ void paged_attn_kernel(AttnArgs a) {
 // are fetched together with the segment's query rows.  The slot itself is written at the
 // end of the wave's slice (row group 0 only), from a copy kept in LDS: stores into the
 // cache while the wave still streams cost ~5% (measured on MI355X), at the end ~0.4%.
+//
+// SW (sliding window): each sequence's list starts at the block that holds its first
+// row's first visible token, so the blocks before the window are never dealt out.  The
+// window is a separate instantiation because its bookkeeping cost 1-2% when compiled in.
 // s_waitcnt immediate for vmcnt(0) with the other counters left open (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmem0 = 0x0F70;
@@ -795,14 +806,14 @@ template <class KV, int NT> struct BalancedWavesPerEU {
                                    : PA_BAL_WAVES_PER_EU;
 };
 
-template <class KV, int D, int NT, int W, int NBUF, bool APP>
+template <class KV, int D, int NT, int W, int NBUF, bool APP, bool SW>
 __global__ __launch_bounds__(kWave* W)
 __attribute__((amdgpu_waves_per_eu(BalancedWavesPerEU<KV, NT>::value)))
 void paged_attn_balanced_kernel(AttnArgs a) {
   constexpr bool kInt8 = IsInt8<KV>::value;
   constexpr int kStage = 64;
   __shared__ int s_pref[kMaxBalancedSeqs + 1];
-  __shared__ int s_fb[kMaxBalancedSeqs];  // first block a row of the sequence may see
+  __shared__ int s_fb[SW ? kMaxBalancedSeqs : 1];  // first block a row of the sequence may see
   const int64_t wid = xcd_logical_id();
   if (wid >= a.num_workgroups) return;
   const int lane = threadIdx.x & (kWave - 1);
@@ -824,8 +835,11 @@ void paged_attn_balanced_kernel(AttnArgs a) {
       const int Lb = clamp_len(a.seq_lens[bb], a.max_blocks);
       int lam0 = Lb - a.num_q_pos + 1;
       lam0 = lam0 < 0 ? 0 : lam0;
-      const int fb = window_start(lam0, a.window) / kBlockTokens;
-      s_fb[bb] = fb;
+      int fb = 0;
+      if constexpr (SW) {
+        fb = window_start(lam0, a.window) / kBlockTokens;
+        s_fb[bb] = fb;
+      }
       nb = (Lb + kBlockTokens - 1) / kBlockTokens - fb;
     }
     s_scan[threadIdx.x] = nb;
@@ -877,7 +891,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     sg.j = gr * B + lo_b;
     sg.start = gr * T + __builtin_amdgcn_readfirstlane(s_pref[lo_b]);
     sg.end = gr * T + __builtin_amdgcn_readfirstlane(s_pref[lo_b + 1]);
-    sg.fb = __builtin_amdgcn_readfirstlane(s_fb[lo_b]);
+    sg.fb = SW ? __builtin_amdgcn_readfirstlane(s_fb[lo_b]) : 0;
     return sg;
   };
 
@@ -904,7 +918,8 @@ void paged_attn_balanced_kernel(AttnArgs a) {
         if (s_pref[mid] <= r) lo_b = mid; else hi_b = mid - 1;
       }
       const int g = gr / nrg;
-      const int ph = a.block_tables[(int64_t)lo_b * a.max_blocks + (r - s_pref[lo_b]) + s_fb[lo_b]];
+      const int ph = a.block_tables[(int64_t)lo_b * a.max_blocks + (r - s_pref[lo_b]) +
+                                    (SW ? s_fb[lo_b] : 0)];
       if (ph >= 0 && (int64_t)ph < a.num_blocks) {
         tile = (int)kv_tile(ph, g, a.num_kv_heads);
         if constexpr (kInt8) {
@@ -1005,7 +1020,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
       if (nxt.j < 0) {
         nxt = sg;
         const int Ls = clamp_len(a.seq_lens[sg.b], a.max_blocks);
-        lim_min_next = load_rows<KV, D, NT>(a, sg.b, sg.g, sg.rg, Ls, rows_hi(sg, Ls), qnext,
+        lim_min_next = load_rows<KV, D, NT, SW>(a, sg.b, sg.g, sg.rg, Ls, rows_hi(sg, Ls), qnext,
                                             lim_next, lo_next, lo_max_next, row16, grp);
         if constexpr (APP) {
           const int64_t nrow = ((int64_t)sg.b * a.num_kv_heads + sg.g) * D * KV::kElem;
@@ -1041,8 +1056,8 @@ void paged_attn_balanced_kernel(AttnArgs a) {
       } else {
         // (rare: two segments began within the blocks in flight) load the rows now and
         // wait for them here, so that no later wait has to allow for a pending query load
-        lim_min = load_rows<KV, D, NT>(a, cur.b, cur.g, cur.rg, L, hi, qop, lim, lo_row, lo_max,
-                                       row16, grp);
+        lim_min = load_rows<KV, D, NT, SW>(a, cur.b, cur.g, cur.rg, L, hi, qop, lim, lo_row,
+                                           lo_max, row16, grp);
         if constexpr (APP) {
           const int64_t nrow = ((int64_t)cur.b * a.num_kv_heads + cur.g) * D * KV::kElem;
           KV::load_new(tok, static_cast<const uint8_t*>(a.k_new) + nrow,
@@ -1064,7 +1079,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     if constexpr (APP) {
       if (new_tok) KV::patch(kk, vv, tok, off, row16, grp);
     }
-    st.update(qop, lim, lim_min, lo_row, lo_max, rows_hi(cur, L), kk, vv, tok0,
+    st.template update<SW>(qop, lim, lim_min, lo_row, lo_max, rows_hi(cur, L), kk, vv, tok0,
               a.scale_log2 * (kInt8 ? sl.ks : 1.f), sl.vs, grp);
     if constexpr (APP) {
       if (new_tok && cur.rg == 0) {  // keep the token for the store at the end
@@ -1110,16 +1125,24 @@ int launch_one(const AttnArgs& a, void* stream) {
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg * a.max_parts;
   const int64_t grid = (units + 7) / 8 * 8;
   if (grid > 0x7fffffff) return PA_ERR_DIMS;
-  hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF>), dim3((unsigned)grid), dim3(kWave * W), 0,
-                     static_cast<hipStream_t>(stream), a);
+  if (a.window > 0)
+    hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, true>), dim3((unsigned)grid),
+                       dim3(kWave * W), 0, static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, false>), dim3((unsigned)grid),
+                       dim3(kWave * W), 0, static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 template <class KV, int D, int NT, int W, int NBUF, bool APP>
 int launch_balanced_one(const AttnArgs& a, void* stream) {
   const int64_t grid = ((int64_t)a.num_workgroups + 7) / 8 * 8;
-  hipLaunchKernelGGL((paged_attn_balanced_kernel<KV, D, NT, W, NBUF, APP>), dim3((unsigned)grid),
-                     dim3(kWave * W), 0, static_cast<hipStream_t>(stream), a);
+  if (a.window > 0)
+    hipLaunchKernelGGL((paged_attn_balanced_kernel<KV, D, NT, W, NBUF, APP, true>),
+                       dim3((unsigned)grid), dim3(kWave * W), 0, static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL((paged_attn_balanced_kernel<KV, D, NT, W, NBUF, APP, false>),
+                       dim3((unsigned)grid), dim3(kWave * W), 0, static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -1131,7 +1154,7 @@ int occupancy_one() {
     return PA_ERR_LAUNCH;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &per_cu,
-          reinterpret_cast<const void*>(&paged_attn_balanced_kernel<KV, D, NT, W, NBUF, false>),
+          reinterpret_cast<const void*>(&paged_attn_balanced_kernel<KV, D, NT, W, NBUF, false, false>),
           kWave * W, 0) != hipSuccess)
     return PA_ERR_LAUNCH;
   // Measured on MI355X (Llama-3-8B decode, shared-prefix and 128K bf16 workloads; int8
