@@ -23,10 +23,11 @@ Modules
 ``paging``     block-table translation, de-paging, slot-mapped append, gather.
 ``attention``  attention over the de-paged cache, verify rows, partitions and the
                log-sum-exp merge.
+``quant``      the int8 encoding of a block and the quantising append.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, brute force, a library routine or numbers printed on the
 pages.  None is "parity unpinned".
 """
 
-from . import attention, kvsize, paging, storage  # noqa: F401
+from . import attention, kvsize, paging, quant, storage  # noqa: F401

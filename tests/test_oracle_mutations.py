@@ -68,6 +68,17 @@ MUTATIONS = [
     ("window start ignored", "oracle/attention.py",
      "lo = 0 if starts is None else max(0, int(starts[r]))", "lo = 0",
      "test_oracle_attention.py"),
+    ("int8 scale over 128", "oracle/quant.py", "scale = np.float32(amax / np.float32(QMAX))",
+     "scale = np.float32(amax / np.float32(128))", "test_oracle_quant.py"),
+    ("int8 rounding toward zero", "oracle/quant.py", "q = np.rint(x / scale)",
+     "q = np.trunc(x / scale)", "test_oracle_quant.py"),
+    ("append re-encodes only the new token", "oracle/quant.py", "for t in range(off + 1):",
+     "for t in range(off, off + 1):", "test_oracle_quant.py"),
+    ("staging row ignored", "oracle/quant.py", "row = int(stage_rows[i])", "row = 0",
+     "test_oracle_quant.py"),
+    ("V encoded from the K staging", "oracle/quant.py",
+     "vx = storage.bf16_bits_to_f64(vst[row, g, :off + 1])",
+     "vx = storage.bf16_bits_to_f64(kst[row, g, :off + 1])", "test_oracle_quant.py"),
     ("copy direction swapped", "oracle/paging.py", "kc[dst] = k_cache[src]",
      "kc[src] = k_cache[dst]", "test_oracle_paging.py"),
     ("copy skips V", "oracle/paging.py", "vc[dst] = v_cache[src]", "pass",
