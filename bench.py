@@ -219,6 +219,49 @@ def copy_blocks_bench(P, torch, W, steps):
     return res
 
 
+def append_quant_bench(P, torch, W, steps):
+    """kv_append_quant for one decode step of a Llama-3-8B-shaped int8 cache: 64 new tokens
+    (one per sequence, at the end of each sequence of the seeded Llama-3-8B lengths) into
+    8 KV heads, each re-encoding its open block from a bf16 staging row.  Bytes per (token,
+    head) = staged tokens read + new token read + staged token written + the block's live
+    codes written (K and V) + the two scales; launches back to back between two events."""
+    wl = W.generate(W.scaled("llama3_8b", kv_dtype="i8", append=False), poison=False,
+                    spare_blocks=64)
+    c = wl.cfg
+    dev = torch.device("cuda:0")
+    nb, h = wl.k_cache.shape[:2]
+    d = c.head_dim
+    kc, vc = wl.k_cache.to(dev), wl.v_cache.to(dev)
+    ks, vs = wl.k_scale.to(dev), wl.v_scale.to(dev)
+    alloc = wl.meta["allocator"]
+    slots = torch.tensor([alloc.append_token(b)[0] for b in range(c.batch)], dtype=torch.int64)
+    gen = torch.Generator().manual_seed(7)
+    kn = torch.randn((c.batch, h, d), generator=gen).to(torch.bfloat16).to(dev)
+    vn = torch.randn((c.batch, h, d), generator=gen).to(torch.bfloat16).to(dev)
+    kst = torch.randn((c.batch, h, 16, d), generator=gen).to(torch.bfloat16).to(dev)
+    vst = torch.randn((c.batch, h, 16, d), generator=gen).to(torch.bfloat16).to(dev)
+    rows = torch.arange(c.batch, dtype=torch.int32, device=dev)
+    sl = slots.to(dev)
+    dims = P.make_dims(c.batch, c.num_q_heads, h, d, wl.block_tables.shape[1], nb, "bf16", "i8")
+    for _ in range(3):
+        P.kv_append_quant(dims, kn, vn, sl, rows, c.batch, kst, vst, kc, vc, ks, vs)
+    torch.cuda.synchronize()
+    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    e0.record()
+    for _ in range(steps):
+        P.kv_append_quant(dims, kn, vn, sl, rows, c.batch, kst, vst, kc, vc, ks, vs)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    offs = (slots % 16).tolist()
+    nbytes = sum(h * (2 * (o * d * 2) + 2 * d * 2 + 2 * d * 2 + 2 * (o + 1) * d + 8)
+                 for o in offs)
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"tokens": c.batch, "kv_heads": h, "bytes": nbytes, "us_per_launch": round(us, 2),
+            "GBps": round(nbytes / us / 1e3, 1)}
+
+
 def summarize(wl, wall, steps, attn):
     kv = wl.kv_bytes()
     us_step = wall / steps * 1e6
@@ -391,11 +434,14 @@ def trace_summary(args, trace_dir):
     # the attention kernels start a new workload whenever their instantiation changes or
     # a run of calls ends with a copy (the next workload's uploads)
     groups, cur, last = [], None, None
-    copies = []
+    copies, quants = [], []
     for n, s0, e in rows:
         k = short(n)
         if "kv_copy_blocks" in k:
             copies.append((e - s0) / 1000)
+            continue
+        if "kv_append_quant" in k:
+            quants.append((e - s0) / 1000)
             continue
         if "copyBuffer" in k or "elementwise" in k or "fill" in k.lower():
             last = "copy"
@@ -428,6 +474,10 @@ def trace_summary(args, trace_dir):
             if v:
                 lines.append(f"| llama3_8b pool | `{label}` | {len(v)} | {np.mean(v):.2f} | "
                              f"{np.median(v):.2f} |")
+    if quants:
+        v = quants[3:]      # 3 warm-up launches
+        lines.append(f"| llama3_8b int8 cache | `kv_append_quant` 64 tokens x 8 heads | {len(v)} | "
+                     f"{np.mean(v):.2f} | {np.median(v):.2f} |")
     out = os.path.join(ROOT, "profiles", f"{args.path}_{args.layout}_kernel_trace.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -481,6 +531,7 @@ def main():
             torch.cuda.empty_cache()
 
         others["kv_copy_blocks"] = copy_blocks_bench(P, torch, W, min(args.steps, 40))
+        others["kv_append_quant"] = append_quant_bench(P, torch, W, min(args.steps, 40))
 
     achieved = res["attn_kernel_GBps"]
     kernel = KERNEL_NAME[args.path]

@@ -193,6 +193,35 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
               void* k_out, void* v_out, void* stream);
 
 /*
+ * kv_append_quant -- append new tokens to an int8 cache (lecture 10's symmetric int8
+ * rule, zero point 0; in-depth guide section 5.2: per-head scales for KV caches).  A
+ * (block, KV head) keeps one fp32 scale = max|x| / 127 over its live tokens and codes
+ * round-half-even(x / scale) clamped to +-127 (all 0 when the scale is 0), the same
+ * encoding as a cache quantised whole.  Because the scale depends on every token of the
+ * block, the open block of each sequence is kept in bf16 in a staging row; token i is
+ * written to staging offset slot % 16 and the block's live tokens 0 .. slot % 16 are
+ * re-encoded from the staging row into the cache together with the new scale.  Once the
+ * block's 16th token is in, the block is final.
+ *   k_new, v_new   device bf16 [num_tokens][Hkv][head_dim]
+ *   slot_mapping   device int64 [num_tokens]; < 0 or outside the pool: token skipped
+ *   stage_rows     device int32 [num_tokens]: the staging row of the token's sequence;
+ *                  outside [0, num_stage_rows): token skipped
+ *   k_stage, v_stage device bf16 [num_stage_rows][Hkv][16][head_dim] (token-major), read
+ *                  and written: offsets 0 .. slot % 16 - 1 of the row must hold the
+ *                  block's earlier tokens (written by earlier calls, or by the caller
+ *                  after filling a block some other way)
+ *   k_cache, v_cache device int8, written (offsets after slot % 16 are left as they are)
+ *   k_scale, v_scale device fp32 [num_blocks][Hkv], written
+ * dims->kv_dtype must be PA_I8 (else PA_ERR_DTYPE).  No two tokens of one call may share
+ * a block or a staging row (they would race); a decode step appends one token per
+ * sequence.  New tokens, staging rows and caches must be 16-byte aligned (PA_ERR_ALIGN).
+ */
+int kv_append_quant(const pa_dims* dims, const void* k_new, const void* v_new,
+                    const int64_t* slot_mapping, const int32_t* stage_rows, int32_t num_tokens,
+                    int32_t num_stage_rows, void* k_stage, void* v_stage, void* k_cache,
+                    void* v_cache, float* k_scale, float* v_scale, void* stream);
+
+/*
  * kv_copy_blocks -- copy whole physical blocks: for each pair (src, dst), every KV head's K
  * and V of block src (and, for int8, its k_scale / v_scale) is copied to block dst, bit
  * for bit.  This is the copy-on-write step of block sharing (tutorial section 7: shared

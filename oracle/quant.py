@@ -51,7 +51,8 @@ def append_quant(k_cache, v_cache, k_scale, v_scale, k_stage, v_stage, k_new, v_
 
     Caches: int8 in the project format (k [NB, Hkv, d/16, 16, 16], v [NB, Hkv, d, 16]);
     scales [NB, Hkv] fp32; staging [S, Hkv, 16, d] bf16 bit patterns.  A slot < 0 or
-    outside the pool writes nothing.  Tokens are taken in order; no two tokens of one call
+    outside the pool, or a staging row outside [0, S), writes nothing.  Tokens are taken
+    in order; no two tokens of one call
     may fall into the same block (each one re-encodes the block from its staging row).
     """
     kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
@@ -64,6 +65,8 @@ def append_quant(k_cache, v_cache, k_scale, v_scale, k_stage, v_stage, k_new, v_
             continue
         blk, off = divmod(int(s), block_size)
         row = int(stage_rows[i])
+        if row < 0 or row >= kst.shape[0]:
+            continue
         for g in range(hkv):
             kst[row, g, off] = k_new[i, g]
             vst[row, g, off] = v_new[i, g]

@@ -224,6 +224,27 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
                            elem_bytes(dims->kv_dtype), k_out, v_out, stream);
 }
 
+int kv_append_quant(const pa_dims* dims, const void* k_new, const void* v_new,
+                    const int64_t* slot_mapping, const int32_t* stage_rows, int32_t num_tokens,
+                    int32_t num_stage_rows, void* k_stage, void* v_stage, void* k_cache,
+                    void* v_cache, float* k_scale, float* v_scale, void* stream) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->kv_dtype != PA_I8) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_stage_rows < 0) return PA_ERR_DIMS;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !stage_rows || !k_stage || !v_stage || !k_cache ||
+      !v_cache || !k_scale || !v_scale)
+    return PA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_stage) || !aligned16(v_stage) ||
+      !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_ALIGN;
+  return pa::launch_append_quant(k_new, v_new, slot_mapping, stage_rows, num_tokens,
+                                 num_stage_rows, dims->num_kv_heads, dims->head_dim,
+                                 dims->num_blocks, tile_stride(dims), k_stage, v_stage, k_cache,
+                                 v_cache, k_scale, v_scale, stream);
+}
+
 int kv_copy_blocks(const pa_dims* dims, const int32_t* block_pairs, int32_t num_pairs,
                    void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                    void* stream) {

@@ -11,6 +11,12 @@
 // tile addressing the attention kernels use, so its output checks that translation
 // bit for bit.
 //
+// Quantising append into an int8 cache (lecture 10 symmetric int8 rule; in-depth guide
+// section 5.2 per-head scales): a block's scale is max|x| / 127 over its live tokens, so
+// the sequence's open block is kept in bf16 in a staging row and re-encoded from it
+// whenever a token arrives.  One workgroup per (token, KV head), 2 * head_dim threads:
+// thread j owns token j / (d / 8) of the block and 8 dims of it.
+//
 // Block copy (copy-on-write of shared blocks, tutorial section 7): for each (src, dst)
 // pair every KV head's K and V tile of block src is copied to block dst (and the int8
 // scales).  Each thread moves one 16-byte piece of one pair.
@@ -132,7 +138,119 @@ __global__ __launch_bounds__(256) void kv_copy_blocks_kernel(
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(2 * D) void kv_append_quant_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int64_t* __restrict__ slot_mapping, const int32_t* __restrict__ stage_rows,
+    int32_t num_kv_heads, int64_t num_blocks, int32_t num_stage_rows, int64_t tile_stride,
+    uint16_t* __restrict__ k_stage, uint16_t* __restrict__ v_stage, int8_t* __restrict__ k_cache,
+    int8_t* __restrict__ v_cache, float* __restrict__ k_scale, float* __restrict__ v_scale) {
+  constexpr int TPT = D / 8;  // threads per token
+  constexpr int NW = 2 * D / kWave;
+  const int64_t i = blockIdx.x / num_kv_heads;
+  const int g = (int)(blockIdx.x % num_kv_heads);
+  const int64_t slot = slot_mapping[i];
+  const int row = stage_rows[i];
+  if (slot < 0 || slot >= num_blocks * kBlockTokens || row < 0 || row >= num_stage_rows) return;
+  const int64_t blk = slot / kBlockTokens;
+  const int off = (int)(slot % kBlockTokens);
+  const int t = threadIdx.x / TPT;
+  const int k0 = (threadIdx.x % TPT) * 8;
+  const int64_t srow = (((int64_t)row * num_kv_heads + g) * kBlockTokens + t) * D + k0;
+  const int64_t nrow = ((int64_t)i * num_kv_heads + g) * D + k0;
+
+  // this thread's 8 dims of token t: from the staging row, or the new token itself
+  u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+  if (t < off) {
+    kw = *reinterpret_cast<const u32x4*>(k_stage + srow);
+    vw = *reinterpret_cast<const u32x4*>(v_stage + srow);
+  } else if (t == off) {
+    kw = *reinterpret_cast<const u32x4*>(k_new + nrow);
+    vw = *reinterpret_cast<const u32x4*>(v_new + nrow);
+    *reinterpret_cast<u32x4*>(k_stage + srow) = kw;
+    *reinterpret_cast<u32x4*>(v_stage + srow) = vw;
+  }
+  float kx[8], vx[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    kx[2 * e] = bf16_bits_to_f32(kw[e] & 0xffffu);
+    kx[2 * e + 1] = bf16_bits_to_f32(kw[e] >> 16);
+    vx[2 * e] = bf16_bits_to_f32(vw[e] & 0xffffu);
+    vx[2 * e + 1] = bf16_bits_to_f32(vw[e] >> 16);
+  }
+  // max |x| over the live tokens (tokens after `off` hold zeros here)
+  float km = 0.f, vm = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    km = fmaxf(km, fabsf(kx[e]));
+    vm = fmaxf(vm, fabsf(vx[e]));
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    km = fmaxf(km, __shfl_xor(km, o));
+    vm = fmaxf(vm, __shfl_xor(vm, o));
+  }
+  __shared__ float s_max[2][NW];
+  const int wv = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    s_max[0][wv] = km;
+    s_max[1][wv] = vm;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    km = fmaxf(km, s_max[0][w]);
+    vm = fmaxf(vm, s_max[1][w]);
+  }
+  const float ks = km / 127.f, vs = vm / 127.f;  // correctly rounded fp32 divisions
+  if (threadIdx.x == 0) {
+    k_scale[kv_tile(blk, g, num_kv_heads)] = ks;
+    v_scale[kv_tile(blk, g, num_kv_heads)] = vs;
+  }
+  if (t > off) return;
+  const int64_t tile = kv_tile(blk, g, num_kv_heads) * tile_stride;
+  // codes: round-half-even(x / scale) clamped to +-127, 0 for a zero scale
+  uint32_t kc[2] = {0u, 0u};
+  int8_t* vt = v_cache + tile;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float qk = ks > 0.f ? __builtin_rintf(kx[e] / ks) : 0.f;
+    float qv = vs > 0.f ? __builtin_rintf(vx[e] / vs) : 0.f;
+    qk = fminf(fmaxf(qk, -127.f), 127.f);
+    qv = fminf(fmaxf(qv, -127.f), 127.f);
+    kc[e / 4] |= ((uint32_t)(int32_t)qk & 0xffu) << (8 * (e % 4));
+    vt[v_elem(t, k0 + e)] = (int8_t)(int)qv;
+  }
+  // the 8 dims are contiguous inside one 16-byte K column
+  *reinterpret_cast<u32x2*>(k_cache + tile + k_elem<1>(t, k0)) = u32x2{kc[0], kc[1]};
+}
+
 }  // namespace
+
+int launch_append_quant(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                        const int32_t* stage_rows, int32_t num_tokens, int32_t num_stage_rows,
+                        int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                        int64_t tile_stride, void* k_stage, void* v_stage, void* k_cache,
+                        void* v_cache, float* k_scale, float* v_scale, void* stream) {
+  const int64_t grid = (int64_t)num_tokens * num_kv_heads;
+  if (grid > 0x7fffffff) return PA_ERR_DIMS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto k8 = static_cast<int8_t*>(k_cache);
+  auto v8 = static_cast<int8_t*>(v_cache);
+  auto kn = static_cast<const uint16_t*>(k_new);
+  auto vn = static_cast<const uint16_t*>(v_new);
+  auto kst = static_cast<uint16_t*>(k_stage);
+  auto vst = static_cast<uint16_t*>(v_stage);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(kv_append_quant_kernel<64>, dim3((unsigned)grid), dim3(128), 0, s, kn, vn,
+                       slot_mapping, stage_rows, num_kv_heads, num_blocks, num_stage_rows,
+                       tile_stride, kst, vst, k8, v8, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(kv_append_quant_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, kn, vn,
+                       slot_mapping, stage_rows, num_kv_heads, num_blocks, num_stage_rows,
+                       tile_stride, kst, vst, k8, v8, k_scale, v_scale);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
 
 int launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, int32_t num_kv_heads,
                        int32_t head_dim, int64_t num_blocks, int64_t tile_stride,

@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
               "lse_merge", "paged_attn_balanced", "paged_attn_balanced_merge",
               "paged_attn_balanced_workspace_bytes", "paged_attn_balanced_workgroups",
               "paged_split_workspace_bytes", "kv_gather", "paged_status_string",
-              "paged_decode_step", "kv_copy_blocks"]:
+              "paged_decode_step", "kv_copy_blocks", "kv_append_quant"]:
         assert n in names
 
 
@@ -174,3 +174,17 @@ def test_binding_raises_on_status():
     with pytest.raises(P.PagedAttnError) as e:
         P.paged_decode_attn(d, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 0.1, FAKE)
     assert e.value.status == -4
+
+
+def test_append_quant_checks():
+    f = ctypes.c_void_p(FAKE)
+    d = _dims(kv_dtype="i8")
+    args = lambda n, rows=4, **kw: [kw.get(k, f) for k in ("kn", "vn", "sm", "sr")] + \
+        [n, rows] + [kw.get(k, f) for k in ("kst", "vst", "kc", "vc", "ks", "vs")] + [None]
+    assert P.lib.kv_append_quant(ctypes.byref(d), *args(0)) == 0
+    assert P.lib.kv_append_quant(ctypes.byref(d), *args(-1)) == -2
+    assert P.lib.kv_append_quant(ctypes.byref(d), *args(2, rows=-1)) == -2
+    assert P.lib.kv_append_quant(ctypes.byref(d), *args(2, ks=None)) == -1
+    assert P.lib.kv_append_quant(ctypes.byref(d), *args(2, kst=ctypes.c_void_p(FAKE + 2))) == -9
+    db = _dims()
+    assert P.lib.kv_append_quant(ctypes.byref(db), *args(2)) == -3

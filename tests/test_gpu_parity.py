@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import workloads as W
-from oracle import attention, paging
+from oracle import attention, paging, quant
 from _helpers import (TOL, Dev, dims_of, gpu_append, gpu_attention, gpu_decode_step, max_err,
                       oracle_attention, oracle_caches, raw, say)
 
@@ -349,6 +349,129 @@ def test_balanced_workspace_errors(P):
     with pytest.raises(P.PagedAttnError) as e:
         P.paged_attn_balanced_merge(d, 1, 4, ws, out)
     assert e.value.status == -8
+
+
+# ---- quantising append into an int8 cache: bit exact --------------------------------------
+def _rand_bf16(gen, shape, scale=1.0):
+    return (torch.randn(shape, generator=gen) * scale).to(torch.bfloat16)
+
+
+def _interleave_i8(kc, vc):
+    nb, h = kc.shape[:2]
+    tile = kc[0, 0].numel()
+    comb = torch.empty((nb, h, 2, tile), dtype=torch.int8, device="cuda:0")
+    comb[:, :, 0] = kc.reshape(nb, h, tile).cuda()
+    comb[:, :, 1] = vc.reshape(nb, h, tile).cuda()
+    return comb, comb.data_ptr() + tile, 2 * tile
+
+
+@pytest.mark.parametrize("interleave", [False, True])
+@pytest.mark.parametrize("d,hkv", [(128, 8), (64, 2)])
+def test_kv_append_quant_bit_exact(P, d, hkv, interleave):
+    gen = torch.Generator().manual_seed(d + hkv + interleave)
+    nb, S, T = 40, 24, 20
+    kc = torch.randint(-127, 128, (nb, hkv, d // 16, 16, 16), generator=gen, dtype=torch.int8)
+    vc = torch.randint(-127, 128, (nb, hkv, d, 16), generator=gen, dtype=torch.int8)
+    ks = torch.rand((nb, hkv), generator=gen)
+    vs = torch.rand((nb, hkv), generator=gen)
+    kst = _rand_bf16(gen, (S, hkv, 16, d), 2.0)
+    vst = _rand_bf16(gen, (S, hkv, 16, d), 0.5)
+    kn = _rand_bf16(gen, (T, hkv, d), 3.0)
+    vn = _rand_bf16(gen, (T, hkv, d))
+    kn[3, 1 % hkv, 5] = 200.0                                   # a token that raises the scale
+    blocks = torch.randperm(nb, generator=gen)[:T]
+    offs = torch.randint(0, 16, (T,), generator=gen)
+    offs[:3] = torch.tensor([0, 15, 1])
+    slots = (blocks * 16 + offs).to(torch.int64)
+    rows = torch.randperm(S, generator=gen)[:T].to(torch.int32)
+    slots[4], slots[5], rows[6], rows[7] = -1, nb * 16, -1, S    # skipped tokens
+    say(f"[case] append_quant d={d} hkv={hkv} interleave={interleave}")
+    if interleave:
+        comb, vptr, stride = _interleave_i8(kc, vc)
+        gk, gv = comb, vptr
+    else:
+        gk, gv, stride = kc.cuda(), vc.cuda(), 0
+    dims = P.make_dims(1, hkv, hkv, d, 1, nb, "bf16", "i8", kv_tile_stride=stride)
+    dks, dvs, dkst, dvst = ks.cuda(), vs.cuda(), kst.cuda(), vst.cuda()
+    P.kv_append_quant(dims, kn.cuda(), vn.cuda(), slots.cuda(), rows.cuda(), T, dkst, dvst, gk, gv,
+                      dks, dvs)
+    torch.cuda.synchronize()
+    r = lambda x: x.view(torch.int16).numpy()
+    ok, ov, oks, ovs, okst, ovst = quant.append_quant(
+        kc.numpy(), vc.numpy(), ks.numpy(), vs.numpy(), r(kst), r(vst), r(kn), r(vn),
+        slots.numpy(), rows.numpy())
+    if interleave:
+        hk = comb[:, :, 0].reshape(kc.shape).cpu().numpy()
+        hv = comb[:, :, 1].reshape(vc.shape).cpu().numpy()
+    else:
+        hk, hv = gk.cpu().numpy(), gv.cpu().numpy()
+    assert np.array_equal(hk, ok) and np.array_equal(hv, ov)
+    assert np.array_equal(dks.cpu().numpy().view(np.uint32), oks.view(np.uint32))
+    assert np.array_equal(dvs.cpu().numpy().view(np.uint32), ovs.view(np.uint32))
+    assert np.array_equal(r(dkst.cpu()), okst) and np.array_equal(r(dvst.cpu()), ovst)
+
+
+@pytest.mark.parametrize("balanced", [None, 0])
+def test_int8_decode_steps_from_empty(P, balanced):
+    """Sequences grow token by token from nothing through kv_append_quant (block
+    boundaries crossed, scales growing), and decode attention reads the int8 cache after
+    every step; the oracle does the same steps with its own quantising append."""
+    gen = torch.Generator().manual_seed(21)
+    B, hq, hkv, d, steps = 5, 16, 4, 128, 37
+    start = [0, 3, 15, 16, 30]                      # the step at which each sequence begins
+    nb = 64
+    alloc = W.BlockAllocator(nb, 16, free_order=torch.randperm(nb, generator=gen).tolist())
+    for b in range(B):
+        alloc.allocate(b, 0)
+    kc = torch.zeros((nb, hkv, d // 16, 16, 16), dtype=torch.int8)
+    vc = torch.zeros((nb, hkv, d, 16), dtype=torch.int8)
+    ks, vs = torch.zeros((nb, hkv)), torch.zeros((nb, hkv))
+    kst = torch.zeros((B, hkv, 16, d), dtype=torch.bfloat16)
+    vst = torch.zeros_like(kst)
+    r = lambda x: x.view(torch.int16).numpy()
+    ora = [kc.numpy(), vc.numpy(), ks.numpy(), vs.numpy(), r(kst), r(vst)]
+    dev = [kc.cuda(), vc.cuda(), ks.cuda(), vs.cuda(), kst.cuda(), vst.cuda()]
+    rows = torch.arange(B, dtype=torch.int32)
+    say(f"[case] int8 decode steps from empty balanced={balanced}")
+    for step in range(steps + max(start)):
+        live = [b for b in range(B) if start[b] <= step < start[b] + steps]
+        slots = torch.full((B,), -1, dtype=torch.int64)
+        for b in live:
+            slots[b] = alloc.append_token(b)[0]
+        kn = _rand_bf16(gen, (B, hkv, d), 1.0 + step % 5)
+        vn = _rand_bf16(gen, (B, hkv, d))
+        dims = P.make_dims(B, hq, hkv, d, 8, nb, "bf16", "i8")
+        P.kv_append_quant(dims, kn.cuda(), vn.cuda(), slots.cuda(), rows.cuda(), B, dev[4], dev[5],
+                          dev[0], dev[1], dev[2], dev[3])
+        ora = list(quant.append_quant(*ora, r(kn), r(vn), slots.numpy(), rows.numpy()))
+        if step % 6 != 5:
+            continue
+        tables = torch.full((B, 8), -1, dtype=torch.int32)
+        for b in range(B):
+            t = alloc.block_tables[b]
+            tables[b, :len(t)] = torch.tensor(t, dtype=torch.int32)
+        lens = torch.tensor([alloc.token_counts[b] for b in range(B)], dtype=torch.int32)
+        q = _rand_bf16(gen, (B, 1, hq, d))
+        out = torch.full((B, 1, hq, d), float("nan"), device="cuda:0")
+        sm = float(np.float32(1 / np.sqrt(d)))
+        if balanced is None:
+            P.paged_decode_attn(dims, q.cuda(), dev[0], dev[1], dev[2], dev[3], tables.cuda(),
+                                lens.cuda(), sm, out)
+        else:
+            G = P.paged_attn_balanced_workgroups(dims, 1)
+            ws = torch.empty(P.paged_attn_balanced_workspace_bytes(dims, 1, G), dtype=torch.uint8,
+                             device="cuda:0")
+            P.paged_attn_balanced(dims, 1, q.cuda(), dev[0], dev[1], dev[2], dev[3], tables.cuda(),
+                                  lens.cuda(), sm, G, ws, out)
+            P.paged_attn_balanced_merge(dims, 1, G, ws, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(dev[0].cpu().numpy(), ora[0]) and np.array_equal(dev[1].cpu().numpy(), ora[1])
+        assert np.array_equal(dev[2].cpu().numpy(), ora[2]) and np.array_equal(dev[3].cpu().numpy(), ora[3])
+        ref, _ = attention.paged_attention(r(q), "bf16", ora[0], ora[1], "i8", tables.numpy(),
+                                           lens.numpy(), sm, 1, ora[2], ora[3])
+        err = max_err(out, ref)
+        say(f"  step {step} lens {lens.tolist()} max abs err {err:.3e}")
+        assert err <= TOL["i8"]
 
 
 # ---- sliding window ------------------------------------------------------------------

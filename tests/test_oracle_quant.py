@@ -88,6 +88,10 @@ def test_negative_and_out_of_pool_slots_write_nothing():
     out = quant.append_quant(*state, kb, kb, np.array([-1, nb * 16]), np.array([0, 1]))
     for a, b in zip(out, state):
         assert np.array_equal(a, b, equal_nan=True)
+    kb = _bf16_bits(np.ones((2, hkv, d)))
+    out = quant.append_quant(*state, kb, kb, np.array([3, 17]), np.array([-1, 2]))   # bad rows
+    for a, b in zip(out, state):
+        assert np.array_equal(a, b, equal_nan=True)
 
 
 def test_staging_rows_are_per_sequence():
