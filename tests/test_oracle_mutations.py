@@ -79,6 +79,16 @@ MUTATIONS = [
     ("V encoded from the K staging", "oracle/quant.py",
      "vx = storage.bf16_bits_to_f64(vst[row, g, :off + 1])",
      "vx = storage.bf16_bits_to_f64(kst[row, g, :off + 1])", "test_oracle_quant.py"),
+    ("fp8 exponent bias 8", "oracle/storage.py", "np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32))",
+     "np.ldexp(1.0 + m / 8.0, (e - 8).astype(np.int32))", "test_oracle_quant.py"),
+    ("fp8 subnormal exponent", "oracle/storage.py", "np.ldexp(m / 8.0, -6))",
+     "np.ldexp(m / 8.0, -7))", "test_oracle_quant.py"),
+    ("fp8 saturates to the NaN code", "oracle/quant.py", "            code = 0x7E\n",
+     "            code = 0x7F\n", "test_oracle_quant.py"),
+    ("fp8 scale over 480", "oracle/quant.py", "scale = np.float32(amax / np.float32(FP8_MAX))",
+     "scale = np.float32(amax / np.float32(480))", "test_oracle_quant.py"),
+    ("fp8 ties away from zero", "oracle/quant.py", "r = int(np.rint(a * 2.0 ** (3 - e)))",
+     "r = int(np.floor(a * 2.0 ** (3 - e) + 0.5))", "test_oracle_quant.py"),
     ("copy direction swapped", "oracle/paging.py", "kc[dst] = k_cache[src]",
      "kc[src] = k_cache[dst]", "test_oracle_paging.py"),
     ("copy skips V", "oracle/paging.py", "vc[dst] = v_cache[src]", "pass",

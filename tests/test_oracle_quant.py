@@ -108,3 +108,91 @@ def test_staging_rows_are_per_sequence():
     assert ks[1, 0] == np.float32(1.0) / np.float32(127) and ks[2, 0] == np.float32(100) / np.float32(127)
     assert (kc[1, 0, :, :2] == 127).all() and (kc[2, 0, :, 0] == 127).all()
     assert (kst[1, 0, 0] == b[0, 0]).all() and (kst[0, 0, 1] == a[0, 0]).all()
+
+
+# ---- fp8 e4m3 --------------------------------------------------------------------------
+def test_fp8_decode_matches_library_and_closed_forms():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = storage.fp8_e4m3_to_f64(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(lib))
+    assert np.array_equal(ours[~np.isnan(ours)], lib[~np.isnan(lib)])
+    assert ours[0x38] == 1.0 and ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
+    assert ours[0x08] == 2.0 ** -6 and ours[0x07] == 7 * 2.0 ** -9 and ours[0xC0] == -2.0
+    assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFF]) and not np.isnan(ours[0x79])
+    assert ours[0x80] == 0.0 and np.signbit(ours[0x80])
+
+
+def test_fp8_encode_rounding_and_saturation():
+    # exact values, ties to even, subnormal ties, saturation, signs
+    y = np.array([1.0, 448.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875, 460.0,
+                  1e6, -500.0, -1.0, 0.0, -0.0, 2.0 ** -6, 15 * 2.0 ** -10], np.float32)
+    want = [0x38, 0x7E, 0x01, 0x00, 0x02, 0x38, 0x3A, 0x7E, 0x7E, 0xFE, 0xB8, 0x00, 0x80,
+            0x08, 0x08]
+    assert quant.fp8_e4m3_encode(y).tolist() == want
+    # against the library's round-to-nearest-even conversion over the finite range,
+    # including every midpoint between neighbouring e4m3 values
+    rng = np.random.default_rng(4)
+    mags = np.exp2(rng.uniform(-12, np.log2(448), 4000)).astype(np.float32)
+    vals = storage.fp8_e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    y = np.concatenate([mags, -mags, mids, -mids, vals.astype(np.float32)])
+    lib = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(quant.fp8_e4m3_encode(y), lib)
+
+
+def test_fp8_quantise_invariants():
+    rng = np.random.default_rng(5)
+    for _ in range(10):
+        x = (rng.standard_normal((7, 32)) * rng.uniform(1e-3, 50)).astype(np.float32)
+        q, s = quant.quantise_fp8(x)
+        assert s == np.float32(np.abs(x).max() / np.float32(448))
+        assert np.abs(storage.fp8_e4m3_to_f64(q)).max() == 448.0
+        deq = storage.decode(q, "fp8", s)
+        # half a step of the e4m3 grid: 2^-4 relative (normal range), 2^-10 * scale below it
+        assert np.all(np.abs(deq - x) <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s) * 1.0001)
+
+
+def test_fp8_token_by_token_equals_the_generators_whole_block_encoding():
+    hkv, d, nb = 2, 32, 3
+    rng = np.random.default_rng(6)
+    toks = (rng.standard_normal((16, hkv, d)) * 2).astype(np.float32)
+    toks[9, 0, 3] = -30.0
+    kb = _bf16_bits(toks)
+    state = _empty_pool(nb, hkv, d, rows=1)
+    blk = 1
+    for t in range(16):
+        state = quant.append_quant(*state, kb[t:t + 1], kb[t:t + 1], np.array([blk * 16 + t]),
+                                   np.array([0]), kind="fp8")
+        kc, vc, ks, vs, _, _ = state
+        x = storage.bf16_bits_to_f64(kb).astype(np.float32)
+        pool = torch.zeros((nb, hkv, 16, d))
+        pool[blk] = torch.from_numpy(x).permute(1, 0, 2)
+        live = torch.zeros((nb, 16), dtype=torch.bool)
+        live[blk, :t + 1] = True
+        ref_q, ref_s = W._quantise_fp8(pool, live)
+        ref_k = W.encode_k(ref_q)
+        assert np.array_equal(kc[blk][:, :, :t + 1].view(np.uint8),
+                              ref_k[blk].numpy()[:, :, :t + 1]), t
+        assert ks[blk].tolist() == ref_s[blk].tolist(), t
+        assert np.array_equal(vc[blk][:, :, :t + 1].view(np.uint8),
+                              W.encode_v(ref_q)[blk].numpy()[:, :, :t + 1]), t
+
+
+def test_fp8_attention_reads_decoded_values_times_scales():
+    """paged attention over an fp8 cache equals attention over an fp32 cache holding
+    value(code) * scale (the decode definition, checked against the library above)."""
+    from oracle import attention
+    wl = W.generate(W.scaled("llama3_8b_fp8", batch=3, length_range=(1, 90), num_q_heads=4,
+                             num_kv_heads=2, head_dim=32), spare_blocks=2)
+    r = lambda x: x.view(torch.int16).numpy()
+    kc, vc = wl.k_cache.numpy(), wl.v_cache.numpy()
+    ks, vs = wl.k_scale.numpy(), wl.v_scale.numpy()
+    out, lse = attention.paged_attention(r(wl.q), "bf16", kc, vc, "fp8", wl.block_tables.numpy(),
+                                         wl.seq_lens.numpy(), 0.17, 1, ks, vs)
+    # (the products rounded to fp32: relative 2^-24, far inside the 1e-6 below)
+    kd = (storage.fp8_e4m3_to_f64(kc) * ks[:, :, None, None, None]).astype(np.float32)
+    vd = (storage.fp8_e4m3_to_f64(vc) * vs[:, :, None, None]).astype(np.float32)
+    out2, lse2 = attention.paged_attention(r(wl.q), "bf16", kd, vd, "f32", wl.block_tables.numpy(),
+                                           wl.seq_lens.numpy(), 0.17, 1)
+    assert np.allclose(out, out2, rtol=0, atol=1e-6) and np.allclose(lse, lse2, rtol=0, atol=1e-6)

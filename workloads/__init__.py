@@ -10,7 +10,8 @@ Cache format (the library's, see include/paged_attn.h):
     v_cache [num_blocks, num_kv_heads, head_dim, 16]
 The generator works on token-major [num_blocks, num_kv_heads, 16, head_dim] arrays and
 encodes them into that format as its last step (``encode_k`` / ``encode_v``).
-    k_scale, v_scale [num_blocks, num_kv_heads] fp32 (int8 caches only)
+    k_scale, v_scale [num_blocks, num_kv_heads] fp32 (int8 and fp8 caches; fp8 codes are
+    stored as uint8 bytes)
     block_tables [B, max_blocks] int32 (unused entries = -1)
     seq_lens [B] int32, q [B, nq, Hq, d], slot_mapping [B] int64
 
@@ -135,7 +136,7 @@ class Config:
     num_kv_heads: int
     head_dim: int
     q_dtype: str                      # "f32" | "bf16"
-    kv_dtype: str                     # "f32" | "bf16" | "i8"
+    kv_dtype: str                     # "f32" | "bf16" | "i8" | "fp8"
     lengths: Optional[Tuple[int, ...]] = None      # fixed context lengths, or
     length_range: Optional[Tuple[int, int]] = None  # inclusive uniform range
     lengths_are_cached: bool = False  # True: the step appends after these tokens
@@ -176,6 +177,9 @@ CONFIGS = {
     # speculative verify: 1 + 5 draft positions, causal, int8 KV, context U[1024, 8192]
     "verify_int8": Config("verify_int8", 32, 32, 8, 128, "bf16", "i8",
                           length_range=(1024, 8192), num_q_pos=6, append=False, seed=1004),
+    # fp8 e4m3 KV (per-(block, head) scales), the Llama-3-8B decode shape: half the bytes
+    "llama3_8b_fp8": Config("llama3_8b_fp8", 64, 32, 8, 128, "bf16", "fp8",
+                            length_range=(512, 4096), append=False, seed=1006),
     # sliding-window decode (Mistral-7B-shaped layer: 32q/8kv, d128, window 4096), batch
     # 64, context U[2048, 16384] so that most sequences run past the window
     "mistral_7b_window": Config("mistral_7b_window", 64, 32, 8, 128, "bf16", "bf16",
@@ -207,11 +211,11 @@ class Workload:
         """Algorithmic bytes of K and V one pass over every sequence must read:
         each attended token's K and V once (plus the int8 scales of used blocks)."""
         c = self.cfg
-        elem = {"f32": 4, "bf16": 2, "i8": 1}[c.kv_dtype]
+        elem = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1}[c.kv_dtype]
         toks = sum(self.visible_range(int(L))[1] - self.visible_range(int(L))[0]
                    for L in self.seq_lens.tolist())
         nbytes = toks * 2 * c.num_kv_heads * c.head_dim * elem
-        if c.kv_dtype == "i8":
+        if c.kv_dtype in ("i8", "fp8"):
             used = 0
             for L in self.seq_lens.tolist():
                 lo, hi = self.visible_range(int(L))
@@ -299,14 +303,17 @@ def generate(cfg, seed=None, *, poison=True, spare_blocks=0, shuffle_batch=False
 
     live = torch.arange(BLOCK_SIZE)[None, :] < occ[:, None]          # [NB, 16]
     k_scale = v_scale = None
-    if cfg.kv_dtype == "i8":
-        k_tok, k_scale = _quantise_int8(k32, live)
-        v_tok, v_scale = _quantise_int8(v32, live)
+    if cfg.kv_dtype in ("i8", "fp8"):
+        enc = _quantise_int8 if cfg.kv_dtype == "i8" else _quantise_fp8
+        k_tok, k_scale = enc(k32, live)
+        v_tok, v_scale = enc(v32, live)
         if poison:
+            # int8: extreme codes; fp8: NaN codes (any byte of an unused slot may be one)
+            kp, vp = (127, -127) if cfg.kv_dtype == "i8" else (0x7F, 0xFF)
             for blk in (occ < BLOCK_SIZE).nonzero().flatten().tolist():
                 n = int(occ[blk])
-                k_tok[blk, :, n:, :] = 127
-                v_tok[blk, :, n:, :] = -127
+                k_tok[blk, :, n:, :] = kp
+                v_tok[blk, :, n:, :] = vp
                 if n == 0:
                     k_scale[blk] = float("nan")
                     v_scale[blk] = float("nan")
@@ -323,8 +330,8 @@ def generate(cfg, seed=None, *, poison=True, spare_blocks=0, shuffle_batch=False
     # ---- the step's new token: position L-1 of each sequence ------------------------
     slot_mapping = k_new = v_new = None
     if cfg.append:
-        if cfg.kv_dtype == "i8":
-            raise ValueError("append into an int8 cache is not part of this path")
+        if cfg.kv_dtype in ("i8", "fp8"):
+            raise ValueError("an 8-bit cache takes its new tokens through kv_append_quant")
         dt = _TORCH_DT[cfg.kv_dtype]
         k_new = torch.randn((B, Hkv, d), generator=gen).to(dt)
         v_new = torch.randn((B, Hkv, d), generator=gen).to(dt)
@@ -410,6 +417,20 @@ def _quantise_int8(x32, live):
     xq = torch.round(x32 / safe[:, :, None, None]).clamp_(-127, 127)
     xq = torch.where(scale[:, :, None, None] > 0, xq, torch.zeros(()))
     return xq.to(torch.int8), scale
+
+
+def _quantise_fp8(x32, live):
+    """e4m3 encoding per (block, KV head) of a token-major [NB, H, 16, d] pool: scale =
+    max|x| / 448 over the block's live slots, codes = x / scale converted to torch's
+    float8_e4m3fn (round to nearest even) after clamping to +-448, returned as uint8."""
+    m = live[:, None, :, None].expand_as(x32)
+    amax = torch.where(m, x32.abs(), torch.zeros(())).amax(dim=(2, 3))
+    scale = (amax / 448.0).to(torch.float32)
+    safe = torch.where(scale > 0, scale, torch.ones(()))
+    y = (x32 / safe[:, :, None, None]).clamp_(-448.0, 448.0)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    codes = torch.where(scale[:, :, None, None] > 0, codes, torch.zeros((), dtype=torch.uint8))
+    return codes, scale
 
 
 def encode_k(k_tok):
