@@ -452,7 +452,8 @@ def trace_summary(args, trace_dir):
         last = k
         if cur is not None:
             cur.setdefault(k, []).append((e - s0) / 1000)
-    names = ["llama3_8b", "llama2_70b_prefix", "long_128k", "verify_int8", "mistral_7b_window"]
+    names = ["llama3_8b", "llama2_70b_prefix", "long_128k", "verify_int8", "mistral_7b_window",
+             "llama3_8b_fp8"]
     lines = [f"# rocprofv3 kernel trace: bench.py --path {args.path} --layout {args.layout}", "",
              "Command (MI355X, one GPU):", "",
              f"    rocprofv3 --kernel-trace --stats -d {trace_dir} -o run -- python bench.py "
@@ -516,7 +517,8 @@ def main():
 
     others = {}
     if not args.no_others:
-        for name in ("llama2_70b_prefix", "long_128k", "verify_int8", "mistral_7b_window"):
+        for name in ("llama2_70b_prefix", "long_128k", "verify_int8", "mistral_7b_window",
+                     "llama3_8b_fp8"):
             w2 = W.generate(name, poison=False)
             copies = 1 if name == "long_128k" else 2
             r2 = Runner(P, w2, "step", None, copies=copies, layout=args.layout)

@@ -20,7 +20,7 @@
  * this library uses
  *
  *   k_cache[num_blocks][num_kv_heads][head_dim / x][16][x]   x = 16 / element bytes
- *                                                         (x = 4 fp32, 8 bf16, 16 int8)
+ *                                                (x = 4 fp32, 8 bf16, 16 int8 / fp8)
  *   v_cache[num_blocks][num_kv_heads][head_dim][16]
  *
  * so one (block, KV head) tile of K or V is one contiguous 16 x head_dim piece of memory.
@@ -32,7 +32,7 @@
  * Inside a K tile, element k of the token at offset o sits at [k / x][o][k % x]: each
  * 16-byte column of the 16 tokens' K rows is contiguous.  Inside a V tile, element k of
  * that token sits at [k][o].
- * int8 caches carry one fp32 scale per (physical block, KV head) for each of K and V:
+ * int8 and fp8 caches carry one fp32 scale per (physical block, KV head) for each of K and V:
  * k_scale[num_blocks][num_kv_heads], v_scale[num_blocks][num_kv_heads]; the stored code x_q
  * stands for x_q * scale (lecture 10 "Quantization 量化 / 基本概念", zero point 0).
  *
@@ -61,8 +61,12 @@
 extern "C" {
 #endif
 
-/* element types */
-enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 };
+/* element types.  PA_I8 and PA_FP8 caches hold 8-bit codes with one fp32 scale per
+   (physical block, KV head) for K and one for V (k_scale, v_scale [num_blocks][Hkv]):
+   x = code * scale.  PA_I8 codes are signed integers; PA_FP8 codes are OCP e4m3 floats
+   (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 NaN).
+   A per-head calibrated fp8 scale is every block of the head holding the same value. */
+enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2, PA_FP8 = 3 };
 
 /* status codes */
 enum {
@@ -89,7 +93,7 @@ typedef struct pa_dims {
   int32_t max_blocks_per_seq; /* row length of block_tables (>= 1)                         */
   int64_t num_blocks;         /* physical blocks in each of k_cache / v_cache (>= 1)       */
   int32_t q_dtype;            /* PA_F32 or PA_BF16                                         */
-  int32_t kv_dtype;           /* PA_F32, PA_BF16 or PA_I8                                  */
+  int32_t kv_dtype;           /* PA_F32, PA_BF16, PA_I8 or PA_FP8                          */
   int64_t kv_tile_stride;     /* elements from one (block, KV head) tile to the next in
                                  k_cache and in v_cache; 0 means 16 * head_dim (dense).
                                  Otherwise >= 16 * head_dim and a multiple of 16 bytes
@@ -100,7 +104,7 @@ typedef struct pa_dims {
                                  call honours it; kv_append, kv_gather and kv_copy_blocks
                                  ignore it.  < 0 is PA_ERR_DIMS                             */
 } pa_dims;
-/* Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, I8). */
+/* Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, I8), (BF16, FP8). */
 
 /*
  * kv_append -- write each new token's K and V into its cache slot.
@@ -121,7 +125,8 @@ int kv_append(const pa_dims* dims, const void* k_new, const void* v_new,
  * paged_decode_attn -- single-token decode attention over the paged cache (nq = 1).
  *   q            device, [B][Hq][head_dim], q_dtype
  *   k_cache, v_cache device, layout above, kv_dtype
- *   k_scale, v_scale device, [num_blocks][Hkv] fp32; required for PA_I8, ignored otherwise
+ *   k_scale, v_scale device, [num_blocks][Hkv] fp32; required for PA_I8 and PA_FP8, ignored
+ *                otherwise
  *   block_tables device, [B][max_blocks_per_seq] int32
  *   seq_lens     device, [B] int32: tokens attended, including the new one
  *   sm_scale     the softmax scale (1/sqrt(head_dim) for the pages' formula)
@@ -193,11 +198,12 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
               void* k_out, void* v_out, void* stream);
 
 /*
- * kv_append_quant -- append new tokens to an int8 cache (lecture 10's symmetric int8
- * rule, zero point 0; in-depth guide section 5.2: per-head scales for KV caches).  A
- * (block, KV head) keeps one fp32 scale = max|x| / 127 over its live tokens and codes
- * round-half-even(x / scale) clamped to +-127 (all 0 when the scale is 0), the same
- * encoding as a cache quantised whole.  Because the scale depends on every token of the
+ * kv_append_quant -- append new tokens to an int8 or fp8 cache (lecture 10's symmetric int8
+ * rule, zero point 0; in-depth guide section 5.2: per-head scales for KV caches, FP8 KV
+ * caches).  A (block, KV head) keeps one fp32 scale over its live tokens: int8 scale =
+ * max|x| / 127 and codes round-half-even(x / scale) clamped to +-127; fp8 scale =
+ * max|x| / 448 and codes e4m3(x / scale), round to nearest even, saturating at +-448;
+ * all codes 0 when the scale is 0.  That is the same encoding as a cache quantised whole.  Because the scale depends on every token of the
  * block, the open block of each sequence is kept in bf16 in a staging row; token i is
  * written to staging offset slot % 16 and the block's live tokens 0 .. slot % 16 are
  * re-encoded from the staging row into the cache together with the new scale.  Once the
@@ -210,10 +216,10 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
  *                  and written: offsets 0 .. slot % 16 - 1 of the row must hold the
  *                  block's earlier tokens (written by earlier calls, or by the caller
  *                  after filling a block some other way)
- *   k_cache, v_cache device int8, written (offsets after slot % 16 are left as they are)
+ *   k_cache, v_cache device 8-bit, written (offsets after slot % 16 are left as they are)
  *   k_scale, v_scale device fp32 [num_blocks][Hkv], written
- * dims->kv_dtype must be PA_I8 (else PA_ERR_DTYPE).  No two tokens of one call may share
- * a block or a staging row (they would race); a decode step appends one token per
+ * dims->kv_dtype must be PA_I8 or PA_FP8 (else PA_ERR_DTYPE).  No two tokens of one call
+ * may share a block or a staging row (they would race); a decode step appends one token per
  * sequence.  New tokens, staging rows and caches must be 16-byte aligned (PA_ERR_ALIGN).
  */
 int kv_append_quant(const pa_dims* dims, const void* k_new, const void* v_new,
@@ -223,15 +229,15 @@ int kv_append_quant(const pa_dims* dims, const void* k_new, const void* v_new,
 
 /*
  * kv_copy_blocks -- copy whole physical blocks: for each pair (src, dst), every KV head's K
- * and V of block src (and, for int8, its k_scale / v_scale) is copied to block dst, bit
+ * and V of block src (and, for int8 / fp8, its k_scale / v_scale) is copied to block dst, bit
  * for bit.  This is the copy-on-write step of block sharing (tutorial section 7: shared
  * blocks carry reference counts; a sequence about to write into a shared, partly filled
  * block first gets a private copy of it).
  *   block_pairs  device, [num_pairs][2] int32 (src, dst); a pair with a block outside
  *                [0, num_blocks) or src == dst is skipped
  *   k_cache, v_cache device, written in place (either layout, kv_tile_stride honoured)
- *   k_scale, v_scale device, [num_blocks][Hkv] fp32, written; required for PA_I8,
- *                ignored otherwise
+ *   k_scale, v_scale device, [num_blocks][Hkv] fp32, written; required for PA_I8 and
+ *                PA_FP8, ignored otherwise
  * Copies run concurrently: no destination may also be a source or appear twice (a
  * destination is a freshly allocated block).  num_pairs may be 0 (nothing is launched).
  */
@@ -279,8 +285,9 @@ int paged_attn_balanced(const pa_dims* dims, int32_t num_q_pos, const void* q,
  * L - 1, L = seq_lens[b] (which counts it); its slot comes from the block table,
  * block_tables[b][(L - 1) / 16] * 16 + (L - 1) % 16 (tutorial section 7), so no slot
  * mapping is passed.
- *   k_new, v_new   device, [B][Hkv][head_dim] in kv_dtype (PA_F32 or PA_BF16; PA_I8 gives
- *                  PA_ERR_DTYPE); k_new 16-byte aligned
+ *   k_new, v_new   device, [B][Hkv][head_dim] in kv_dtype (PA_F32 or PA_BF16; PA_I8 and
+ *                  PA_FP8 give PA_ERR_DTYPE: use kv_append_quant, then
+ *                  paged_attn_balanced); k_new 16-byte aligned
  *   k_cache, v_cache device, read and written: the new token lands in its slot bit for bit
  *   other arguments as paged_attn_balanced with num_q_pos = 1; complete the step with
  *   paged_attn_balanced_merge (num_q_pos = 1) on the same stream.

@@ -9,7 +9,7 @@ names over torch tensors.  Importing it fails if the library has not been built
 (``python paged_gqa_decode_kv_amd/build.py``).
 """
 from ._binding import (  # noqa: F401
-    LIB_PATH, PA_BF16, PA_F32, PA_I8, PagedAttnError, kv_append, kv_gather, lib, lse_merge,
+    LIB_PATH, PA_BF16, PA_F32, PA_FP8, PA_I8, PagedAttnError, kv_append, kv_gather, lib, lse_merge,
     make_dims, pa_dims, paged_decode_attn, paged_decode_attn_split, paged_split_workspace_bytes,
     paged_status_string, paged_verify_attn, paged_attn_balanced, paged_attn_balanced_workgroups,
     paged_attn_balanced_workspace_bytes, paged_attn_balanced_merge, paged_decode_step,

@@ -41,9 +41,13 @@ int64_t tile_stride(const pa_dims* d) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// 8-bit codes with per-(block, KV head) scales
+bool scaled8(int dtype) { return dtype == PA_I8 || dtype == PA_FP8; }
+bool known_kv(int dtype) { return dtype == PA_F32 || dtype == PA_BF16 || scaled8(dtype); }
+
 int check_attn_types(const pa_dims* d) {
   if (d->q_dtype == PA_F32 && d->kv_dtype == PA_F32) return PA_OK;
-  if (d->q_dtype == PA_BF16 && (d->kv_dtype == PA_BF16 || d->kv_dtype == PA_I8)) return PA_OK;
+  if (d->q_dtype == PA_BF16 && (d->kv_dtype == PA_BF16 || scaled8(d->kv_dtype))) return PA_OK;
   return PA_ERR_DTYPE;
 }
 
@@ -55,7 +59,7 @@ int check_attn_inputs(const pa_dims* d, const void* q, const void* k, const void
   st = check_attn_types(d);
   if (st != PA_OK) return st;
   if (!q || !k || !v || !tables || !lens) return PA_ERR_NULL;
-  if (d->kv_dtype == PA_I8 && (!ks || !vs)) return PA_ERR_NULL;
+  if (scaled8(d->kv_dtype) && (!ks || !vs)) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return PA_ERR_ALIGN;
   return PA_OK;
 }
@@ -213,8 +217,7 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
               void* k_out, void* v_out, void* stream) {
   int st = check_dims(dims);
   if (st != PA_OK) return st;
-  if (dims->kv_dtype != PA_F32 && dims->kv_dtype != PA_BF16 && dims->kv_dtype != PA_I8)
-    return PA_ERR_DTYPE;
+  if (!known_kv(dims->kv_dtype)) return PA_ERR_DTYPE;
   if (max_len < 0) return PA_ERR_DIMS;
   if (max_len == 0) return PA_OK;
   if (!k_cache || !v_cache || !block_tables || !seq_lens || !k_out || !v_out) return PA_ERR_NULL;
@@ -230,7 +233,7 @@ int kv_append_quant(const pa_dims* dims, const void* k_new, const void* v_new,
                     void* v_cache, float* k_scale, float* v_scale, void* stream) {
   int st = check_dims(dims);
   if (st != PA_OK) return st;
-  if (dims->kv_dtype != PA_I8) return PA_ERR_DTYPE;
+  if (!scaled8(dims->kv_dtype)) return PA_ERR_DTYPE;
   if (num_tokens < 0 || num_stage_rows < 0) return PA_ERR_DIMS;
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !stage_rows || !k_stage || !v_stage || !k_cache ||
@@ -241,8 +244,8 @@ int kv_append_quant(const pa_dims* dims, const void* k_new, const void* v_new,
     return PA_ERR_ALIGN;
   return pa::launch_append_quant(k_new, v_new, slot_mapping, stage_rows, num_tokens,
                                  num_stage_rows, dims->num_kv_heads, dims->head_dim,
-                                 dims->num_blocks, tile_stride(dims), k_stage, v_stage, k_cache,
-                                 v_cache, k_scale, v_scale, stream);
+                                 dims->num_blocks, tile_stride(dims), dims->kv_dtype == PA_FP8,
+                                 k_stage, v_stage, k_cache, v_cache, k_scale, v_scale, stream);
 }
 
 int kv_copy_blocks(const pa_dims* dims, const int32_t* block_pairs, int32_t num_pairs,
@@ -250,17 +253,16 @@ int kv_copy_blocks(const pa_dims* dims, const int32_t* block_pairs, int32_t num_
                    void* stream) {
   int st = check_dims(dims);
   if (st != PA_OK) return st;
-  if (dims->kv_dtype != PA_F32 && dims->kv_dtype != PA_BF16 && dims->kv_dtype != PA_I8)
-    return PA_ERR_DTYPE;
+  if (!known_kv(dims->kv_dtype)) return PA_ERR_DTYPE;
   if (num_pairs < 0) return PA_ERR_DIMS;
   if (num_pairs == 0) return PA_OK;
   if (!block_pairs || !k_cache || !v_cache) return PA_ERR_NULL;
-  if (dims->kv_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (scaled8(dims->kv_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
   return pa::launch_copy_blocks(block_pairs, num_pairs, dims->num_kv_heads, dims->head_dim,
                                 dims->num_blocks, tile_stride(dims), elem_bytes(dims->kv_dtype),
-                                k_cache, v_cache, dims->kv_dtype == PA_I8 ? k_scale : nullptr,
-                                dims->kv_dtype == PA_I8 ? v_scale : nullptr, stream);
+                                k_cache, v_cache, scaled8(dims->kv_dtype) ? k_scale : nullptr,
+                                scaled8(dims->kv_dtype) ? v_scale : nullptr, stream);
 }
 
 int paged_attn_balanced_workgroups(const pa_dims* dims, int32_t num_q_pos) {

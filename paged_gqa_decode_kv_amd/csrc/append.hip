@@ -11,10 +11,10 @@
 // tile addressing the attention kernels use, so its output checks that translation
 // bit for bit.
 //
-// Quantising append into an int8 cache (lecture 10 symmetric int8 rule; in-depth guide
-// section 5.2 per-head scales): a block's scale is max|x| / 127 over its live tokens, so
-// the sequence's open block is kept in bf16 in a staging row and re-encoded from it
-// whenever a token arrives.  One workgroup per (token, KV head), 2 * head_dim threads:
+// Quantising append into an int8 or fp8 cache (lecture 10 symmetric int8 rule; in-depth
+// guide section 5.2 per-head scales, FP8 KV caches): a block's scale is max|x| / 127
+// (int8) or max|x| / 448 (fp8 e4m3) over its live tokens, so the sequence's open block is
+// kept in bf16 in a staging row and re-encoded from it whenever a token arrives.  One workgroup per (token, KV head), 2 * head_dim threads:
 // thread j owns token j / (d / 8) of the block and 8 dims of it.
 //
 // Block copy (copy-on-write of shared blocks, tutorial section 7): for each (src, dst)
@@ -138,7 +138,31 @@ __global__ __launch_bounds__(256) void kv_copy_blocks_kernel(
   }
 }
 
-template <int D>
+// e4m3 byte of an fp32 value (OCP format: bias 7, 3 mantissa bits, subnormals below 2^-6):
+// round to nearest, ties to even, magnitudes at or above 448 saturate to 448; the sign bit
+// is the value's own.  The power-of-two scalings are exact, so rintf does the rounding.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t code;
+  if (!(a < 448.f)) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {             // subnormal grid m * 2^-9 (m = 8 is 2^-6)
+    code = (uint32_t)__builtin_rintf(a * 512.f);
+  } else {
+    int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFF) - 127;
+    int r = (int)__builtin_rintf(ldexpf(a, 3 - e));   // 8 .. 16
+    if (r == 16) {
+      e += 1;
+      r = 8;
+    }
+    code = (uint32_t)(((e + 7) << 3) | (r - 8));
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  return code | sign;
+}
+
+template <int D, bool FP8>
 __global__ __launch_bounds__(2 * D) void kv_append_quant_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int64_t* __restrict__ slot_mapping, const int32_t* __restrict__ stage_rows,
@@ -202,24 +226,34 @@ __global__ __launch_bounds__(2 * D) void kv_append_quant_kernel(
     km = fmaxf(km, s_max[0][w]);
     vm = fmaxf(vm, s_max[1][w]);
   }
-  const float ks = km / 127.f, vs = vm / 127.f;  // correctly rounded fp32 divisions
+  constexpr float kMax = FP8 ? 448.f : 127.f;
+  const float ks = km / kMax, vs = vm / kMax;  // correctly rounded fp32 divisions
   if (threadIdx.x == 0) {
     k_scale[kv_tile(blk, g, num_kv_heads)] = ks;
     v_scale[kv_tile(blk, g, num_kv_heads)] = vs;
   }
   if (t > off) return;
   const int64_t tile = kv_tile(blk, g, num_kv_heads) * tile_stride;
-  // codes: round-half-even(x / scale) clamped to +-127, 0 for a zero scale
+  // codes: int8 round-half-even(x / scale) clamped to +-127, or e4m3(x / scale); 0 for a
+  // zero scale
   uint32_t kc[2] = {0u, 0u};
   int8_t* vt = v_cache + tile;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float qk = ks > 0.f ? __builtin_rintf(kx[e] / ks) : 0.f;
-    float qv = vs > 0.f ? __builtin_rintf(vx[e] / vs) : 0.f;
-    qk = fminf(fmaxf(qk, -127.f), 127.f);
-    qv = fminf(fmaxf(qv, -127.f), 127.f);
-    kc[e / 4] |= ((uint32_t)(int32_t)qk & 0xffu) << (8 * (e % 4));
-    vt[v_elem(t, k0 + e)] = (int8_t)(int)qv;
+    uint32_t ck = 0u, cv = 0u;
+    if constexpr (FP8) {
+      if (ks > 0.f) ck = e4m3_encode(kx[e] / ks);
+      if (vs > 0.f) cv = e4m3_encode(vx[e] / vs);
+    } else {
+      float qk = ks > 0.f ? __builtin_rintf(kx[e] / ks) : 0.f;
+      float qv = vs > 0.f ? __builtin_rintf(vx[e] / vs) : 0.f;
+      qk = fminf(fmaxf(qk, -127.f), 127.f);
+      qv = fminf(fmaxf(qv, -127.f), 127.f);
+      ck = (uint32_t)(int32_t)qk & 0xffu;
+      cv = (uint32_t)(int32_t)qv & 0xffu;
+    }
+    kc[e / 4] |= ck << (8 * (e % 4));
+    vt[v_elem(t, k0 + e)] = (int8_t)(uint8_t)cv;
   }
   // the 8 dims are contiguous inside one 16-byte K column
   *reinterpret_cast<u32x2*>(k_cache + tile + k_elem<1>(t, k0)) = u32x2{kc[0], kc[1]};
@@ -230,8 +264,9 @@ __global__ __launch_bounds__(2 * D) void kv_append_quant_kernel(
 int launch_append_quant(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                         const int32_t* stage_rows, int32_t num_tokens, int32_t num_stage_rows,
                         int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
-                        int64_t tile_stride, void* k_stage, void* v_stage, void* k_cache,
-                        void* v_cache, float* k_scale, float* v_scale, void* stream) {
+                        int64_t tile_stride, bool fp8, void* k_stage, void* v_stage,
+                        void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                        void* stream) {
   const int64_t grid = (int64_t)num_tokens * num_kv_heads;
   if (grid > 0x7fffffff) return PA_ERR_DIMS;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -241,14 +276,15 @@ int launch_append_quant(const void* k_new, const void* v_new, const int64_t* slo
   auto vn = static_cast<const uint16_t*>(v_new);
   auto kst = static_cast<uint16_t*>(k_stage);
   auto vst = static_cast<uint16_t*>(v_stage);
+  auto go = [&](auto kern, int threads) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), 0, s, kn, vn, slot_mapping,
+                       stage_rows, num_kv_heads, num_blocks, num_stage_rows, tile_stride, kst, vst,
+                       k8, v8, k_scale, v_scale);
+  };
   if (head_dim == 64)
-    hipLaunchKernelGGL(kv_append_quant_kernel<64>, dim3((unsigned)grid), dim3(128), 0, s, kn, vn,
-                       slot_mapping, stage_rows, num_kv_heads, num_blocks, num_stage_rows,
-                       tile_stride, kst, vst, k8, v8, k_scale, v_scale);
+    fp8 ? go(kv_append_quant_kernel<64, true>, 128) : go(kv_append_quant_kernel<64, false>, 128);
   else
-    hipLaunchKernelGGL(kv_append_quant_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, kn, vn,
-                       slot_mapping, stage_rows, num_kv_heads, num_blocks, num_stage_rows,
-                       tile_stride, kst, vst, k8, v8, k_scale, v_scale);
+    fp8 ? go(kv_append_quant_kernel<128, true>, 256) : go(kv_append_quant_kernel<128, false>, 256);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -350,8 +350,56 @@ struct I8Kv {
   }
 };
 
-template <class KV> struct IsInt8 { static constexpr bool value = false; };
-template <int D> struct IsInt8<I8Kv<D>> { static constexpr bool value = true; };
+// fp8 e4m3 codes (OCP format) with the same per-(block, KV head) scales and tile layout as
+// int8.  gfx950 converts two e4m3 bytes to two fp16 values in one instruction
+// (v_cvt_scalef32_pk_f16_fp8, scale 1); every e4m3 value, subnormals included, is exact in
+// fp16, so the MFMA operands are exact as for int8.  Unlike int8, any byte pattern of an
+// unused slot may be a NaN code, so V codes past the sequence end are zeroed.
+__device__ __forceinline__ f16x4 fp8x4_to_f16x4(uint32_t w) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  return f16x4{a[0], a[1], b[0], b[1]};
+}
+
+template <int D>
+struct Fp8Kv : I8Kv<D> {
+  using Base = I8Kv<D>;
+  using typename Base::K;
+  using typename Base::V;
+  using typename Base::KMat;
+  using typename Base::VMat;
+  static constexpr int NH = Base::NH;
+  static constexpr int ND = Base::ND;
+  __device__ static KMat k_mat(const K& k) {
+    KMat m;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const f16x4 a0 = fp8x4_to_f16x4(k.v[h].x), a1 = fp8x4_to_f16x4(k.v[h].y);
+      const f16x4 a2 = fp8x4_to_f16x4(k.v[h].z), a3 = fp8x4_to_f16x4(k.v[h].w);
+      m.v[2 * h] = f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      m.v[2 * h + 1] = f16x8{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
+    }
+    return m;
+  }
+  __device__ static VMat v_mat(const V& v) {
+    VMat m;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) m.v[t] = fp8x4_to_f16x4(v.v[t]);
+    return m;
+  }
+  // this lane's V words hold tokens 4 * grp .. 4 * grp + 3 (one byte each) of its dims
+  __device__ static void mask_v(V& v, int nvalid, int grp) {
+    const int keep = nvalid - 4 * grp;
+    const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : (1u << (8 * keep)) - 1u);
+#pragma unroll
+    for (int t = 0; t < ND; ++t) v.v[t] &= m;
+  }
+};
+
+// 8-bit codes with per-(block, KV head) scales (int8 or fp8)
+template <class KV> struct Scaled8 { static constexpr bool value = false; };
+template <int D> struct Scaled8<I8Kv<D>> { static constexpr bool value = true; };
+template <int D> struct Scaled8<Fp8Kv<D>> { static constexpr bool value = true; };
 
 // ---------------------------------------------------------------------------------------
 // Where a unit writes its rows.
@@ -364,7 +412,7 @@ enum OutMode { kDirect = 0, kSplit = 1, kBalanced = 2 };
 template <class KV, int D, int NT>
 struct Rows {
   static constexpr int ND = D / 16;
-  static constexpr bool kInt8 = IsInt8<KV>::value;
+  static constexpr bool kScaled = Scaled8<KV>::value;
   f32x4 acc[NT][ND];
   float m[NT], l[NT];
   float v_ref, inv_vref256;
@@ -377,8 +425,8 @@ struct Rows {
 #pragma unroll
       for (int t = 0; t < ND; ++t) acc[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    v_ref = kInt8 ? vref : 1.f;
-    inv_vref256 = kInt8 ? 256.f / vref : 1.f;
+    v_ref = kScaled ? vref : 1.f;
+    inv_vref256 = kScaled ? 256.f / vref : 1.f;
   }
 
   // One 16-token block whose first token is tok0: rows see tokens in [lo[nt], lim[nt])
@@ -392,7 +440,7 @@ struct Rows {
                                          typename KV::K& kk, typename KV::V& vv,
                                          int tok0, float sc, float vs, int grp) {
     float vfac = 1.f;
-    if constexpr (kInt8) {
+    if constexpr (kScaled) {
       vfac = vs * inv_vref256;
       if (vfac > 4096.f) {
         // this block's V scale is far above the reference: move the reference to it so
@@ -454,7 +502,7 @@ struct Rows {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       l[nt] = wave_sum_across_groups(l[nt]);
-      if (kInt8) {
+      if (kScaled) {
         const float f = v_ref * (1.f / 256.f);
 #pragma unroll
         for (int t = 0; t < ND; ++t) acc[nt][t] *= f;
@@ -551,7 +599,7 @@ template <class KV, int D, int NT, int W, int NBUF, bool SW>
 __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int b, int g, int rg,
                                             int L, int lo, int hi, int64_t slot) {
   constexpr int ND = D / 16;
-  constexpr bool kInt8 = IsInt8<KV>::value;
+  constexpr bool kScaled = Scaled8<KV>::value;
   constexpr int kStage = 64;  // table entries staged in LDS per wave
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -577,8 +625,8 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   // Lane i fetches the entry of this wave's block k0 + i; the loop then reads them back
   // from LDS, so no dependent HBM load sits between consecutive tile loads.
   __shared__ int s_tbl[W][kStage];
-  __shared__ float s_ks[W][kInt8 ? kStage : 1];
-  __shared__ float s_vs[W][kInt8 ? kStage : 1];
+  __shared__ float s_ks[W][kScaled ? kStage : 1];
+  __shared__ float s_vs[W][kScaled ? kStage : 1];
   auto stage = [&](int k0) {
     const int k = k0 + lane;
     int ph = -1;
@@ -587,7 +635,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
       if (ph < 0 || (int64_t)ph >= a.num_blocks) ph = -1;
     }
     s_tbl[w][lane] = ph;
-    if constexpr (kInt8) {
+    if constexpr (kScaled) {
       float ks = 0.f, vs = 0.f;
       if (ph >= 0) {
         ks = a.k_scale[kv_tile(ph, g, a.num_kv_heads)];
@@ -611,7 +659,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
     if (k < nk) {
       const int si = k & (kStage - 1);
       sl.ph = __builtin_amdgcn_readfirstlane(s_tbl[w][si]);
-      if constexpr (kInt8) {
+      if constexpr (kScaled) {
         sl.ks = lds_uniform_f(s_ks[w][si]);
         sl.vs = lds_uniform_f(s_vs[w][si]);
       }
@@ -621,7 +669,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
 
   // int8: each block's V scale is folded into P relative to a reference scale
   float v_ref = 1.f;
-  if constexpr (kInt8) {
+  if constexpr (kScaled) {
     if (nk > 0) {
       const float s0 = lds_uniform_f(s_vs[w][0]);
       if (s0 > 0.f && s0 < 3.0e38f) v_ref = s0;
@@ -643,7 +691,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
     if (sl.ph < 0) return;
     const int tok0 = (jb + w + W * kidx) * kBlockTokens;
     st.template update<SW>(qop, lim, lim_min, lo_row, lo_max, hi, kk, vv, tok0,
-              a.scale_log2 * (kInt8 ? sl.ks : 1.f), sl.vs, grp);
+              a.scale_log2 * (kScaled ? sl.ks : 1.f), sl.vs, grp);
   };
 
   {
@@ -810,7 +858,7 @@ template <class KV, int D, int NT, int W, int NBUF, bool APP, bool SW>
 __global__ __launch_bounds__(kWave* W)
 __attribute__((amdgpu_waves_per_eu(BalancedWavesPerEU<KV, NT>::value)))
 void paged_attn_balanced_kernel(AttnArgs a) {
-  constexpr bool kInt8 = IsInt8<KV>::value;
+  constexpr bool kScaled = Scaled8<KV>::value;
   constexpr int kStage = 64;
   __shared__ int s_pref[kMaxBalancedSeqs + 1];
   __shared__ int s_fb[SW ? kMaxBalancedSeqs : 1];  // first block a row of the sequence may see
@@ -902,8 +950,8 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   // ---- per-wave LDS staging: tile index (physical block * Hkv + g, -1 = none) and int8
   // scales of this wave's blocks k0 .. k0 + 63; lane i resolves its own block's segment.
   __shared__ int s_tile[W][kStage];
-  __shared__ float s_ks[W][kInt8 ? kStage : 1];
-  __shared__ float s_vs[W][kInt8 ? kStage : 1];
+  __shared__ float s_ks[W][kScaled ? kStage : 1];
+  __shared__ float s_vs[W][kScaled ? kStage : 1];
   auto stage = [&](int k0) {
     const int k = k0 + lane;
     int tile = -1;
@@ -922,14 +970,14 @@ void paged_attn_balanced_kernel(AttnArgs a) {
                                     (SW ? s_fb[lo_b] : 0)];
       if (ph >= 0 && (int64_t)ph < a.num_blocks) {
         tile = (int)kv_tile(ph, g, a.num_kv_heads);
-        if constexpr (kInt8) {
+        if constexpr (kScaled) {
           ks = a.k_scale[tile];
           vs = a.v_scale[tile];
         }
       }
     }
     s_tile[w][lane] = tile;
-    if constexpr (kInt8) {
+    if constexpr (kScaled) {
       s_ks[w][lane] = ks;
       s_vs[w][lane] = vs;
     }
@@ -946,7 +994,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     if (k < n) {
       const int si = k & (kStage - 1);
       sl.tile = __builtin_amdgcn_readfirstlane(s_tile[w][si]);
-      if constexpr (kInt8) {
+      if constexpr (kScaled) {
         sl.ks = lds_uniform_f(s_ks[w][si]);
         sl.vs = lds_uniform_f(s_vs[w][si]);
       }
@@ -1067,7 +1115,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
         if (nxt.j >= 0 && nxt.j <= cur.j) nxt.j = -1;
       }
       float vref = 1.f;
-      if constexpr (kInt8) {
+      if constexpr (kScaled) {
         if (sl.tile >= 0 && sl.vs > 0.f && sl.vs < 3.0e38f) vref = sl.vs;
       }
       st.reset(vref);
@@ -1080,7 +1128,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
       if (new_tok) KV::patch(kk, vv, tok, off, row16, grp);
     }
     st.template update<SW>(qop, lim, lim_min, lo_row, lo_max, rows_hi(cur, L), kk, vv, tok0,
-              a.scale_log2 * (kInt8 ? sl.ks : 1.f), sl.vs, grp);
+              a.scale_log2 * (kScaled ? sl.ks : 1.f), sl.vs, grp);
     if constexpr (APP) {
       if (new_tok && cur.rg == 0) {  // keep the token for the store at the end
         if (napp == kAppCap) drain();
@@ -1183,7 +1231,7 @@ template <template <int> class KVT, int D>
 int dispatch_dim(const AttnArgs& a, Op op, void* stream) {
   constexpr int W = PA_WAVES;
   using KV = KVT<D>;
-  constexpr bool kCanAppend = !IsInt8<KV>::value;
+  constexpr bool kCanAppend = !Scaled8<KV>::value;
   if (a.rows <= 16) {
     if (op == kLaunch) return launch_one<KV, D, 1, W, PA_NBUF_1>(a, stream);
     if (op == kLaunchBalanced) return launch_balanced_one<KV, D, 1, W, PA_NBUF_1, false>(a, stream);
@@ -1211,6 +1259,7 @@ int dispatch(const AttnArgs& a, int q_dtype, int kv_dtype, Op op, void* stream) 
   if (q_dtype == PA_F32 && kv_dtype == PA_F32) return dispatch_kv<F32Kv>(a, op, stream);
   if (q_dtype == PA_BF16 && kv_dtype == PA_BF16) return dispatch_kv<Bf16Kv>(a, op, stream);
   if (q_dtype == PA_BF16 && kv_dtype == PA_I8) return dispatch_kv<I8Kv>(a, op, stream);
+  if (q_dtype == PA_BF16 && kv_dtype == PA_FP8) return dispatch_kv<Fp8Kv>(a, op, stream);
   return PA_ERR_DTYPE;
 }
 

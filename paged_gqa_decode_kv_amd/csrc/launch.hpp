@@ -74,8 +74,9 @@ int launch_append(const void* k_new, const void* v_new, const int64_t* slot_mapp
 int launch_append_quant(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                         const int32_t* stage_rows, int32_t num_tokens, int32_t num_stage_rows,
                         int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
-                        int64_t tile_stride, void* k_stage, void* v_stage, void* k_cache,
-                        void* v_cache, float* k_scale, float* v_scale, void* stream);
+                        int64_t tile_stride, bool fp8, void* k_stage, void* v_stage,
+                        void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                        void* stream);
 
 // tile_stride in elements; scales may be null (non-int8 caches)
 int launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, int32_t num_kv_heads,

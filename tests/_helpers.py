@@ -8,8 +8,8 @@ import torch
 import workloads as W
 from oracle import attention, paging
 
-KIND = {"f32": "f32", "bf16": "bf16", "i8": "i8"}
-TOL = {"f32": 1e-5, "bf16": 2e-3, "i8": 4e-3}
+KIND = {"f32": "f32", "bf16": "bf16", "i8": "i8", "fp8": "fp8"}
+TOL = {"f32": 1e-5, "bf16": 2e-3, "i8": 4e-3, "fp8": 4e-3}
 
 
 def say(msg):

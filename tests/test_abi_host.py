@@ -63,11 +63,13 @@ def _decode(d, q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, t=FAKE, lens=FAKE, out=
     (dict(sliding_window=-1), -2),
     (dict(q_dtype="f32", kv_dtype="bf16"), -3),
     (dict(q_dtype="bf16", kv_dtype="f32"), -3),
+    (dict(q_dtype="f32", kv_dtype="fp8"), -3),
+    (dict(kv_dtype=7), -3),
 ])
 def test_decode_dimension_and_type_checks(change, status):
     d = _dims()
     for k, v in change.items():
-        setattr(d, k, {"f32": 0, "bf16": 1, "i8": 2}.get(v, v) if isinstance(v, str) else v)
+        setattr(d, k, {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3}.get(v, v) if isinstance(v, str) else v)
     assert _decode(d) == status
 
 
@@ -188,3 +190,8 @@ def test_append_quant_checks():
     assert P.lib.kv_append_quant(ctypes.byref(d), *args(2, kst=ctypes.c_void_p(FAKE + 2))) == -9
     db = _dims()
     assert P.lib.kv_append_quant(ctypes.byref(db), *args(2)) == -3
+    d8 = _dims(kv_dtype="fp8")
+    assert P.lib.kv_append_quant(ctypes.byref(d8), *args(0)) == 0
+    assert P.lib.kv_append_quant(ctypes.byref(d8), *args(2, vs=None)) == -1
+    # fp8 attention needs the scales like int8
+    assert _decode(d8) == -1 and _decode(d8, ks=FAKE, vs=FAKE, out=FAKE + 8) == -9

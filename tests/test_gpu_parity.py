@@ -258,6 +258,10 @@ CASES = [
     ("verify_int8", dict(batch=4, length_range=(1, 40), num_q_pos=3, num_q_heads=16,
                          num_kv_heads=8)),
     ("llama3_8b", dict(batch=4, length_range=(1, 200), num_q_pos=4, append=False)),     # bf16 verify
+    ("llama3_8b_fp8", dict(batch=6, length_range=(1, 700))),                            # fp8 KV
+    ("llama3_8b_fp8", dict(batch=4, length_range=(1, 300), head_dim=64, num_q_heads=16,
+                           num_kv_heads=2)),
+    ("verify_int8", dict(batch=5, length_range=(6, 600), kv_dtype="fp8")),              # fp8 verify
 ]
 
 
@@ -365,13 +369,14 @@ def _interleave_i8(kc, vc):
     return comb, comb.data_ptr() + tile, 2 * tile
 
 
+@pytest.mark.parametrize("kind", ["i8", "fp8"])
 @pytest.mark.parametrize("interleave", [False, True])
 @pytest.mark.parametrize("d,hkv", [(128, 8), (64, 2)])
-def test_kv_append_quant_bit_exact(P, d, hkv, interleave):
+def test_kv_append_quant_bit_exact(P, d, hkv, interleave, kind):
     gen = torch.Generator().manual_seed(d + hkv + interleave)
     nb, S, T = 40, 24, 20
-    kc = torch.randint(-127, 128, (nb, hkv, d // 16, 16, 16), generator=gen, dtype=torch.int8)
-    vc = torch.randint(-127, 128, (nb, hkv, d, 16), generator=gen, dtype=torch.int8)
+    kc = torch.randint(-128, 128, (nb, hkv, d // 16, 16, 16), generator=gen, dtype=torch.int8)
+    vc = torch.randint(-128, 128, (nb, hkv, d, 16), generator=gen, dtype=torch.int8)
     ks = torch.rand((nb, hkv), generator=gen)
     vs = torch.rand((nb, hkv), generator=gen)
     kst = _rand_bf16(gen, (S, hkv, 16, d), 2.0)
@@ -385,13 +390,13 @@ def test_kv_append_quant_bit_exact(P, d, hkv, interleave):
     slots = (blocks * 16 + offs).to(torch.int64)
     rows = torch.randperm(S, generator=gen)[:T].to(torch.int32)
     slots[4], slots[5], rows[6], rows[7] = -1, nb * 16, -1, S    # skipped tokens
-    say(f"[case] append_quant d={d} hkv={hkv} interleave={interleave}")
+    say(f"[case] append_quant {kind} d={d} hkv={hkv} interleave={interleave}")
     if interleave:
         comb, vptr, stride = _interleave_i8(kc, vc)
         gk, gv = comb, vptr
     else:
         gk, gv, stride = kc.cuda(), vc.cuda(), 0
-    dims = P.make_dims(1, hkv, hkv, d, 1, nb, "bf16", "i8", kv_tile_stride=stride)
+    dims = P.make_dims(1, hkv, hkv, d, 1, nb, "bf16", kind, kv_tile_stride=stride)
     dks, dvs, dkst, dvst = ks.cuda(), vs.cuda(), kst.cuda(), vst.cuda()
     P.kv_append_quant(dims, kn.cuda(), vn.cuda(), slots.cuda(), rows.cuda(), T, dkst, dvst, gk, gv,
                       dks, dvs)
@@ -399,7 +404,7 @@ def test_kv_append_quant_bit_exact(P, d, hkv, interleave):
     r = lambda x: x.view(torch.int16).numpy()
     ok, ov, oks, ovs, okst, ovst = quant.append_quant(
         kc.numpy(), vc.numpy(), ks.numpy(), vs.numpy(), r(kst), r(vst), r(kn), r(vn),
-        slots.numpy(), rows.numpy())
+        slots.numpy(), rows.numpy(), kind=kind)
     if interleave:
         hk = comb[:, :, 0].reshape(kc.shape).cpu().numpy()
         hv = comb[:, :, 1].reshape(vc.shape).cpu().numpy()
@@ -411,8 +416,9 @@ def test_kv_append_quant_bit_exact(P, d, hkv, interleave):
     assert np.array_equal(r(dkst.cpu()), okst) and np.array_equal(r(dvst.cpu()), ovst)
 
 
+@pytest.mark.parametrize("kind", ["i8", "fp8"])
 @pytest.mark.parametrize("balanced", [None, 0])
-def test_int8_decode_steps_from_empty(P, balanced):
+def test_int8_decode_steps_from_empty(P, balanced, kind):
     """Sequences grow token by token from nothing through kv_append_quant (block
     boundaries crossed, scales growing), and decode attention reads the int8 cache after
     every step; the oracle does the same steps with its own quantising append."""
@@ -432,7 +438,7 @@ def test_int8_decode_steps_from_empty(P, balanced):
     ora = [kc.numpy(), vc.numpy(), ks.numpy(), vs.numpy(), r(kst), r(vst)]
     dev = [kc.cuda(), vc.cuda(), ks.cuda(), vs.cuda(), kst.cuda(), vst.cuda()]
     rows = torch.arange(B, dtype=torch.int32)
-    say(f"[case] int8 decode steps from empty balanced={balanced}")
+    say(f"[case] {kind} decode steps from empty balanced={balanced}")
     for step in range(steps + max(start)):
         live = [b for b in range(B) if start[b] <= step < start[b] + steps]
         slots = torch.full((B,), -1, dtype=torch.int64)
@@ -440,10 +446,11 @@ def test_int8_decode_steps_from_empty(P, balanced):
             slots[b] = alloc.append_token(b)[0]
         kn = _rand_bf16(gen, (B, hkv, d), 1.0 + step % 5)
         vn = _rand_bf16(gen, (B, hkv, d))
-        dims = P.make_dims(B, hq, hkv, d, 8, nb, "bf16", "i8")
+        dims = P.make_dims(B, hq, hkv, d, 8, nb, "bf16", kind)
         P.kv_append_quant(dims, kn.cuda(), vn.cuda(), slots.cuda(), rows.cuda(), B, dev[4], dev[5],
                           dev[0], dev[1], dev[2], dev[3])
-        ora = list(quant.append_quant(*ora, r(kn), r(vn), slots.numpy(), rows.numpy()))
+        ora = list(quant.append_quant(*ora, r(kn), r(vn), slots.numpy(), rows.numpy(),
+                                      kind=kind))
         if step % 6 != 5:
             continue
         tables = torch.full((B, 8), -1, dtype=torch.int32)
@@ -467,11 +474,11 @@ def test_int8_decode_steps_from_empty(P, balanced):
         torch.cuda.synchronize()
         assert np.array_equal(dev[0].cpu().numpy(), ora[0]) and np.array_equal(dev[1].cpu().numpy(), ora[1])
         assert np.array_equal(dev[2].cpu().numpy(), ora[2]) and np.array_equal(dev[3].cpu().numpy(), ora[3])
-        ref, _ = attention.paged_attention(r(q), "bf16", ora[0], ora[1], "i8", tables.numpy(),
+        ref, _ = attention.paged_attention(r(q), "bf16", ora[0], ora[1], kind, tables.numpy(),
                                            lens.numpy(), sm, 1, ora[2], ora[3])
         err = max_err(out, ref)
         say(f"  step {step} lens {lens.tolist()} max abs err {err:.3e}")
-        assert err <= TOL["i8"]
+        assert err <= TOL[kind]
 
 
 # ---- sliding window ------------------------------------------------------------------
@@ -667,6 +674,26 @@ def test_full_llama3_8b(P):
     _check_attention(P, wl, split=(512, 8))
     _check_attention(P, wl, balanced=0)
     _check_attention(P, wl, balanced=0, interleave=True)
+
+
+def test_full_llama3_8b_fp8(P):
+    wl = W.generate("llama3_8b_fp8")
+    _check_attention(P, wl, balanced=0, interleave=True)
+    _check_attention(P, wl, split=(512, 8))
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("llama3_8b_fp8", dict(batch=6, length_range=(1, 700))),
+    ("verify_int8", dict(batch=5, length_range=(6, 600), kv_dtype="fp8")),
+    ("llama3_8b_fp8", dict(batch=6, length_range=(1, 700), sliding_window=40)),
+])
+def test_fp8_all_modes(P, name, kw):
+    wl = _small(name, **kw)
+    _check_attention(P, wl, interleave=True)
+    _check_attention(P, wl, balanced=0)
+    _check_attention(P, wl, balanced=5, interleave=True)
+    if wl.cfg.num_q_pos == 1:
+        _check_attention(P, wl, split=(64, 40))
 
 
 def test_full_llama2_70b_shared_prefix(P):
