@@ -299,10 +299,36 @@ struct I8Kv {
 #pragma unroll
     for (int h = 0; h < NH; ++h) k.v[h] = stream_load<u32x4>(p + 1024 * h);
   }
+  // V is loaded 16 bytes at a time: lane (row16, grp) takes all 16 tokens of dims
+  // 16 * (TPG * grp + u) + row16 (u < TPG = ND / 4), one 16-byte row of the [d][16] tile
+  // each, so word 4u + c holds tokens 4c .. 4c + 3 of those dims.  v_mat() moves word c of
+  // row group s to row group c (transpose_rows4), which gives every lane the tokens
+  // 4 * grp .. 4 * grp + 3 of dims 16 t + row16 that the MFMA operand wants.  (Four-byte
+  // loads in the operand order issue four times as many load instructions; the 16-byte
+  // form measured 3-6% faster on the 8-bit workloads.)
+  static constexpr int TPG = ND / 4;
   __device__ static void load_v(V& v, const void* tile, int row16, int grp) {
-    const uint8_t* p = static_cast<const uint8_t*>(tile) + row16 * 16 + 4 * grp;
+    const uint8_t* p = static_cast<const uint8_t*>(tile) + (16 * TPG * grp + row16) * 16;
 #pragma unroll
-    for (int t = 0; t < ND; ++t) v.v[t] = stream_load<uint32_t>(p + t * 256);
+    for (int u = 0; u < TPG; ++u) {
+      const u32x4 x = stream_load<u32x4>(p + 256 * u);
+      v.v[4 * u] = x.x;
+      v.v[4 * u + 1] = x.y;
+      v.v[4 * u + 2] = x.z;
+      v.v[4 * u + 3] = x.w;
+    }
+  }
+  // the operand word of tile t = TPG * c + u after the transpose of set u
+  __device__ static void v_words(const V& v, uint32_t* w) {
+#pragma unroll
+    for (int u = 0; u < TPG; ++u) {
+      uint32_t a = v.v[4 * u], b = v.v[4 * u + 1], c = v.v[4 * u + 2], d = v.v[4 * u + 3];
+      transpose_rows4(a, b, c, d);
+      w[u] = a;
+      w[TPG + u] = b;
+      w[2 * TPG + u] = c;
+      w[3 * TPG + u] = d;
+    }
   }
   // int8 codes decoded once per block to exact fp16 MFMA operands (shared by all row tiles)
   struct KMat { f16x8 v[2 * NH]; };
@@ -319,9 +345,11 @@ struct I8Kv {
     return m;
   }
   __device__ static VMat v_mat(const V& v) {
+    uint32_t w[ND];
+    v_words(v, w);
     VMat m;
 #pragma unroll
-    for (int t = 0; t < ND; ++t) m.v[t] = i8x4_to_f16x4(v.v[t]);
+    for (int t = 0; t < ND; ++t) m.v[t] = i8x4_to_f16x4(w[t]);
     return m;
   }
   __device__ static f32x4 qk(const KMat& k, const Q& q) {
@@ -382,17 +410,22 @@ struct Fp8Kv : I8Kv<D> {
     return m;
   }
   __device__ static VMat v_mat(const V& v) {
+    uint32_t w[ND];
+    Base::v_words(v, w);
     VMat m;
 #pragma unroll
-    for (int t = 0; t < ND; ++t) m.v[t] = fp8x4_to_f16x4(v.v[t]);
+    for (int t = 0; t < ND; ++t) m.v[t] = fp8x4_to_f16x4(w[t]);
     return m;
   }
-  // this lane's V words hold tokens 4 * grp .. 4 * grp + 3 (one byte each) of its dims
-  __device__ static void mask_v(V& v, int nvalid, int grp) {
-    const int keep = nvalid - 4 * grp;
-    const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : (1u << (8 * keep)) - 1u);
+  // as loaded, word 4u + c holds tokens 4c .. 4c + 3 (one byte each)
+  __device__ static void mask_v(V& v, int nvalid, int) {
 #pragma unroll
-    for (int t = 0; t < ND; ++t) v.v[t] &= m;
+    for (int c = 0; c < 4; ++c) {
+      const int keep = nvalid - 4 * c;
+      const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : (1u << (8 * keep)) - 1u);
+#pragma unroll
+      for (int u = 0; u < Base::TPG; ++u) v.v[4 * u + c] &= m;
+    }
   }
 };
 

@@ -96,6 +96,22 @@ __device__ __forceinline__ float xor32_pair_sum(float x) {
   xor32_pair(x, a, b);
   return a + b;
 }
+// 4 x 4 transpose of 32-bit words across the four 16-lane rows: on entry row s holds
+// M[s][0..3] in w0..w3, on exit row g holds M[0..3][g].  The xor-32 swaps exchange the
+// off-diagonal 2 x 2 blocks between the halves, the xor-16 swaps transpose each block.
+__device__ __forceinline__ void transpose_rows4(uint32_t& w0, uint32_t& w1, uint32_t& w2,
+                                                uint32_t& w3) {
+  auto r02 = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
+  auto r13 = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
+  const uint32_t a0 = r02[0], a2 = r02[1], a1 = r13[0], a3 = r13[1];
+  auto r01 = __builtin_amdgcn_permlane16_swap(a0, a1, false, false);
+  auto r23 = __builtin_amdgcn_permlane16_swap(a2, a3, false, false);
+  w0 = r01[0];
+  w1 = r01[1];
+  w2 = r23[0];
+  w3 = r23[1];
+}
+
 __device__ __forceinline__ float wave_max_across_groups(float x) {
   return xor32_pair_max(xor16_pair_max(x));
 }
