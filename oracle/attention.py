@@ -28,6 +28,15 @@ only to the most recent W tokens).  Reading taken: the W tokens end at and inclu
 row's own position p, so a row sees tokens max(0, p - W + 1) .. p; W = 0 means no window
 (the whole causal prefix).
 
+Multi-query rows (guide §3.3 speculative trees; §4.1 chunked prefill): the last nq
+tokens of a sequence are query positions, already in the cache.  Chunked prefill is the
+causal case above with nq up to a few hundred.  A speculative tree puts nq candidate
+tokens in the cache in tree order (a parent before its children); candidate i then sees
+every context token t < L - nq and the candidate j (position L - nq + j) only if j is i
+itself or one of its ancestors.  Reading taken: the tree arrives as a visibility mask
+mask[i][j] over the nq candidates (1 = visible), so any mask, the causal one included,
+is accepted.
+
 Context split (not on the pages; stated by the benchmark spec): the tokens visible to a row
 are cut into partitions, attention is taken over each (o_p, lse_p), and the
 partials are recombined with the log-sum-exp identity
@@ -79,6 +88,34 @@ def row_starts(seq_len, num_q_pos, window):
     return [max(0, lam - window) for lam in row_limits(seq_len, num_q_pos)]
 
 
+def attend_indices(q_rows, K, V, sigma, index_lists):
+    """fp64 attention of each row over the rows index_lists[r] of K and V."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    R, d = q_rows.shape
+    out = np.zeros((R, d), dtype=np.float64)
+    lse = np.full((R,), -np.inf, dtype=np.float64)
+    for r in range(R):
+        idx = np.asarray(index_lists[r], dtype=np.int64)
+        if idx.size == 0:
+            continue
+        s = sigma * (K[idx] @ q_rows[r])
+        m = s.max()
+        e = np.exp(s - m)
+        l = e.sum()
+        out[r] = (e @ V[idx]) / l
+        lse[r] = m + np.log(l)
+    return out, lse
+
+
+def tree_visible(seq_len, num_q_pos, i, mask_row):
+    """Tokens query position i sees under a candidate mask: all context tokens
+    t < seq_len - nq, then candidate j at seq_len - nq + j where mask_row[j] is set
+    (candidates before position 0 of the sequence do not exist)."""
+    base = seq_len - num_q_pos
+    ctx = list(range(max(0, base)))
+    return ctx + [base + j for j in range(num_q_pos) if mask_row[j] and base + j >= 0]
+
+
 def _group_rows(q_dec, b, g, G, num_q_pos):
     """Rows (i, head) of sequence b that read KV head g, in (i, head) order."""
     rows, idx = [], []
@@ -91,7 +128,8 @@ def _group_rows(q_dec, b, g, G, num_q_pos):
 
 
 def paged_attention(q, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens, sigma,
-                    num_q_pos=1, k_scale=None, v_scale=None, pairs=None, fast=True, window=0):
+                    num_q_pos=1, k_scale=None, v_scale=None, pairs=None, fast=True, window=0,
+                    tree_mask=None):
     """Attention of every query row against its sequence's paged cache.
 
     q: [B, nq, Hq, d] stored as ``q_kind``; caches in the project format (see
@@ -99,7 +137,9 @@ def paged_attention(q, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens
     ``pairs`` (a list of (b, g)) only those sequence/KV-head pairs are computed and
     every other entry is NaN.  ``sigma`` is used as given (pass the fp32 value the
     kernel receives, widened).  ``window`` > 0: sliding-window attention over the
-    ``window`` most recent tokens of each row (``row_starts``).
+    ``window`` most recent tokens of each row (``row_starts``).  ``tree_mask``
+    ([B, nq, nq] booleans, or None for causal rows): candidate visibility
+    (``tree_visible``); it is not combined with a window.
     """
     qd = storage.decode(q, q_kind)
     B, nq, Hq, d = qd.shape
@@ -115,9 +155,13 @@ def paged_attention(q, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens
         L = int(seq_lens[b])
         K, V = dep(k_cache, v_cache, kv_kind, block_tables[b], L, g, k_scale, v_scale)
         rows, idx = _group_rows(qd, b, g, G, nq)
-        lim = row_limits(L, nq)
-        lo = row_starts(L, nq, window)
-        o, ls = attend(rows, K, V, sigma, [lim[i] for i, _ in idx], [lo[i] for i, _ in idx])
+        if tree_mask is None:
+            lim = row_limits(L, nq)
+            lo = row_starts(L, nq, window)
+            o, ls = attend(rows, K, V, sigma, [lim[i] for i, _ in idx], [lo[i] for i, _ in idx])
+        else:
+            vis = [tree_visible(L, nq, i, tree_mask[b][i]) for i in range(nq)]
+            o, ls = attend_indices(rows, K, V, sigma, [vis[i] for i, _ in idx])
         for r, (i, h) in enumerate(idx):
             out[b, i, h] = o[r]
             lse[b, i, h] = ls[r]

@@ -291,3 +291,84 @@ def test_sliding_window_at_least_the_context_is_full_attention():
     assert attention.row_starts(50, 3, 0) == [0, 0, 0]
     assert attention.row_starts(50, 3, 10) == [38, 39, 40]
     assert attention.row_starts(5, 3, 10) == [0, 0, 0]
+
+
+# ---- multi-query rows: speculative trees and chunked prefill ---------------------------
+def test_causal_tree_mask_is_the_verify_result():
+    wl = _small("verify_int8", head_dim=32, num_q_heads=4, num_kv_heads=2, length_range=(1, 70))
+    nq = wl.cfg.num_q_pos
+    causal = torch.tril(torch.ones((nq, nq), dtype=torch.bool)).expand(wl.cfg.batch, nq, nq)
+    out, lse = _paged(wl)
+    out2, lse2 = _paged(wl, tree_mask=causal.numpy())
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_tree_closed_form():
+    # uniform attention over V[t] = t: candidate i's output is the mean position of the
+    # context tokens and of its ancestors-or-self
+    nq, d, G = 7, 4, 2
+    parents = [-1, 0, 0, 1, 1, 2, 5]
+    mask = W.tree_mask_from_parents(parents).numpy()[None]
+    tables = np.array([[2, 0, 1]], dtype=np.int32)
+    kc = np.ones((3, 1, d // 4, 16, 4), np.float32)
+    vc = np.zeros((3, 1, d, 16), np.float32)
+    for t in range(48):
+        vc[tables[0, t // 16], 0, :, t % 16] = t
+    q = np.ones((1, nq, G, d), np.float32)
+    for L in (7, 20, 40):
+        out, lse = attention.paged_attention(q, "f32", kc, vc, "f32", tables, np.array([L]), 0.5,
+                                             nq, tree_mask=mask)
+        base = L - nq
+        for i in range(nq):
+            anc, j = [], i
+            while j >= 0:
+                anc.append(base + j)
+                j = parents[j]
+            vis = list(range(base)) + anc
+            assert np.allclose(out[0, i], np.mean(vis), atol=1e-12), (L, i)
+            assert abs(lse[0, i, 1] - (0.5 * d + math.log(len(vis)))) < 1e-12
+
+
+def test_tree_row_equals_decode_over_its_path():
+    """Brute force through another cache: candidate i's result equals decode attention
+    over a fresh one-sequence pool holding the context and then the path root .. i."""
+    wl = W.generate(W.scaled("tree_verify", batch=3, length_range=(20, 70), num_q_pos=12,
+                             head_dim=32, num_q_heads=4, num_kv_heads=2, lengths=None),
+                    spare_blocks=2)
+    c = wl.cfg
+    nq = c.num_q_pos
+    out, lse = _paged(wl, tree_mask=wl.tree_mask.numpy())
+    Kt = W.k_token_rows(wl.k_cache)
+    Vt = wl.v_cache.transpose(2, 3)
+    raw = lambda x: x.view(torch.int16).numpy()
+    for b in range(c.batch):
+        L = int(wl.seq_lens[b])
+        for i in range(nq):
+            toks = list(range(L - nq)) + [L - nq + j for j in range(nq) if wl.tree_mask[b, i, j]]
+            nb = -(-len(toks) // 16)
+            kt = torch.zeros((nb, c.num_kv_heads, 16, c.head_dim), dtype=torch.bfloat16)
+            vt = torch.zeros_like(kt)
+            for n, t in enumerate(toks):
+                blk = int(wl.block_tables[b, t // 16])
+                kt[n // 16, :, n % 16] = Kt[blk, :, t % 16]
+                vt[n // 16, :, n % 16] = Vt[blk, :, t % 16]
+            o2, l2 = attention.paged_attention(
+                raw(wl.q[b:b + 1, i:i + 1]), "bf16", raw(W.encode_k(kt)), raw(W.encode_v(vt)),
+                "bf16", np.arange(nb, dtype=np.int32)[None], np.array([len(toks)]),
+                float(np.float32(wl.sm_scale)), 1)
+            assert np.allclose(out[b, i], o2[0, 0], rtol=0, atol=1e-13)
+            assert np.allclose(lse[b, i], l2[0, 0], rtol=0, atol=1e-12)
+
+
+def test_tree_rows_that_see_nothing():
+    # no context and a candidate whose row is empty: out 0, lse -inf
+    nq, d = 3, 4
+    mask = np.array([[[1, 0, 0], [0, 0, 0], [1, 1, 1]]], dtype=bool)
+    kc = np.ones((1, 1, 1, 16, 4), np.float32)
+    vc = np.ones((1, 1, d, 16), np.float32)
+    out, lse = attention.paged_attention(np.ones((1, nq, 1, d), np.float32), "f32", kc, vc, "f32",
+                                         np.array([[0]], np.int32), np.array([3]), 1.0, nq,
+                                         tree_mask=mask)
+    assert (out[0, 1] == 0).all() and lse[0, 1, 0] == -np.inf
+    assert np.allclose(out[0, 0], 1.0) and np.allclose(out[0, 2], 1.0)
+    assert W.tree_mask_words(torch.from_numpy(mask)).tolist() == [[[1], [0], [7]]]

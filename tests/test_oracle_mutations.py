@@ -89,6 +89,14 @@ MUTATIONS = [
      "scale = np.float32(amax / np.float32(480))", "test_oracle_quant.py"),
     ("fp8 ties away from zero", "oracle/quant.py", "r = int(np.rint(a * 2.0 ** (3 - e)))",
      "r = int(np.floor(a * 2.0 ** (3 - e) + 0.5))", "test_oracle_quant.py"),
+    ("tree mask transposed", "oracle/attention.py",
+     "vis = [tree_visible(L, nq, i, tree_mask[b][i]) for i in range(nq)]",
+     "vis = [tree_visible(L, nq, i, [tree_mask[b][r][i] for r in range(nq)]) for i in range(nq)]",
+     "test_oracle_attention.py"),
+    ("tree context one token short", "oracle/attention.py", "ctx = list(range(max(0, base)))",
+     "ctx = list(range(max(0, base - 1)))", "test_oracle_attention.py"),
+    ("tree candidate shifted", "oracle/attention.py", "if mask_row[j] and base + j >= 0]",
+     "if mask_row[j - 1] and base + j >= 0]", "test_oracle_attention.py"),
     ("copy direction swapped", "oracle/paging.py", "kc[dst] = k_cache[src]",
      "kc[src] = k_cache[dst]", "test_oracle_paging.py"),
     ("copy skips V", "oracle/paging.py", "vc[dst] = v_cache[src]", "pass",

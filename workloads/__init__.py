@@ -149,6 +149,7 @@ class Config:
     peaked_fraction: float = 0.0      # fraction of K slots scaled by peaked_factor
     peaked_factor: float = 8.0
     sliding_window: int = 0           # 0 = whole context; W = the W most recent tokens
+    tree: bool = False                # the nq query positions form a speculative tree
     seed: int = 0
 
     @property
@@ -177,6 +178,14 @@ CONFIGS = {
     # speculative verify: 1 + 5 draft positions, causal, int8 KV, context U[1024, 8192]
     "verify_int8": Config("verify_int8", 32, 32, 8, 128, "bf16", "i8",
                           length_range=(1024, 8192), num_q_pos=6, append=False, seed=1004),
+    # chunked prefill: a 256-token chunk of each of 4 prompts attends causally to the
+    # prompt so far (Llama-3-8B layer shape), context U[2048, 8192] including the chunk
+    "prefill_chunk": Config("prefill_chunk", 4, 32, 8, 128, "bf16", "bf16",
+                            length_range=(2048, 8192), num_q_pos=256, append=False, seed=1007),
+    # speculative tree verify: 64 candidates in a random tree per sequence, batch 32
+    "tree_verify": Config("tree_verify", 32, 32, 8, 128, "bf16", "bf16",
+                          length_range=(1024, 4096), num_q_pos=64, append=False, tree=True,
+                          seed=1008),
     # fp8 e4m3 KV (per-(block, head) scales), the Llama-3-8B decode shape: half the bytes
     "llama3_8b_fp8": Config("llama3_8b_fp8", 64, 32, 8, 128, "bf16", "fp8",
                             length_range=(512, 4096), append=False, seed=1006),
@@ -202,6 +211,7 @@ class Workload:
     v_new: Optional[torch.Tensor]
     occupancy: torch.Tensor           # live slots per physical block
     meta: dict = field(default_factory=dict)
+    tree_mask: Optional[torch.Tensor] = None   # [B, nq, nq] bool: candidate j visible to i
 
     @property
     def sm_scale(self):
@@ -348,14 +358,51 @@ def generate(cfg, seed=None, *, poison=True, spare_blocks=0, shuffle_batch=False
     k_cache, v_cache = encode_k(k_tok), encode_v(v_tok)
     del k_tok, v_tok
 
+    tree_mask = None
+    if cfg.tree:
+        tree_mask = torch.stack([tree_mask_from_parents(random_tree(cfg.num_q_pos, gen))
+                                 for _ in range(B)])
     wl = Workload(cfg, q, k_cache, v_cache, k_scale, v_scale, tables,
                   torch.tensor(lens, dtype=torch.int32), slot_mapping, k_new, v_new, occ,
                   meta={"seed": seed, "num_blocks": NB, "max_blocks": max_blocks,
-                        "allocator": alloc})
+                        "allocator": alloc}, tree_mask=tree_mask)
     if shuffle_batch:
         perm = torch.randperm(B, generator=gen)
         wl = permute_batch(wl, perm)
     return wl
+
+
+def random_tree(n, gen):
+    """Parent list of a random n-node candidate tree in tree order: node 0 is the root
+    (parent -1) and node j > 0 hangs under a node drawn uniformly from 0 .. j - 1."""
+    parents = [-1]
+    for j in range(1, n):
+        parents.append(int(torch.randint(0, j, (1,), generator=gen)))
+    return parents
+
+
+def tree_mask_from_parents(parents):
+    """[n, n] bool: mask[i][j] is True when node j is node i or one of its ancestors."""
+    n = len(parents)
+    m = torch.zeros((n, n), dtype=torch.bool)
+    for i in range(n):
+        j = i
+        while j >= 0:
+            m[i, j] = True
+            j = parents[j]
+    return m
+
+
+def tree_mask_words(mask):
+    """Bit rows of a [B, nq, nq] bool mask as the library reads them: [B, nq, ceil(nq/32)]
+    int32 words, bit j % 32 of word j // 32 of row i set when candidate j is visible."""
+    B, nq, _ = mask.shape
+    nw = -(-nq // 32)
+    words = torch.zeros((B, nq, nw), dtype=torch.int64)
+    for j in range(nq):
+        words[:, :, j // 32] |= mask[:, :, j].to(torch.int64) << (j % 32)
+    words = torch.where(words >= 2 ** 31, words - 2 ** 32, words)
+    return words.to(torch.int32).contiguous()
 
 
 def permute_batch(wl: Workload, perm):
@@ -367,6 +414,7 @@ def permute_batch(wl: Workload, perm):
         slot_mapping=None if wl.slot_mapping is None else wl.slot_mapping[p].contiguous(),
         k_new=None if wl.k_new is None else wl.k_new[p].contiguous(),
         v_new=None if wl.v_new is None else wl.v_new[p].contiguous(),
+        tree_mask=None if wl.tree_mask is None else wl.tree_mask[p].contiguous(),
         meta=dict({k: v for k, v in wl.meta.items() if k != "allocator"},
                   batch_perm=p.tolist()))
 
