@@ -262,6 +262,66 @@ def append_quant_bench(P, torch, W, steps):
             "GBps": round(nbytes / us / 1e3, 1)}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def multi_query_bench(P, torch, W, name, steps):
+    """paged_multi_query_attn on a multi-query workload (chunked prefill: 256 causal
+    positions per sequence; speculative tree verify: 64 candidates per sequence), interleaved
+    pool, two pool copies used in turn, launches back to back between two events.  FLOPs =
+    for every query row, 4 * head_dim per visible token (q.K and P.V, multiply-add = 2)."""
+    wl = W.generate(name, poison=False)
+    c = wl.cfg
+    dev = torch.device("cuda:0")
+    nb, h = wl.k_cache.shape[:2]
+    tile = wl.k_cache[0, 0].numel()
+    pools = []
+    for _ in range(2):
+        comb = torch.empty((nb, h, 2, tile), dtype=wl.k_cache.dtype, device=dev)
+        comb[:, :, 0] = wl.k_cache.reshape(nb, h, tile).to(dev)
+        comb[:, :, 1] = wl.v_cache.reshape(nb, h, tile).to(dev)
+        pools.append((comb, comb.data_ptr() + tile * comb.element_size()))
+    dims = P.make_dims(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                       wl.block_tables.shape[1], nb, c.q_dtype, c.kv_dtype,
+                       kv_tile_stride=2 * tile)
+    q, tables, lens = wl.q.to(dev), wl.block_tables.to(dev), wl.seq_lens.to(dev)
+    words = None if wl.tree_mask is None else W.tree_mask_words(wl.tree_mask).to(dev)
+    out = torch.empty((c.batch, c.num_q_pos, c.num_q_heads, c.head_dim), device=dev)
+    sm = float(np.float32(c.sm_scale))
+
+    def launch(i):
+        kc, vc = pools[i % 2]
+        P.paged_multi_query_attn(dims, c.num_q_pos, q, kc, vc, None, None, tables, lens, sm, out,
+                                 None, words)
+    for i in range(3):
+        launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    e0.record()
+    for i in range(steps):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nq = c.num_q_pos
+    vis = 0
+    for b, L in enumerate(wl.seq_lens.tolist()):
+        for i in range(nq):
+            if wl.tree_mask is None:
+                vis += max(0, L - nq + 1 + i)
+            else:
+                vis += max(0, L - nq) + int(wl.tree_mask[b, i].sum())
+    flops = vis * c.num_q_heads * 4 * c.head_dim
+    tflops = flops / us / 1e6
+    del pools
+    torch.cuda.empty_cache()
+    return {"batch": c.batch, "num_q_pos": nq, "tree": wl.tree_mask is not None,
+            "flops": flops, "kv_bytes": wl.kv_bytes(), "us_per_launch": round(us, 2),
+            "TFLOPs": round(tflops, 1),
+            "frac_of_bf16_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kv_GBps": round(wl.kv_bytes() / us / 1e3, 1)}
+
+
 def summarize(wl, wall, steps, attn):
     kv = wl.kv_bytes()
     us_step = wall / steps * 1e6
@@ -434,7 +494,7 @@ def trace_summary(args, trace_dir):
     # the attention kernels start a new workload whenever their instantiation changes or
     # a run of calls ends with a copy (the next workload's uploads)
     groups, cur, last = [], None, None
-    copies, quants = [], []
+    copies, quants, rows_k = [], [], {}
     for n, s0, e in rows:
         k = short(n)
         if "kv_copy_blocks" in k:
@@ -442,6 +502,9 @@ def trace_summary(args, trace_dir):
             continue
         if "kv_append_quant" in k:
             quants.append((e - s0) / 1000)
+            continue
+        if "paged_attn_rows_kernel" in k:
+            rows_k.setdefault(k, []).append((e - s0) / 1000)
             continue
         if "copyBuffer" in k or "elementwise" in k or "fill" in k.lower():
             last = "copy"
@@ -479,6 +542,9 @@ def trace_summary(args, trace_dir):
         v = quants[3:]      # 3 warm-up launches
         lines.append(f"| llama3_8b int8 cache | `kv_append_quant` 64 tokens x 8 heads | {len(v)} | "
                      f"{np.mean(v):.2f} | {np.median(v):.2f} |")
+    for (label, (k, v)) in zip(("prefill_chunk", "tree_verify"), rows_k.items()):
+        v = v[3:]       # 3 warm-up launches
+        lines.append(f"| {label} | `{k}` | {len(v)} | {np.mean(v):.2f} | {np.median(v):.2f} |")
     out = os.path.join(ROOT, "profiles", f"{args.path}_{args.layout}_kernel_trace.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -534,6 +600,8 @@ def main():
 
         others["kv_copy_blocks"] = copy_blocks_bench(P, torch, W, min(args.steps, 40))
         others["kv_append_quant"] = append_quant_bench(P, torch, W, min(args.steps, 40))
+        for name in ("prefill_chunk", "tree_verify"):
+            others[name] = multi_query_bench(P, torch, W, name, min(args.steps, 20))
 
     achieved = res["attn_kernel_GBps"]
     kernel = KERNEL_NAME[args.path]

@@ -198,6 +198,34 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
               void* k_out, void* v_out, void* stream);
 
 /*
+ * paged_multi_query_attn -- num_q_pos query positions per sequence against its paged
+ * cache: chunked prefill (guide section 4.1: a long prompt's prefill cut into chunks that
+ * run beside decode steps) and speculative candidate trees (guide section 3.3).  The last
+ * num_q_pos = nq tokens of each sequence (seq_lens counts them; their K and V are already
+ * in the cache) are the query positions.
+ *   tree_mask == NULL: causal rows, query i sees tokens t <= L - nq + i (as
+ *                paged_verify_attn), within the sliding window if dims sets one.
+ *   tree_mask != NULL: query i sees every token t < L - nq and candidate j (token
+ *                L - nq + j) iff bit j % 32 of word j / 32 of its mask row is set (for a
+ *                tree: i itself and its ancestors).  nq <= 128 and no sliding window,
+ *                else PA_ERR_DIMS.
+ *   q          device [B][nq][Hq][d] in q_dtype
+ *   tree_mask  device int32 [B][nq][ceil(nq / 32)] bit rows, or NULL
+ *   out        device fp32 [B][nq][Hq][d]; out_lse device fp32 [B][nq][Hq] (natural log)
+ *              or NULL.  A row that sees nothing gets 0 and lse -inf.
+ *   other arguments as paged_verify_attn.
+ * Each wave owns 32 query rows of a (sequence, KV head) (rows = nq * Hq / Hkv) and reads
+ * every block they may see, the four waves of a workgroup sharing the blocks through the
+ * caches: meant for rows >= 32.  Decode and short verify are faster through
+ * paged_attn_balanced.
+ */
+int paged_multi_query_attn(const pa_dims* dims, int32_t num_q_pos, const void* q,
+                           const void* k_cache, const void* v_cache, const float* k_scale,
+                           const float* v_scale, const int32_t* block_tables,
+                           const int32_t* seq_lens, const int32_t* tree_mask, float sm_scale,
+                           float* out, float* out_lse, void* stream);
+
+/*
  * kv_append_quant -- append new tokens to an int8 or fp8 cache (lecture 10's symmetric int8
  * rule, zero point 0; in-depth guide section 5.2: per-head scales for KV caches, FP8 KV
  * caches).  A (block, KV head) keeps one fp32 scale over its live tokens: int8 scale =

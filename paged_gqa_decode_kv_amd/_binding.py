@@ -58,6 +58,7 @@ def _load(path=_LIB_PATH):
         "paged_decode_step": [D, P, P, P, P, P, P, P, F32, I32, P, ctypes.c_size_t, P, P, P],
         "kv_copy_blocks": [D, P, I32, P, P, P, P, P],
         "kv_append_quant": [D, P, P, P, P, I32, I32, P, P, P, P, P, P, P],
+        "paged_multi_query_attn": [D, I32, P, P, P, P, P, P, P, P, F32, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -184,6 +185,15 @@ def kv_append_quant(dims, k_new, v_new, slot_mapping, stage_rows, num_tokens, k_
         ctypes.byref(dims), _p(k_new), _p(v_new), _p(slot_mapping), _p(stage_rows), num_tokens,
         k_stage.shape[0], _p(k_stage), _p(v_stage), _p(k_cache), _p(v_cache), _p(k_scale),
         _p(v_scale), _stream(stream)))
+
+
+def paged_multi_query_attn(dims, num_q_pos, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                           seq_lens, sm_scale, out, out_lse=None, tree_mask=None, stream=None):
+    """tree_mask: int32 bit rows [B][nq][ceil(nq/32)] (workloads.tree_mask_words) or None."""
+    _check("paged_multi_query_attn", lib.paged_multi_query_attn(
+        ctypes.byref(dims), num_q_pos, _p(q), _p(k_cache), _p(v_cache), _p(k_scale), _p(v_scale),
+        _p(block_tables), _p(seq_lens), _p(tree_mask), ctypes.c_float(sm_scale), _p(out),
+        _p(out_lse), _stream(stream)))
 
 
 def kv_copy_blocks(dims, block_pairs, num_pairs, k_cache, v_cache, k_scale=None, v_scale=None,

@@ -265,6 +265,29 @@ int kv_copy_blocks(const pa_dims* dims, const int32_t* block_pairs, int32_t num_
                                 scaled8(dims->kv_dtype) ? v_scale : nullptr, stream);
 }
 
+int paged_multi_query_attn(const pa_dims* dims, int32_t num_q_pos, const void* q,
+                           const void* k_cache, const void* v_cache, const float* k_scale,
+                           const float* v_scale, const int32_t* block_tables,
+                           const int32_t* seq_lens, const int32_t* tree_mask, float sm_scale,
+                           float* out, float* out_lse, void* stream) {
+  int st = check_attn_inputs(dims, q, k_cache, v_cache, k_scale, v_scale, block_tables, seq_lens);
+  if (st != PA_OK) return st;
+  if (num_q_pos < 1) return PA_ERR_DIMS;
+  if (!out) return PA_ERR_NULL;
+  if (!aligned16(out)) return PA_ERR_ALIGN;
+  if (tree_mask != nullptr && (num_q_pos > pa::kMaxTreeNodes || dims->sliding_window > 0))
+    return PA_ERR_DIMS;
+  if ((int64_t)num_q_pos * (dims->num_q_heads / dims->num_kv_heads) > INT_MAX / 2)
+    return PA_ERR_DIMS;
+  pa::AttnArgs a = make_args(dims, num_q_pos, q, k_cache, v_cache, k_scale, v_scale,
+                             block_tables, seq_lens, sm_scale);
+  a.out = out;
+  a.ws_out_lse = out_lse;
+  a.tree_mask = tree_mask;
+  a.mask_words = (num_q_pos + 31) / 32;
+  return pa::launch_rows(a, dims->q_dtype, dims->kv_dtype, stream);
+}
+
 int paged_attn_balanced_workgroups(const pa_dims* dims, int32_t num_q_pos) {
   int st = check_balanced(dims, num_q_pos, 1);
   if (st != PA_OK) return st;

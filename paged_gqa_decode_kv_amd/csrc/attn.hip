@@ -438,6 +438,14 @@ template <int D> struct Scaled8<Fp8Kv<D>> { static constexpr bool value = true; 
 // Where a unit writes its rows.
 enum OutMode { kDirect = 0, kSplit = 1, kBalanced = 2 };
 
+// Candidate visibility of a wave's query rows (multi-query rows with a tree mask): the
+// mask words of each of the lane's NT rows and the position of the first candidate.
+template <int NT>
+struct TreeRows {
+  uint32_t w[NT][4];
+  int base;
+};
+
 // Running online-softmax state of one wave's query rows (a tile of 16 * NT rows) over
 // the blocks it has consumed: the output accumulators (O^T layout), and per row the
 // running max (log2 domain, equal in the four lanes of a row) and this lane's share of the
@@ -466,11 +474,13 @@ struct Rows {
   // (lim_min is the smallest limit over the wave's rows, lo_max the largest start: a
   // sliding window's); tokens >= hi are past the sequence end and their V may be poisoned.  sc = softmax scale * log2(e) (times the block's K scale for int8);
   // vs = the block's V scale (int8).
-  // SW: a sliding window is in force (the lower bounds are tested at all).
-  template <bool SW>
+  // SW: a sliding window is in force (the lower bounds are tested at all).  TREE: the
+  // tokens from tr.base on are candidates, each visible to a row only if its bit in the
+  // row's mask words is set.
+  template <bool SW, bool TREE = false>
   __device__ __forceinline__ void update(const typename KV::Q* qop, const int* lim, int lim_min,
-                                         const int* lo, int lo_max, int hi,
-                                         typename KV::K& kk, typename KV::V& vv,
+                                         const int* lo, int lo_max, const TreeRows<NT>& tr,
+                                         int hi, typename KV::K& kk, typename KV::V& vv,
                                          int tok0, float sc, float vs, int grp) {
     float vfac = 1.f;
     if constexpr (kScaled) {
@@ -502,6 +512,14 @@ struct Rows {
         if (need_mask) {
           const int t = tok0 + 4 * grp + e;
           if (t >= lim[nt] || (SW && t < lo[nt])) x = -INFINITY;
+          if constexpr (TREE) {
+            const int j = t - tr.base;
+            if (j >= 0) {
+              const uint32_t wd = j < 32 ? tr.w[nt][0]
+                                         : (j < 64 ? tr.w[nt][1] : (j < 96 ? tr.w[nt][2] : tr.w[nt][3]));
+              if (((wd >> (j & 31)) & 1u) == 0u) x = -INFINITY;
+            }
+          }
         }
         sv[e] = x;
       }
@@ -553,10 +571,13 @@ __device__ __forceinline__ int window_start(int lam, int window) {
 // Query rows of row tile rg for KV head g of sequence b: the MFMA B operand of each 16-row
 // tile and the visible range of this lane's row (tokens [lo, lim); lim capped at hi).
 // Returns the smallest limit over the tile's rows; lo_max receives the largest start.
-template <class KV, int D, int NT, bool SW>
+// TREE: every row may see tokens < L, the candidates [L - nq, L) subject to the row's mask
+// words (loaded into tr); the returned limit is then the first candidate, from which on
+// blocks need the per-token test.
+template <class KV, int D, int NT, bool SW, bool TREE = false>
 __device__ __forceinline__ int load_rows(const AttnArgs& a, int b, int g, int rg, int L, int hi,
                                          typename KV::Q* qop, int* lim, int* lo, int& lo_max,
-                                         int row16, int grp) {
+                                         TreeRows<NT>& tr, int row16, int grp) {
   const int row_base = rg * 16 * NT;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -568,8 +589,22 @@ __device__ __forceinline__ int load_rows(const AttnArgs& a, int b, int g, int rg
     KV::load_q(qop[nt], static_cast<const uint8_t*>(a.q) + qoff * KV::kQElem, valid, grp);
     int lam = valid ? L - a.num_q_pos + 1 + i : L;
     lam = lam < 0 ? 0 : lam;
+    if constexpr (TREE) {
+      lam = L;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        tr.w[nt][k] = valid && k < a.mask_words
+                          ? (uint32_t)a.tree_mask[((int64_t)b * a.num_q_pos + i) * a.mask_words + k]
+                          : 0u;
+    }
     lim[nt] = lam < hi ? lam : hi;
     lo[nt] = SW ? window_start(lam, a.window) : 0;
+  }
+  if constexpr (TREE) {
+    tr.base = L - a.num_q_pos;
+    const int first = tr.base < 0 ? 0 : tr.base;
+    lo_max = 0;
+    return first < hi ? first : hi;
   }
   lo_max = 0;
   if constexpr (SW) {  // the tile's last row has the largest start
@@ -628,26 +663,31 @@ __device__ __forceinline__ void write_rows(const AttnArgs& a, const Rows<KV, D, 
 // `slot` is the partition index (split mode).  SW: a sliding window is in force (each row
 // also has a first visible token).  Every wave of the workgroup must call this together
 // (it contains barriers).
-template <class KV, int D, int NT, int W, int NBUF, bool SW>
+template <class KV, int D, int NT, int W, int NBUF, bool SW, bool TREE = false>
 __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int b, int g, int rg,
                                             int L, int lo, int hi, int64_t slot) {
   constexpr int ND = D / 16;
   constexpr bool kScaled = Scaled8<KV>::value;
   constexpr int kStage = 64;  // table entries staged in LDS per wave
+  // W > 1: the workgroup's W waves share the unit's rows and take interleaved blocks.
+  // W == 1: each wave of the workgroup (up to 4) is a unit of its own, with its own rows.
+  constexpr int kSlots = W > 1 ? W : 4;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wb = W > 1 ? w : 0;  // this wave's place in the block interleave
   const int row16 = lane & 15;
   const int grp = lane >> 4;
 
   const int jb = lo / kBlockTokens;
   const int je = (hi + kBlockTokens - 1) / kBlockTokens;
-  // this wave's blocks: jb + w + W * k for k in [0, nk)
-  const int nk = je - jb - w > 0 ? (je - jb - w + W - 1) / W : 0;
+  // this wave's blocks: jb + wb + W * k for k in [0, nk)
+  const int nk = je - jb - wb > 0 ? (je - jb - wb + W - 1) / W : 0;
 
   typename KV::Q qop[NT];
   int lim[NT], lo_row[NT], lo_max;
-  const int lim_min = load_rows<KV, D, NT, SW>(a, b, g, rg, L, hi, qop, lim, lo_row, lo_max,
-                                               row16, grp);
+  TreeRows<NT> tr;
+  const int lim_min = load_rows<KV, D, NT, SW, TREE>(a, b, g, rg, L, hi, qop, lim, lo_row,
+                                                     lo_max, tr, row16, grp);
 
   const int64_t tile_bytes = a.tile_stride;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache);
@@ -657,14 +697,14 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   // ---- per-wave LDS staging of block-table entries (and int8 scales) -------------------
   // Lane i fetches the entry of this wave's block k0 + i; the loop then reads them back
   // from LDS, so no dependent HBM load sits between consecutive tile loads.
-  __shared__ int s_tbl[W][kStage];
-  __shared__ float s_ks[W][kScaled ? kStage : 1];
-  __shared__ float s_vs[W][kScaled ? kStage : 1];
+  __shared__ int s_tbl[kSlots][kStage];
+  __shared__ float s_ks[kSlots][kScaled ? kStage : 1];
+  __shared__ float s_vs[kSlots][kScaled ? kStage : 1];
   auto stage = [&](int k0) {
     const int k = k0 + lane;
     int ph = -1;
     if (k < nk) {
-      ph = table[jb + w + W * k];
+      ph = table[jb + wb + W * k];
       if (ph < 0 || (int64_t)ph >= a.num_blocks) ph = -1;
     }
     s_tbl[w][lane] = ph;
@@ -722,8 +762,8 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   };
   auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, const Slot& sl) {
     if (sl.ph < 0) return;
-    const int tok0 = (jb + w + W * kidx) * kBlockTokens;
-    st.template update<SW>(qop, lim, lim_min, lo_row, lo_max, hi, kk, vv, tok0,
+    const int tok0 = (jb + wb + W * kidx) * kBlockTokens;
+    st.template update<SW, TREE>(qop, lim, lim_min, lo_row, lo_max, tr, hi, kk, vv, tok0,
               a.scale_log2 * (kScaled ? sl.ks : 1.f), sl.vs, grp);
   };
 
@@ -792,7 +832,8 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
     __syncthreads();
     if (w != 0) return;
   }
-  write_rows<KV, D, NT>(a, st, mode, b, g, rg, slot, nullptr, row16, grp);
+  write_rows<KV, D, NT>(a, st, mode, b, g, rg, slot, mode == kDirect ? a.ws_out_lse : nullptr,
+                        row16, grp);
 }
 
 __device__ __forceinline__ int clamp_len(int L, int max_blocks) {
@@ -847,6 +888,35 @@ void paged_attn_kernel(AttnArgs a) {
     if (hi < lo) hi = lo;  // lo is a multiple of 16 here, so the unit reads no block
   }
   attend_unit<KV, D, NT, W, NBUF, SW>(a, a.split ? kSplit : kDirect, b, g, rg, L, lo, hi, p);
+}
+
+// Multi-query rows (chunked prefill, speculative trees): one wave per 16 * NT query rows of a
+// (sequence, KV head), reading every block those rows may see.  The four waves of a
+// workgroup take consecutive row tiles of the same (sequence, KV head) and consecutive
+// workgroups the next ones, on the same XCD, so the waves that stream the same blocks run
+// side by side and share them through L1 and L2.  No wave waits for another.
+template <class KV, int D, int NT, int NBUF, bool SW, bool TREE>
+__global__ __launch_bounds__(kWave * 4) __attribute__((amdgpu_waves_per_eu(WavesPerEU<KV, NT>::value)))
+void paged_attn_rows_kernel(AttnArgs a) {
+  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
+  const int wgs = (nrg + 3) / 4;  // workgroups per (sequence, KV head)
+  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * wgs;
+  const int64_t u = xcd_logical_id();
+  if (u >= units) return;
+  const int wr = (int)(u % wgs);
+  const int64_t bg = u / wgs;
+  const int g = (int)(bg % a.num_kv_heads);
+  const int b = (int)(bg / a.num_kv_heads);
+  const int rg = wr * 4 + (int)(threadIdx.x / kWave);
+  if (rg >= nrg) return;
+  const int L = clamp_len(a.seq_lens[b], a.max_blocks);
+  int lo = 0;
+  if (SW) {  // the tile's first row has the earliest window
+    int lam0 = L - a.num_q_pos + 1 + (rg * 16 * NT) / a.group;
+    lam0 = lam0 < 0 ? 0 : lam0;
+    lo = window_start(lam0, a.window) / kBlockTokens * kBlockTokens;
+  }
+  attend_unit<KV, D, NT, 1, NBUF, SW, TREE>(a, kDirect, b, g, rg, L, lo, L, 0);
 }
 
 // Balanced mode.  All (segment, block) pairs of the batch are laid out in one flat list --
@@ -1041,6 +1111,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   cur.end = x0;  // nothing consumed yet
   cur.j = -1;
   int L = 0, lim_min = 0, lim[NT], lo_row[NT], lo_max = 0;
+  TreeRows<NT> no_tree;  // (the balanced kernel has causal rows only)
   typename KV::Q qop[NT], qnext[NT];
   int lim_next[NT], lim_min_next = 0, lo_next[NT], lo_max_next = 0;
   typename KV::NewTok tok, tok_next;  // APP: the new token of the current / next segment
@@ -1102,7 +1173,8 @@ void paged_attn_balanced_kernel(AttnArgs a) {
         nxt = sg;
         const int Ls = clamp_len(a.seq_lens[sg.b], a.max_blocks);
         lim_min_next = load_rows<KV, D, NT, SW>(a, sg.b, sg.g, sg.rg, Ls, rows_hi(sg, Ls), qnext,
-                                            lim_next, lo_next, lo_max_next, row16, grp);
+                                                lim_next, lo_next, lo_max_next, no_tree, row16,
+                                                grp);
         if constexpr (APP) {
           const int64_t nrow = ((int64_t)sg.b * a.num_kv_heads + sg.g) * D * KV::kElem;
           KV::load_new(tok_next, static_cast<const uint8_t*>(a.k_new) + nrow,
@@ -1138,7 +1210,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
         // (rare: two segments began within the blocks in flight) load the rows now and
         // wait for them here, so that no later wait has to allow for a pending query load
         lim_min = load_rows<KV, D, NT, SW>(a, cur.b, cur.g, cur.rg, L, hi, qop, lim, lo_row,
-                                           lo_max, row16, grp);
+                                           lo_max, no_tree, row16, grp);
         if constexpr (APP) {
           const int64_t nrow = ((int64_t)cur.b * a.num_kv_heads + cur.g) * D * KV::kElem;
           KV::load_new(tok, static_cast<const uint8_t*>(a.k_new) + nrow,
@@ -1160,8 +1232,8 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     if constexpr (APP) {
       if (new_tok) KV::patch(kk, vv, tok, off, row16, grp);
     }
-    st.template update<SW>(qop, lim, lim_min, lo_row, lo_max, rows_hi(cur, L), kk, vv, tok0,
-              a.scale_log2 * (kScaled ? sl.ks : 1.f), sl.vs, grp);
+    st.template update<SW>(qop, lim, lim_min, lo_row, lo_max, no_tree, rows_hi(cur, L), kk, vv,
+                           tok0, a.scale_log2 * (kScaled ? sl.ks : 1.f), sl.vs, grp);
     if constexpr (APP) {
       if (new_tok && cur.rg == 0) {  // keep the token for the store at the end
         if (napp == kAppCap) drain();
@@ -1215,6 +1287,26 @@ int launch_one(const AttnArgs& a, void* stream) {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+template <class KV, int D, int NBUF>
+int launch_rows_one(const AttnArgs& a, void* stream) {
+  constexpr int NT = 2;
+  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
+  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * ((nrg + 3) / 4);
+  const int64_t grid = (units + 7) / 8 * 8;
+  if (grid > 0x7fffffff) return PA_ERR_DIMS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.tree_mask != nullptr)
+    hipLaunchKernelGGL((paged_attn_rows_kernel<KV, D, NT, NBUF, false, true>), dim3((unsigned)grid),
+                       dim3(kWave * 4), 0, s, a);
+  else if (a.window > 0)
+    hipLaunchKernelGGL((paged_attn_rows_kernel<KV, D, NT, NBUF, true, false>), dim3((unsigned)grid),
+                       dim3(kWave * 4), 0, s, a);
+  else
+    hipLaunchKernelGGL((paged_attn_rows_kernel<KV, D, NT, NBUF, false, false>), dim3((unsigned)grid),
+                       dim3(kWave * 4), 0, s, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 template <class KV, int D, int NT, int W, int NBUF, bool APP>
 int launch_balanced_one(const AttnArgs& a, void* stream) {
   const int64_t grid = ((int64_t)a.num_workgroups + 7) / 8 * 8;
@@ -1258,13 +1350,14 @@ int occupancy_one() {
 #define PA_NBUF_2 2
 #endif
 
-enum Op { kLaunch, kLaunchBalanced, kLaunchBalancedAppend, kOccupancy };
+enum Op { kLaunch, kLaunchBalanced, kLaunchBalancedAppend, kOccupancy, kLaunchRows };
 
 template <template <int> class KVT, int D>
 int dispatch_dim(const AttnArgs& a, Op op, void* stream) {
   constexpr int W = PA_WAVES;
   using KV = KVT<D>;
   constexpr bool kCanAppend = !Scaled8<KV>::value;
+  if (op == kLaunchRows) return launch_rows_one<KV, D, PA_NBUF_2>(a, stream);
   if (a.rows <= 16) {
     if (op == kLaunch) return launch_one<KV, D, 1, W, PA_NBUF_1>(a, stream);
     if (op == kLaunchBalanced) return launch_balanced_one<KV, D, 1, W, PA_NBUF_1, false>(a, stream);
@@ -1300,6 +1393,10 @@ int dispatch(const AttnArgs& a, int q_dtype, int kv_dtype, Op op, void* stream) 
 
 int launch_attention(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream) {
   return dispatch(a, q_dtype, kv_dtype, kLaunch, stream);
+}
+
+int launch_rows(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream) {
+  return dispatch(a, q_dtype, kv_dtype, kLaunchRows, stream);
 }
 
 int balanced_row_tile(int32_t rows) { return rows <= 16 ? 16 : 32; }

@@ -37,12 +37,21 @@ struct AttnArgs {
   // sequence, [B][Hkv][head_dim] in the cache's element type
   const void* k_new;
   const void* v_new;
+  // multi-query rows: candidate visibility bit rows [B][num_q_pos][mask_words] (null =
+  // causal rows)
+  const int32_t* tree_mask;
+  int32_t mask_words;
 };
+
+// most candidates a visibility mask may cover (bit rows of up to 4 words per query row)
+constexpr int kMaxTreeNodes = 128;
 
 // most sequences the balanced mode accepts in one call (its prefix lives in LDS)
 constexpr int kMaxBalancedSeqs = 2048;
 
 int launch_attention(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream);
+// multi-query rows: each wave owns 32 query rows and reads every block they may see
+int launch_rows(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream);
 
 // rows of one partial (16 or 32): the row tile the kernel uses for `rows` query rows
 int balanced_row_tile(int32_t rows);

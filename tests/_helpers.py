@@ -133,6 +133,23 @@ def gpu_decode_step(P, wl, dv, G=0, seq_lens=None):
     return out, out_lse
 
 
+def gpu_multi_query(P, wl, dv, tree=None):
+    """paged_multi_query_attn; tree=None: the workload's own mask if it has one.
+    Returns (out, out_lse)."""
+    import workloads as W
+    c = wl.cfg
+    d = dims_of(P, wl, dv)
+    mask = wl.tree_mask if tree is None else tree
+    words = None if mask is None else W.tree_mask_words(mask).to("cuda:0")
+    out = torch.full((c.batch, c.num_q_pos, c.num_q_heads, c.head_dim), float("nan"),
+                     device="cuda:0")
+    out_lse = torch.full((c.batch, c.num_q_pos, c.num_q_heads), float("nan"), device="cuda:0")
+    P.paged_multi_query_attn(d, c.num_q_pos, dv.q, dv.k_cache, dv.v_cache, dv.k_scale,
+                             dv.v_scale, dv.block_tables, dv.seq_lens,
+                             float(np.float32(wl.sm_scale)), out, out_lse, words)
+    return out, out_lse
+
+
 def oracle_caches(wl, appended=True):
     """Host caches as the oracle sees them (after the step's append, by the oracle's own
     scatter)."""
@@ -142,13 +159,14 @@ def oracle_caches(wl, appended=True):
     return kc, vc
 
 
-def oracle_attention(wl, kc, vc, seq_lens=None, pairs=None):
+def oracle_attention(wl, kc, vc, seq_lens=None, pairs=None, tree_mask=None):
     c = wl.cfg
     lens = wl.seq_lens.numpy() if seq_lens is None else np.asarray(seq_lens)
     return attention.paged_attention(raw(wl.q), c.q_dtype, kc, vc, c.kv_dtype,
                                      wl.block_tables.numpy(), lens, float(np.float32(wl.sm_scale)),
                                      c.num_q_pos, raw(wl.k_scale), raw(wl.v_scale), pairs=pairs,
-                                     window=c.sliding_window)
+                                     window=c.sliding_window,
+                                     tree_mask=None if tree_mask is None else tree_mask.numpy())
 
 
 def max_err(gpu_out, ref, pairs=None, group=None):

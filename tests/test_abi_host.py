@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
               "lse_merge", "paged_attn_balanced", "paged_attn_balanced_merge",
               "paged_attn_balanced_workspace_bytes", "paged_attn_balanced_workgroups",
               "paged_split_workspace_bytes", "kv_gather", "paged_status_string",
-              "paged_decode_step", "kv_copy_blocks", "kv_append_quant"]:
+              "paged_decode_step", "kv_copy_blocks", "kv_append_quant",
+              "paged_multi_query_attn"]:
         assert n in names
 
 
@@ -195,3 +196,19 @@ def test_append_quant_checks():
     assert P.lib.kv_append_quant(ctypes.byref(d8), *args(2, vs=None)) == -1
     # fp8 attention needs the scales like int8
     assert _decode(d8) == -1 and _decode(d8, ks=FAKE, vs=FAKE, out=FAKE + 8) == -9
+
+
+def test_multi_query_checks():
+    f = ctypes.c_void_p(FAKE)
+
+    def call(d, nq, mask=None, out=FAKE):
+        return P.lib.paged_multi_query_attn(ctypes.byref(d), nq, f, f, f, None, None, f, f, mask,
+                                            ctypes.c_float(0.1), ctypes.c_void_p(out) if out else None,
+                                            None, None)
+    d = _dims()
+    assert call(d, 0) == -2
+    assert call(d, 4, out=None) == -1
+    assert call(d, 4, out=FAKE + 4) == -9
+    assert call(d, 129, mask=f) == -2                  # a mask covers at most 128 candidates
+    assert call(_dims(sliding_window=8), 4, mask=f) == -2
+    assert call(_dims(kv_dtype="i8"), 4) == -1         # 8-bit caches need their scales

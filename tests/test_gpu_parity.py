@@ -7,8 +7,8 @@ import torch
 
 import workloads as W
 from oracle import attention, paging, quant
-from _helpers import (TOL, Dev, dims_of, gpu_append, gpu_attention, gpu_decode_step, max_err,
-                      oracle_attention, oracle_caches, raw, say)
+from _helpers import (TOL, Dev, dims_of, gpu_append, gpu_attention, gpu_decode_step,
+                      gpu_multi_query, max_err, oracle_attention, oracle_caches, raw, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -479,6 +479,84 @@ def test_int8_decode_steps_from_empty(P, balanced, kind):
         err = max_err(out, ref)
         say(f"  step {step} lens {lens.tolist()} max abs err {err:.3e}")
         assert err <= TOL[kind]
+
+
+# ---- multi-query rows: chunked prefill and speculative trees --------------------------------
+def _check_multi_query(P, wl, interleave=False, pairs=None):
+    c = wl.cfg
+    say(f"[case] multi-query {c.name} B={c.batch} nq={c.num_q_pos} Hq={c.num_q_heads} "
+        f"Hkv={c.num_kv_heads} d={c.head_dim} kv={c.kv_dtype} tree={wl.tree_mask is not None} "
+        f"window={c.sliding_window} interleave={interleave} seed={wl.meta['seed']}")
+    dv = Dev(wl, interleave)
+    out, out_lse = gpu_multi_query(P, wl, dv)
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches(wl, appended=False)
+    ref, ref_lse = oracle_attention(wl, kc, vc, pairs=pairs, tree_mask=wl.tree_mask)
+    err = max_err(out, ref, pairs, c.group_size)
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[c.kv_dtype]
+    g = out_lse.cpu().numpy()
+    sel = np.isfinite(ref_lse)
+    if pairs is not None:
+        m = np.zeros(ref_lse.shape, bool)
+        for b, kv in pairs:
+            m[b, ..., kv * c.group_size:(kv + 1) * c.group_size] = True
+        sel &= m
+    else:
+        assert np.all(g[ref_lse == -np.inf] == -np.inf)
+    assert np.all(np.abs(g[sel] - ref_lse[sel]) <= 1e-3 * np.maximum(1, np.abs(ref_lse[sel])))
+
+
+MQ_CASES = [
+    ("prefill_chunk", dict(batch=3, num_q_pos=40, length_range=(40, 300), num_q_heads=8,
+                           num_kv_heads=2)),
+    ("prefill_chunk", dict(batch=2, num_q_pos=70, length_range=(1, 200), num_q_heads=4,
+                           num_kv_heads=4, head_dim=64)),                    # L < nq rows
+    ("prefill_chunk", dict(batch=3, num_q_pos=33, length_range=(33, 400), kv_dtype="i8")),
+    ("prefill_chunk", dict(batch=3, num_q_pos=33, length_range=(33, 400), kv_dtype="fp8")),
+    ("prefill_chunk", dict(batch=2, num_q_pos=24, length_range=(30, 300), q_dtype="f32",
+                           kv_dtype="f32", num_q_heads=8, num_kv_heads=1)),
+    ("prefill_chunk", dict(batch=3, num_q_pos=40, length_range=(40, 500), sliding_window=50)),
+    ("tree_verify", dict(batch=4, num_q_pos=20, length_range=(20, 300))),
+    ("tree_verify", dict(batch=3, num_q_pos=128, length_range=(1, 400), head_dim=64,
+                         num_q_heads=4, num_kv_heads=2)),
+    ("tree_verify", dict(batch=3, num_q_pos=64, length_range=(64, 300), kv_dtype="fp8")),
+    ("tree_verify", dict(batch=3, num_q_pos=37, length_range=(30, 300), kv_dtype="i8",
+                         num_q_heads=32, num_kv_heads=1)),
+]
+
+
+@pytest.mark.parametrize("interleave", [False, True])
+@pytest.mark.parametrize("name,kw", MQ_CASES)
+def test_multi_query_small(P, name, kw, interleave):
+    _check_multi_query(P, _small(name, **kw), interleave)
+
+
+def test_multi_query_causal_mask_matches_causal_rows(P):
+    """A lower-triangular candidate mask gives the same result as the causal rows."""
+    wl = _small("prefill_chunk", batch=3, num_q_pos=48, length_range=(48, 300))
+    say("[case] multi-query causal mask")
+    dv = Dev(wl)
+    nq = wl.cfg.num_q_pos
+    causal = torch.tril(torch.ones((nq, nq), dtype=torch.bool)).expand(wl.cfg.batch, nq, nq)
+    a, la = gpu_multi_query(P, wl, dv)
+    b, lb = gpu_multi_query(P, wl, dv, tree=causal.contiguous())
+    torch.cuda.synchronize()
+    assert torch.allclose(a, b, rtol=0, atol=1e-6) and torch.allclose(la, lb, rtol=0, atol=1e-6)
+
+
+def test_full_prefill_chunk(P):
+    wl = W.generate("prefill_chunk")
+    rng = np.random.default_rng(12)
+    pairs = [(int(b), int(g)) for b, g in zip(rng.integers(0, 4, 4), rng.integers(0, 8, 4))]
+    _check_multi_query(P, wl, interleave=True, pairs=pairs)
+
+
+def test_full_tree_verify(P):
+    wl = W.generate("tree_verify")
+    rng = np.random.default_rng(13)
+    pairs = [(int(b), int(g)) for b, g in zip(rng.integers(0, 32, 8), rng.integers(0, 8, 8))]
+    _check_multi_query(P, wl, interleave=True, pairs=pairs)
 
 
 # ---- sliding window ------------------------------------------------------------------
