@@ -214,10 +214,9 @@ int kv_gather(const pa_dims* dims, const void* k_cache, const void* v_cache,
  *   out        device fp32 [B][nq][Hq][d]; out_lse device fp32 [B][nq][Hq] (natural log)
  *              or NULL.  A row that sees nothing gets 0 and lse -inf.
  *   other arguments as paged_verify_attn.
- * Each wave owns 32 query rows of a (sequence, KV head) (rows = nq * Hq / Hkv) and reads
- * every block they may see, the four waves of a workgroup sharing the blocks through the
- * caches: meant for rows >= 32.  Decode and short verify are faster through
- * paged_attn_balanced.
+ * A workgroup owns up to 32 query rows of a (sequence, KV head) (rows = nq * Hq / Hkv), its
+ * four waves taking interleaved blocks of every token those rows may see and merging
+ * through LDS.  Decode and short verify are faster through paged_attn_balanced.
  */
 int paged_multi_query_attn(const pa_dims* dims, int32_t num_q_pos, const void* q,
                            const void* k_cache, const void* v_cache, const float* k_scale,

@@ -285,7 +285,7 @@ int paged_multi_query_attn(const pa_dims* dims, int32_t num_q_pos, const void* q
   a.ws_out_lse = out_lse;
   a.tree_mask = tree_mask;
   a.mask_words = (num_q_pos + 31) / 32;
-  return pa::launch_rows(a, dims->q_dtype, dims->kv_dtype, stream);
+  return pa::launch_multi_query(a, dims->q_dtype, dims->kv_dtype, stream);
 }
 
 int paged_attn_balanced_workgroups(const pa_dims* dims, int32_t num_q_pos) {

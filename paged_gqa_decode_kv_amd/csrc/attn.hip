@@ -669,19 +669,15 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   constexpr int ND = D / 16;
   constexpr bool kScaled = Scaled8<KV>::value;
   constexpr int kStage = 64;  // table entries staged in LDS per wave
-  // W > 1: the workgroup's W waves share the unit's rows and take interleaved blocks.
-  // W == 1: each wave of the workgroup (up to 4) is a unit of its own, with its own rows.
-  constexpr int kSlots = W > 1 ? W : 4;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wb = W > 1 ? w : 0;  // this wave's place in the block interleave
   const int row16 = lane & 15;
   const int grp = lane >> 4;
 
   const int jb = lo / kBlockTokens;
   const int je = (hi + kBlockTokens - 1) / kBlockTokens;
-  // this wave's blocks: jb + wb + W * k for k in [0, nk)
-  const int nk = je - jb - wb > 0 ? (je - jb - wb + W - 1) / W : 0;
+  // this wave's blocks: jb + w + W * k for k in [0, nk)
+  const int nk = je - jb - w > 0 ? (je - jb - w + W - 1) / W : 0;
 
   typename KV::Q qop[NT];
   int lim[NT], lo_row[NT], lo_max;
@@ -697,14 +693,14 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   // ---- per-wave LDS staging of block-table entries (and int8 scales) -------------------
   // Lane i fetches the entry of this wave's block k0 + i; the loop then reads them back
   // from LDS, so no dependent HBM load sits between consecutive tile loads.
-  __shared__ int s_tbl[kSlots][kStage];
-  __shared__ float s_ks[kSlots][kScaled ? kStage : 1];
-  __shared__ float s_vs[kSlots][kScaled ? kStage : 1];
+  __shared__ int s_tbl[W][kStage];
+  __shared__ float s_ks[W][kScaled ? kStage : 1];
+  __shared__ float s_vs[W][kScaled ? kStage : 1];
   auto stage = [&](int k0) {
     const int k = k0 + lane;
     int ph = -1;
     if (k < nk) {
-      ph = table[jb + wb + W * k];
+      ph = table[jb + w + W * k];
       if (ph < 0 || (int64_t)ph >= a.num_blocks) ph = -1;
     }
     s_tbl[w][lane] = ph;
@@ -762,7 +758,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   };
   auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, const Slot& sl) {
     if (sl.ph < 0) return;
-    const int tok0 = (jb + wb + W * kidx) * kBlockTokens;
+    const int tok0 = (jb + w + W * kidx) * kBlockTokens;
     st.template update<SW, TREE>(qop, lim, lim_min, lo_row, lo_max, tr, hi, kk, vv, tok0,
               a.scale_log2 * (kScaled ? sl.ks : 1.f), sl.vs, grp);
   };
@@ -856,7 +852,8 @@ template <class KV, int NT> struct WavesPerEU {
 };
 
 // Direct and split modes: one unit per (KV head, sequence, row group, partition).
-template <class KV, int D, int NT, int W, int NBUF, bool SW>
+// TREE: multi-query rows whose candidates are filtered by a visibility mask (direct mode).
+template <class KV, int D, int NT, int W, int NBUF, bool SW, bool TREE = false>
 __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(WavesPerEU<KV, NT>::value)))
 void paged_attn_kernel(AttnArgs a) {
   const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
@@ -887,36 +884,8 @@ void paged_attn_kernel(AttnArgs a) {
     lo = lo > w0 ? lo : w0;
     if (hi < lo) hi = lo;  // lo is a multiple of 16 here, so the unit reads no block
   }
-  attend_unit<KV, D, NT, W, NBUF, SW>(a, a.split ? kSplit : kDirect, b, g, rg, L, lo, hi, p);
-}
-
-// Multi-query rows (chunked prefill, speculative trees): one wave per 16 * NT query rows of a
-// (sequence, KV head), reading every block those rows may see.  The four waves of a
-// workgroup take consecutive row tiles of the same (sequence, KV head) and consecutive
-// workgroups the next ones, on the same XCD, so the waves that stream the same blocks run
-// side by side and share them through L1 and L2.  No wave waits for another.
-template <class KV, int D, int NT, int NBUF, bool SW, bool TREE>
-__global__ __launch_bounds__(kWave * 4) __attribute__((amdgpu_waves_per_eu(WavesPerEU<KV, NT>::value)))
-void paged_attn_rows_kernel(AttnArgs a) {
-  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
-  const int wgs = (nrg + 3) / 4;  // workgroups per (sequence, KV head)
-  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * wgs;
-  const int64_t u = xcd_logical_id();
-  if (u >= units) return;
-  const int wr = (int)(u % wgs);
-  const int64_t bg = u / wgs;
-  const int g = (int)(bg % a.num_kv_heads);
-  const int b = (int)(bg / a.num_kv_heads);
-  const int rg = wr * 4 + (int)(threadIdx.x / kWave);
-  if (rg >= nrg) return;
-  const int L = clamp_len(a.seq_lens[b], a.max_blocks);
-  int lo = 0;
-  if (SW) {  // the tile's first row has the earliest window
-    int lam0 = L - a.num_q_pos + 1 + (rg * 16 * NT) / a.group;
-    lam0 = lam0 < 0 ? 0 : lam0;
-    lo = window_start(lam0, a.window) / kBlockTokens * kBlockTokens;
-  }
-  attend_unit<KV, D, NT, 1, NBUF, SW, TREE>(a, kDirect, b, g, rg, L, lo, L, 0);
+  attend_unit<KV, D, NT, W, NBUF, SW, TREE>(a, a.split ? kSplit : kDirect, b, g, rg, L, lo, hi,
+                                            p);
 }
 
 // Balanced mode.  All (segment, block) pairs of the batch are laid out in one flat list --
@@ -1287,26 +1256,6 @@ int launch_one(const AttnArgs& a, void* stream) {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-template <class KV, int D, int NBUF>
-int launch_rows_one(const AttnArgs& a, void* stream) {
-  constexpr int NT = 2;
-  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
-  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * ((nrg + 3) / 4);
-  const int64_t grid = (units + 7) / 8 * 8;
-  if (grid > 0x7fffffff) return PA_ERR_DIMS;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.tree_mask != nullptr)
-    hipLaunchKernelGGL((paged_attn_rows_kernel<KV, D, NT, NBUF, false, true>), dim3((unsigned)grid),
-                       dim3(kWave * 4), 0, s, a);
-  else if (a.window > 0)
-    hipLaunchKernelGGL((paged_attn_rows_kernel<KV, D, NT, NBUF, true, false>), dim3((unsigned)grid),
-                       dim3(kWave * 4), 0, s, a);
-  else
-    hipLaunchKernelGGL((paged_attn_rows_kernel<KV, D, NT, NBUF, false, false>), dim3((unsigned)grid),
-                       dim3(kWave * 4), 0, s, a);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
-}
-
 template <class KV, int D, int NT, int W, int NBUF, bool APP>
 int launch_balanced_one(const AttnArgs& a, void* stream) {
   const int64_t grid = ((int64_t)a.num_workgroups + 7) / 8 * 8;
@@ -1350,14 +1299,27 @@ int occupancy_one() {
 #define PA_NBUF_2 2
 #endif
 
-enum Op { kLaunch, kLaunchBalanced, kLaunchBalancedAppend, kOccupancy, kLaunchRows };
+// multi-query rows with a candidate mask: two row tiles per unit
+template <class KV, int D, int NBUF>
+int launch_tree_one(const AttnArgs& a, void* stream) {
+  constexpr int NT = 2, W = PA_WAVES;
+  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
+  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg;
+  const int64_t grid = (units + 7) / 8 * 8;
+  if (grid > 0x7fffffff) return PA_ERR_DIMS;
+  hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, false, true>), dim3((unsigned)grid),
+                     dim3(kWave * W), 0, static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+enum Op { kLaunch, kLaunchBalanced, kLaunchBalancedAppend, kOccupancy, kLaunchTree };
 
 template <template <int> class KVT, int D>
 int dispatch_dim(const AttnArgs& a, Op op, void* stream) {
   constexpr int W = PA_WAVES;
   using KV = KVT<D>;
   constexpr bool kCanAppend = !Scaled8<KV>::value;
-  if (op == kLaunchRows) return launch_rows_one<KV, D, PA_NBUF_2>(a, stream);
+  if (op == kLaunchTree) return launch_tree_one<KV, D, PA_NBUF_2>(a, stream);
   if (a.rows <= 16) {
     if (op == kLaunch) return launch_one<KV, D, 1, W, PA_NBUF_1>(a, stream);
     if (op == kLaunchBalanced) return launch_balanced_one<KV, D, 1, W, PA_NBUF_1, false>(a, stream);
@@ -1395,8 +1357,8 @@ int launch_attention(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream)
   return dispatch(a, q_dtype, kv_dtype, kLaunch, stream);
 }
 
-int launch_rows(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream) {
-  return dispatch(a, q_dtype, kv_dtype, kLaunchRows, stream);
+int launch_multi_query(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream) {
+  return dispatch(a, q_dtype, kv_dtype, a.tree_mask != nullptr ? kLaunchTree : kLaunch, stream);
 }
 
 int balanced_row_tile(int32_t rows) { return rows <= 16 ? 16 : 32; }

@@ -50,8 +50,8 @@ constexpr int kMaxTreeNodes = 128;
 constexpr int kMaxBalancedSeqs = 2048;
 
 int launch_attention(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream);
-// multi-query rows: each wave owns 32 query rows and reads every block they may see
-int launch_rows(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream);
+// multi-query rows (causal, or with a candidate mask in a.tree_mask): direct mode
+int launch_multi_query(const AttnArgs& a, int q_dtype, int kv_dtype, void* stream);
 
 // rows of one partial (16 or 32): the row tile the kernel uses for `rows` query rows
 int balanced_row_tile(int32_t rows);
