@@ -156,6 +156,13 @@ struct Bf16Kv {
         reinterpret_cast<uint16_t*>(dst + 2 * D)[16 * t + row16] = (uint16_t)n.v[t];
     }
   }
+  // P = hi + lo (two bf16 terms, relative error ~2^-17) so that P.V keeps fp32-class
+  // accuracy.  FOLD: both terms go through one 16x16x32 MFMA, whose 32-long inner dimension
+  // holds the lane's 4 tokens twice, against hi then lo (sum_k A B = sum_t v_t (hi_t + lo_t)):
+  // half the MFMA cycles for the compute-bound multi-query rows, at the cost of a duplicated
+  // operand (two more registers, which the register-tight balanced kernels do not have).
+  // Otherwise two 16x16x16 MFMAs.
+  template <bool FOLD = false>
   __device__ static void pv(f32x4* acc, const V& v, f32x4 p, float /*vfac*/) {
     bf16x4 hi, lo;
 #pragma unroll
@@ -163,13 +170,23 @@ struct Bf16Kv {
       hi[e] = (__bf16)p[e];
       lo[e] = (__bf16)(p[e] - (float)hi[e]);
     }
-    const s16x4 h = __builtin_bit_cast(s16x4, hi);
-    const s16x4 l = __builtin_bit_cast(s16x4, lo);
+    if constexpr (FOLD) {
+      const bf16x8 hl = {hi[0], hi[1], hi[2], hi[3], lo[0], lo[1], lo[2], lo[3]};
 #pragma unroll
-    for (int t = 0; t < ND; ++t) {
-      const s16x4 a = __builtin_bit_cast(s16x4, v.v[t]);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, h, acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, l, acc[t], 0, 0, 0);
+      for (int t = 0; t < ND; ++t) {
+        const u32x4 a = {v.v[t].x, v.v[t].y, v.v[t].x, v.v[t].y};
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), hl,
+                                                         acc[t], 0, 0, 0);
+      }
+    } else {
+      const s16x4 h = __builtin_bit_cast(s16x4, hi);
+      const s16x4 l = __builtin_bit_cast(s16x4, lo);
+#pragma unroll
+      for (int t = 0; t < ND; ++t) {
+        const s16x4 a = __builtin_bit_cast(s16x4, v.v[t]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, h, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, l, acc[t], 0, 0, 0);
+      }
     }
   }
 };
@@ -220,6 +237,7 @@ struct F32Kv {
       for (int e = 0; e < 4; ++e)
         if (4 * grp + e >= nvalid) v.v[t][e] = 0.f;
   }
+  template <bool FOLD = false>
   __device__ static void pv(f32x4* acc, const V& v, f32x4 p, float /*vfac*/) {
 #pragma unroll
     for (int t = 0; t < ND; ++t)
@@ -368,6 +386,7 @@ struct I8Kv {
   // p is scaled by vfac = 256 * v_scale(block) / v_ref and rounded once to fp16 (relative
   // error <= 2^-11 per weight, so |error of out| <= 2^-11 * max|V|, inside the int8
   // tolerance); the factor 256 keeps small weights out of the fp16 subnormal range.
+  template <bool FOLD = false>
   __device__ static void pv(f32x4* acc, const VMat& v, f32x4 p, float vfac) {
     f16x4 ph;
 #pragma unroll
@@ -477,7 +496,7 @@ struct Rows {
   // SW: a sliding window is in force (the lower bounds are tested at all).  TREE: the
   // tokens from tr.base on are candidates, each visible to a row only if its bit in the
   // row's mask words is set.
-  template <bool SW, bool TREE = false>
+  template <bool SW, bool TREE = false, bool FOLD = false>
   __device__ __forceinline__ void update(const typename KV::Q* qop, const int* lim, int lim_min,
                                          const int* lo, int lo_max, const TreeRows<NT>& tr,
                                          int hi, typename KV::K& kk, typename KV::V& vv,
@@ -545,7 +564,7 @@ struct Rows {
     if (tok0 + kBlockTokens > hi) KV::mask_v(vv, hi - tok0, grp);
     const auto& vm = KV::v_mat(vv);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) KV::pv(acc[nt], vm, pr[nt], vfac);
+    for (int nt = 0; nt < NT; ++nt) KV::template pv<FOLD>(acc[nt], vm, pr[nt], vfac);
   }
 
   // After the last block: full row sums in every lane of the row; int8 scale undone.
@@ -759,7 +778,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, const Slot& sl) {
     if (sl.ph < 0) return;
     const int tok0 = (jb + w + W * kidx) * kBlockTokens;
-    st.template update<SW, TREE>(qop, lim, lim_min, lo_row, lo_max, tr, hi, kk, vv, tok0,
+    st.template update<SW, TREE, true>(qop, lim, lim_min, lo_row, lo_max, tr, hi, kk, vv, tok0,
               a.scale_log2 * (kScaled ? sl.ks : 1.f), sl.vs, grp);
   };
 
