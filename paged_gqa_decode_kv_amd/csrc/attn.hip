@@ -67,6 +67,7 @@ struct Bf16Kv {
   static constexpr int NK = D / 32;  // 16x16x32 bf16 steps for q.K
   static constexpr int ND = D / 16;  // d tiles of the output
   static constexpr int kElem = 2;
+  static constexpr float kLazy = 8.f;  // weights below 2^8: far inside fp32 and bf16 range
   static constexpr int kQElem = 2;
   struct Q { bf16x8 v[NK]; };
   struct K { u32x4 v[NK]; };
@@ -197,6 +198,7 @@ struct F32Kv {
   static constexpr int ND = D / 16;
   static constexpr int kElem = 4;
   static constexpr int kQElem = 4;
+  static constexpr float kLazy = 8.f;
   struct Q { f32x4 v[NU]; };
   struct K { f32x4 v[NU]; };
   struct V { f32x4 v[ND]; };
@@ -292,6 +294,8 @@ struct I8Kv {
   static constexpr int ND = D / 16;
   static constexpr int kElem = 1;
   static constexpr int kQElem = 2;
+  // weights below 2^3: times the V-scale factor (at most 4096) they stay inside fp16
+  static constexpr float kLazy = 3.f;
   struct Q { f16x8 v[2 * NH]; };
   struct K { u32x4 v[NH]; };
   struct V { uint32_t v[ND]; };
@@ -520,7 +524,7 @@ struct Rows {
     // (one uniform test: blocks inside every row's range skip the per-token masks)
     const bool need_mask = tok0 + kBlockTokens > lim_min || (SW && tok0 < lo_max);
     f32x4 pr[NT];
-    float alpha[NT];
+    float bmax[NT];
     const auto& km = KV::k_mat(kk);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -543,23 +547,33 @@ struct Rows {
         sv[e] = x;
       }
       float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      bm = wave_max_across_groups(bm);
-      const float mn = fmaxf(m[nt], bm);
-      const float mu = (mn == -INFINITY) ? 0.f : mn;
-      alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - mu);
-      m[nt] = mn;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pr[nt][e] = __builtin_amdgcn_exp2f(sv[e] - mu);
-      l[nt] = l[nt] * alpha[nt] + ((pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]));
+      bmax[nt] = wave_max_across_groups(bm);
+      pr[nt] = sv;
     }
-    bool rescale = false;
+    // Lazy reference: a row's reference m moves only when a score of the block exceeds it
+    // by more than KV::kLazy (log2 units), so the weights exp2(s - m) stay below 2^kLazy
+    // and most blocks skip the rescale of the accumulators.  Softmax does not depend on
+    // the reference, so the result is the same up to rounding.
+    bool move = false;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) rescale |= (alpha[nt] != 1.f);
-    if (__any(rescale)) {
+    for (int nt = 0; nt < NT; ++nt) move |= bmax[nt] > m[nt] + KV::kLazy;
+    if (__any(move)) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt) {
+        const float mn = fmaxf(m[nt], bmax[nt]);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[nt] - mn);
+        m[nt] = mn;
+        l[nt] *= alpha;
 #pragma unroll
-        for (int t = 0; t < ND; ++t) acc[nt][t] *= alpha[nt];
+        for (int t = 0; t < ND; ++t) acc[nt][t] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mu = m[nt] == -INFINITY ? 0.f : m[nt];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pr[nt][e] = __builtin_amdgcn_exp2f(pr[nt][e] - mu);
+      l[nt] += (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
     }
     if (tok0 + kBlockTokens > hi) KV::mask_v(vv, hi - tok0, grp);
     const auto& vm = KV::v_mat(vv);
