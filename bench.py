@@ -503,7 +503,7 @@ def trace_summary(args, trace_dir):
         if "kv_append_quant" in k:
             quants.append((e - s0) / 1000)
             continue
-        if "paged_attn_rows_kernel" in k:
+        if k.startswith("paged_attn_kernel"):       # the multi-query rows (direct kernel)
             rows_k.setdefault(k, []).append((e - s0) / 1000)
             continue
         if "copyBuffer" in k or "elementwise" in k or "fill" in k.lower():
