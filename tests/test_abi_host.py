@@ -212,3 +212,17 @@ def test_multi_query_checks():
     assert call(d, 129, mask=f) == -2                  # a mask covers at most 128 candidates
     assert call(_dims(sliding_window=8), 4, mask=f) == -2
     assert call(_dims(kv_dtype="i8"), 4) == -1         # 8-bit caches need their scales
+
+
+def test_grid_limits_are_checked_before_any_launch():
+    """Sizes whose grid would not fit the launch limits fail on the host (no HIP call)."""
+    f = ctypes.c_void_p(FAKE)
+    d = _dims(num_kv_heads=8, num_q_heads=8)
+    # 2^31 - 1 pairs x 16 pieces per pair
+    assert P.lib.kv_copy_blocks(ctypes.byref(d), f, 2 ** 31 - 1, f, f, None, None, None) == -2
+    d8 = _dims(kv_dtype="i8", num_kv_heads=8, num_q_heads=8)
+    assert P.lib.kv_append_quant(ctypes.byref(d8), f, f, f, f, 2 ** 31 - 1, 4, f, f, f, f, f, f,
+                                 None) == -2
+    big = _dims(num_q_heads=64, num_kv_heads=1)
+    assert P.lib.paged_multi_query_attn(ctypes.byref(big), 2 ** 30, f, f, f, None, None, f, f, None,
+                                        ctypes.c_float(0.1), f, None, None) == -2
