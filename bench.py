@@ -338,6 +338,15 @@ def summarize(wl, wall, steps, attn):
     }
 
 
+def _blas_threads():
+    """Threads numpy's BLAS may use (the oracle's matrix-vector products)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return int(os.environ.get("OMP_NUM_THREADS", "1"))
+
+
 def cpu_baseline(wl, seconds):
     """The fp64 oracle, as it stands, run on the host over the same workload: whole
     passes over all (sequence, KV head) pairs, repeated until about `seconds` of host time
@@ -372,18 +381,83 @@ def cpu_baseline(wl, seconds):
             if done:
                 break
     dt = time.perf_counter() - t0
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
     npairs = c.batch * c.num_kv_heads
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas,
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
             "kind": "oracle",
             "sample": f"{pairs_done} (sequence, KV head) pairs ({pairs_done / npairs:.2f} passes "
                       f"over the {npairs} of {c.name}, seed {wl.meta['seed']}), fp64 numpy, "
                       f"{dt:.1f} s",
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_oracle_others(W, seconds=3.0):
+    """The oracle beside the other measured paths, each on a bounded sample for about
+    `seconds` of host time, in the unit the GPU line reports: attention workloads in GB/s
+    of KV (window, fp8) or TFLOP/s (multi-query rows) over whole (sequence, KV head)
+    pairs; the block copy in GB/s moved; the quantising append in tokens x heads / s."""
+    import torch
+    from oracle import attention, paging, quant
+
+    def raw(x):
+        if x is None:
+            return None
+        return x.view(torch.int16).numpy() if x.dtype == torch.bfloat16 else x.numpy()
+
+    def timed(fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn(n)
+            n += 1
+            if time.perf_counter() - t0 > seconds:
+                return n, time.perf_counter() - t0
+
+    res = {}
+    for name in ("mistral_7b_window", "llama3_8b_fp8", "prefill_chunk", "tree_verify"):
+        wl = W.generate(W.scaled(name, append=False), poison=False)
+        c = wl.cfg
+        pairs = [(b, g) for b in range(c.batch) for g in range(c.num_kv_heads)]
+        tm = None if wl.tree_mask is None else wl.tree_mask.numpy()
+        kc, vc = raw(wl.k_cache), raw(wl.v_cache)
+        args = (raw(wl.q), c.q_dtype, kc, vc, c.kv_dtype, wl.block_tables.numpy(),
+                wl.seq_lens.numpy(), float(np.float32(c.sm_scale)), c.num_q_pos,
+                raw(wl.k_scale), raw(wl.v_scale))
+        n, dt = timed(lambda i: attention.paged_attention(*args, pairs=[pairs[i % len(pairs)]],
+                                                          window=c.sliding_window, tree_mask=tm))
+        done = [pairs[i % len(pairs)] for i in range(n)]
+        if c.num_q_pos == 1:
+            per = wl.kv_bytes() / len(pairs)
+            res[name] = {"value": round(n * per / dt / 1e9, 4), "unit": "GB/s"}
+        else:
+            vis = 0
+            for b, _ in done:
+                L = int(wl.seq_lens[b])
+                for i in range(c.num_q_pos):
+                    vis += (max(0, L - c.num_q_pos + 1 + i) if tm is None
+                            else max(0, L - c.num_q_pos) + int(tm[b, i].sum()))
+            flops = vis * c.group_size * 4 * c.head_dim
+            res[name] = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s"}
+        res[name]["sample"] = f"{n} (sequence, KV head) pairs of {name}, {dt:.1f} s"
+    wl = W.generate(W.scaled("llama3_8b", append=False), poison=False, spare_blocks=4096)
+    pairs = W.copy_pairs(wl, 2048, seed=3).numpy()
+    kc, vc = raw(wl.k_cache), raw(wl.v_cache)
+    n, dt = timed(lambda i: paging.copy_blocks(kc, vc, pairs))
+    moved = 2048 * wl.cfg.num_kv_heads * 2 * wl.k_cache[0, 0].numel() * 2 * 2
+    res["kv_copy_blocks"] = {"value": round(n * moved / dt / 1e9, 4), "unit": "GB/s",
+                             "sample": f"{n} copies of 2048 blocks, {dt:.1f} s"}
+    h, d, T = 8, 128, 64
+    gen = torch.Generator().manual_seed(7)
+    kn = torch.randn((T, h, d), generator=gen).to(torch.bfloat16)
+    st = torch.randn((T, h, 16, d), generator=gen).to(torch.bfloat16)
+    nb = 128
+    cache = (np.zeros((nb, h, d // 16, 16, 16), np.int8), np.zeros((nb, h, d, 16), np.int8),
+             np.zeros((nb, h), np.float32), np.zeros((nb, h), np.float32), raw(st), raw(st))
+    slots = np.arange(T) * 16 + (np.arange(T) * 7) % 16
+    n, dt = timed(lambda i: quant.append_quant(*cache, raw(kn), raw(kn), slots, np.arange(T)))
+    res["kv_append_quant"] = {"value": round(n * T * h / dt, 1), "unit": "token-heads/s",
+                              "sample": f"{n} calls of {T} tokens x {h} heads, {dt:.1f} s"}
+    for v in res.values():
+        v.update(kind="oracle", cores=_blas_threads())
+    return res
 
 
 KERNEL_SOURCES = ["paged_gqa_decode_kv_amd/csrc/attn.hip", "paged_gqa_decode_kv_amd/csrc/pa_common.hpp"]
@@ -639,6 +713,8 @@ def main():
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        if not args.no_others:
+            line["cpu_oracle_others"] = cpu_oracle_others(W)
     print(json.dumps(line), flush=True)
 
 
