@@ -524,18 +524,45 @@ struct Rows {
     // (one uniform test: blocks inside every row's range skip the per-token masks)
     const bool need_mask = tok0 + kBlockTokens > lim_min || (SW && tok0 < lo_max);
     f32x4 pr[NT];
-    float bmax[NT];
     const auto& km = KV::k_mat(kk);
+    // Lazy reference: a row's reference m moves only when a score of the block exceeds it
+    // by more than KV::kLazy (log2 units), so the weights exp2(s - m) stay below 2^kLazy
+    // and most blocks skip the rescale of the accumulators.  Softmax does not depend on
+    // the reference, so the result is the same up to rounding.
+    bool move = false;
+    if constexpr (!TREE) {
+      // Blocks inside every row's range skip the per-token tests (four instructions a
+      // score) in a wave-wide branch, and whether the block moves any reference is decided
+      // from each lane's own 4 scores, so the row maximum is reduced across the row's four
+      // lanes only when it does.
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 sv = KV::qk(km, qop[nt]);
+      for (int nt = 0; nt < NT; ++nt) pr[nt] = KV::qk(km, qop[nt]) * sc;
+      if (__any(need_mask)) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = sv[e] * sc;
-        if (need_mask) {
-          const int t = tok0 + 4 * grp + e;
-          if (t >= lim[nt] || (SW && t < lo[nt])) x = -INFINITY;
-          if constexpr (TREE) {
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = tok0 + 4 * grp + e;
+            if (t >= lim[nt] || (SW && t < lo[nt])) pr[nt][e] = -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float lm = fmaxf(fmaxf(pr[nt][0], pr[nt][1]), fmaxf(pr[nt][2], pr[nt][3]));
+        move |= lm > m[nt] + KV::kLazy;
+      }
+    } else {
+      // candidate masks: every row's maximum is reduced on every block (measured faster
+      // here than the branch above: the mask words keep the register budget tight)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 sv = KV::qk(km, qop[nt]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = sv[e] * sc;
+          if (need_mask) {
+            const int t = tok0 + 4 * grp + e;
+            if (t >= lim[nt]) x = -INFINITY;
             const int j = t - tr.base;
             if (j >= 0) {
               const uint32_t wd = j < 32 ? tr.w[nt][0]
@@ -543,24 +570,18 @@ struct Rows {
               if (((wd >> (j & 31)) & 1u) == 0u) x = -INFINITY;
             }
           }
+          sv[e] = x;
         }
-        sv[e] = x;
+        pr[nt] = sv;
+        const float bm = wave_max_across_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+        move |= bm > m[nt] + KV::kLazy;
       }
-      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      bmax[nt] = wave_max_across_groups(bm);
-      pr[nt] = sv;
     }
-    // Lazy reference: a row's reference m moves only when a score of the block exceeds it
-    // by more than KV::kLazy (log2 units), so the weights exp2(s - m) stay below 2^kLazy
-    // and most blocks skip the rescale of the accumulators.  Softmax does not depend on
-    // the reference, so the result is the same up to rounding.
-    bool move = false;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) move |= bmax[nt] > m[nt] + KV::kLazy;
     if (__any(move)) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float mn = fmaxf(m[nt], bmax[nt]);
+        const float lm = fmaxf(fmaxf(pr[nt][0], pr[nt][1]), fmaxf(pr[nt][2], pr[nt][3]));
+        const float mn = fmaxf(m[nt], wave_max_across_groups(lm));
         const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[nt] - mn);
         m[nt] = mn;
         l[nt] *= alpha;
