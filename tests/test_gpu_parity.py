@@ -104,14 +104,15 @@ def test_kv_append_skips_negative_and_out_of_pool_slots(P):
 
 
 @pytest.mark.parametrize("interleave", [False, True])
-@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b", "verify_int8"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b", "verify_int8", "llama3_8b_fp8"])
 def test_kv_gather_bit_exact(P, name, interleave):
     wl = _small(name, batch=5, length_range=(0, 333), append=False)
     say(f"[case] gather {name} interleave={interleave}")
     dv = Dev(wl, interleave)
     c = wl.cfg
     maxL = int(wl.seq_lens.max()) + 3
-    fill = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}[c.kv_dtype]
+    fill = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8,
+            "fp8": torch.uint8}[c.kv_dtype]
     k_out = torch.full((c.batch, c.num_kv_heads, maxL, c.head_dim), 7, dtype=fill, device="cuda:0")
     v_out = k_out.clone()
     P.kv_gather(dims_of(P, wl, dv), dv.k_cache, dv.v_cache, dv.block_tables, dv.seq_lens, maxL,
@@ -141,7 +142,7 @@ def _check_pool(dv, kc, vc, ks=None, vs=None):
 
 
 @pytest.mark.parametrize("interleave", [False, True])
-@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b", "verify_int8"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b", "verify_int8", "llama3_8b_fp8"])
 def test_kv_copy_blocks_bit_exact(P, name, interleave):
     wl = _small(name, spare=12, batch=6, length_range=(1, 200), append=False)
     nb = wl.k_cache.shape[0]
