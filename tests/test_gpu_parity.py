@@ -778,6 +778,7 @@ def test_fp8_all_modes(P, name, kw):
 def test_full_llama2_70b_shared_prefix(P):
     wl = W.generate("llama2_70b_prefix")
     _check_decode_step(P, wl, 0)
+    _check_decode_step(P, wl, 0, interleave=True)      # the benchmark's launch
     _check_attention(P, wl)
     _check_attention(P, wl, balanced=0)
     wl2 = W.generate("llama2_70b_prefix", shuffle_batch=True)
@@ -790,9 +791,44 @@ def test_full_long_128k(P):
     _check_attention(P, wl, split=(2048, 64), pairs=pairs)
     _check_attention(P, wl, split=(4096, 8), pairs=pairs[:2])   # last partition absorbs the rest
     _check_attention(P, wl, balanced=0, pairs=pairs)
+    _check_decode_step(P, wl, 0, interleave=True, pairs=pairs)   # the benchmark's launch
 
 
 def test_full_verify_int8(P):
     wl = W.generate("verify_int8")
     _check_attention(P, wl)
     _check_attention(P, wl, balanced=0)
+    _check_attention(P, wl, balanced=0, interleave=True)     # the benchmark's launch
+
+
+def test_full_kv_append_quant_llama3_8b_int8(P):
+    """The benchmark's quantising append: 64 tokens, one per sequence at the end of each
+    Llama-3-8B-shaped sequence, into an int8 pool, whole pool and staging compared."""
+    wl = W.generate(W.scaled("llama3_8b", kv_dtype="i8", append=False), spare_blocks=64)
+    c = wl.cfg
+    alloc = wl.meta["allocator"]
+    slots = torch.tensor([alloc.append_token(b)[0] for b in range(c.batch)], dtype=torch.int64)
+    gen = torch.Generator().manual_seed(7)
+    h, d = c.num_kv_heads, c.head_dim
+    kn = _rand_bf16(gen, (c.batch, h, d))
+    vn = _rand_bf16(gen, (c.batch, h, d))
+    kst = _rand_bf16(gen, (c.batch, h, 16, d))
+    vst = _rand_bf16(gen, (c.batch, h, 16, d))
+    rows = torch.arange(c.batch, dtype=torch.int32)
+    say("[case] append_quant full llama3_8b int8")
+    dims = P.make_dims(c.batch, c.num_q_heads, h, d, wl.block_tables.shape[1], wl.k_cache.shape[0],
+                       "bf16", "i8")
+    dk, dv_, dks, dvs = wl.k_cache.cuda(), wl.v_cache.cuda(), wl.k_scale.cuda(), wl.v_scale.cuda()
+    dkst, dvst = kst.cuda(), vst.cuda()
+    P.kv_append_quant(dims, kn.cuda(), vn.cuda(), slots.cuda(), rows.cuda(), c.batch, dkst, dvst,
+                      dk, dv_, dks, dvs)
+    torch.cuda.synchronize()
+    r = lambda x: x.view(torch.int16).numpy()
+    ok, ov, oks, ovs, okst, ovst = quant.append_quant(
+        wl.k_cache.numpy(), wl.v_cache.numpy(), wl.k_scale.numpy(), wl.v_scale.numpy(), r(kst),
+        r(vst), r(kn), r(vn), slots.numpy(), rows.numpy())
+    assert np.array_equal(dk.cpu().numpy(), ok) and np.array_equal(dv_.cpu().numpy(), ov)
+    # scales bit for bit (the untouched, poisoned entries keep their NaN patterns)
+    assert np.array_equal(dks.cpu().numpy().view(np.uint32), oks.view(np.uint32))
+    assert np.array_equal(dvs.cpu().numpy().view(np.uint32), ovs.view(np.uint32))
+    assert np.array_equal(r(dkst.cpu()), okst) and np.array_equal(r(dvst.cpu()), ovst)
