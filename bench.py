@@ -19,7 +19,7 @@ previous step's KV in the 256 MB Infinity Cache.
 
 Printed: ONE JSON line.  value = algorithmic KV bytes per step / step time (GB/s);
 roofline.achieved = the same bytes / the attention kernel's mean duration, timed with
-HIP events on the stream the kernels run on.  The other workloads (Llama-2-70B shared
+HIP events (no system fence) on the stream the kernels run on.  The other workloads (Llama-2-70B shared
 prefix, 128K context, int8 verify) are timed the same way and reported under "others".
 cpu_baseline times the fp64 oracle on a bounded sample of the same workload.
 
@@ -69,6 +69,57 @@ def parse():
                     help="summarise a rocprofv3 --kernel-trace run of this script (profiles/) "
                          "and exit")
     return ap.parse_args()
+
+
+class HipEvent:
+    """A HIP timing event recorded on the current torch stream (the stream the binding
+    launches on), created with hipEventDisableSystemFence: the record writes a timestamp
+    and no system-scope cache writeback / invalidate, which would otherwise sit between
+    the bracketed kernel and its neighbours (about 2 us per bracket here).  The HIP runtime
+    is the one torch has already loaded (same soname)."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        cls = type(self)
+        if cls._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                    ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        self._c = ctypes
+        self.h = ctypes.c_void_p()
+        rc = cls._hip.hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        import torch
+        stream = self._c.c_void_p(torch.cuda.current_stream().cuda_stream)
+        rc = self._hip.hipEventRecord(self.h, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both complete)."""
+        f = self._c.c_float()
+        rc = self._hip.hipEventElapsedTime(self._c.byref(f), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def __del__(self):
+        try:
+            if self.h:
+                self._hip.hipEventDestroy(self.h)
+        except Exception:       # interpreter shutdown
+            pass
 
 
 class Runner:
@@ -165,7 +216,7 @@ class Runner:
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        evs = {i: [HipEvent() for _ in range(2)]
                for i in range(0, steps, every)}
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -203,7 +254,7 @@ def copy_blocks_bench(P, torch, W, steps):
         for i in range(4):
             P.kv_copy_blocks(dims, sets[i % 2], n, comb, vptr)
         torch.cuda.synchronize()
-        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        e0, e1 = (HipEvent() for _ in range(2))
         e0.record()
         for i in range(steps):
             P.kv_copy_blocks(dims, sets[i % 2], n, comb, vptr)
@@ -246,7 +297,7 @@ def append_quant_bench(P, torch, W, steps):
     for _ in range(3):
         P.kv_append_quant(dims, kn, vn, sl, rows, c.batch, kst, vst, kc, vc, ks, vs)
     torch.cuda.synchronize()
-    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    e0, e1 = (HipEvent() for _ in range(2))
     e0.record()
     for _ in range(steps):
         P.kv_append_quant(dims, kn, vn, sl, rows, c.batch, kst, vst, kc, vc, ks, vs)
@@ -296,7 +347,7 @@ def multi_query_bench(P, torch, W, name, steps):
     for i in range(3):
         launch(i)
     torch.cuda.synchronize()
-    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    e0, e1 = (HipEvent() for _ in range(2))
     e0.record()
     for i in range(steps):
         launch(i)
