@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
 // [w * per, (w + 1) * per), so the waves that wrote a partial for segment j are
 // w = S_j / per .. (S_{j+1} - 1) / per, at partial ids w + j.  A segment inside one slice
 // was written out by the attention kernel and is skipped here; an empty segment gets zeros.
-// One workgroup per segment, one wave per query row of its row tile.
+// One wave per query row of the segment's row tile, in one workgroup per segment (two for
+// row tiles of more than 16 rows: blockIdx.y picks the half).
 template <int D>
 __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int row_tile,
                                                               float* __restrict__ out,
@@ -93,52 +94,62 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
   if (s1 > s0 && w0 == w1) return;   // written by the attention kernel
 
   // Within a row's wave the lanes split into PG groups of D / 4 lanes: each group takes one
-  // piece per step, each lane four dims of it; U steps are in flight at once.
+  // piece per step, each lane four dims of it; U steps are in flight at once.  The pieces'
+  // lse values arrive with their rows, so the maximum is a running one (one round trip for
+  // up to PG * U pieces; a further chunk rescales what is summed so far).
   constexpr int LPR = D / 4;
   constexpr int PG = kWave / LPR;
-  constexpr int U = 8;
+  constexpr int U = 8;   // (16 spills: a 1024-thread workgroup leaves 128 VGPRs a lane)
   const int pg = lane / LPR, dl = lane % LPR;
   const int64_t npc = w1 - w0 + 1;  // pieces (0 for an empty segment)
-  for (int rl = wv; rl < row_tile; rl += nwv) {
+  // workgroup y of the segment takes rows y * nwv .. of its row tile, one per wave
+  for (int rl = blockIdx.y * nwv + wv; rl < row_tile && rl < (int)(blockIdx.y + 1) * nwv;
+       rl += nwv) {
     const int r = rg * row_tile + rl;
     if (r >= a.rows) break;
     const int i = r / a.group;
     const int h = g * a.group + r % a.group;
     const int64_t orow = (int64_t)(b * a.num_q_pos + i) * a.num_q_heads + h;
-    // max lse over the pieces: lanes take pieces, then a wave reduction
     float M = -INFINITY;
-    for (int64_t q = lane; q < npc; q += kWave)
-      M = fmaxf(M, a.ws_lse[(w0 + q + j) * row_tile + rl]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    if (M != -INFINITY) {
-      for (int64_t q0 = 0; q0 < npc; q0 += PG * U) {
-        float lp[U];
-        f32x4 v[U];
+    for (int64_t q0 = 0; q0 < npc; q0 += PG * U) {
+      float lp[U];
+      f32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t q = q0 + u * PG + pg;
-          const int64_t pid = w0 + (q < npc ? q : 0) + j;
-          lp[u] = a.ws_lse[pid * row_tile + rl];
-          v[u] = *reinterpret_cast<const f32x4*>(a.ws_out + (pid * row_tile + rl) * D + 4 * dl);
-          if (q >= npc) lp[u] = -INFINITY;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float wq = lp[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lp[u] - M) * kLog2e);
-          if (wq != 0.f) acc += wq * v[u];
-          wsum += wq;
-        }
+      for (int u = 0; u < U; ++u) {
+        const int64_t q = q0 + u * PG + pg;
+        const int64_t pid = w0 + (q < npc ? q : 0) + j;
+        lp[u] = a.ws_lse[pid * row_tile + rl];
+        v[u] = *reinterpret_cast<const f32x4*>(a.ws_out + (pid * row_tile + rl) * D + 4 * dl);
+        if (q >= npc) lp[u] = -INFINITY;
       }
-      // the PG groups' partial sums
+      // the chunk's maximum over all PG groups
+      float mc = M;
 #pragma unroll
-      for (int off = LPR; off < kWave; off <<= 1) {
+      for (int u = 0; u < U; ++u) mc = fmaxf(mc, lp[u]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off);
-        wsum += __shfl_xor(wsum, off);
+      for (int off = LPR; off < kWave; off <<= 1) mc = fmaxf(mc, __shfl_xor(mc, off));
+      if (mc == -INFINITY) continue;
+      if (M != -INFINITY && mc != M) {
+        const float c = __builtin_amdgcn_exp2f((M - mc) * kLog2e);
+        acc *= c;
+        wsum *= c;
       }
+      M = mc;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wq = lp[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lp[u] - M) * kLog2e);
+        if (wq != 0.f) acc += wq * v[u];
+        wsum += wq;
+      }
+    }
+    // the PG groups' partial sums (all groups share M)
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off);
+      wsum += __shfl_xor(wsum, off);
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     if (pg == 0) *reinterpret_cast<f32x4*>(out + orow * D + 4 * dl) = acc * inv;
@@ -154,15 +165,17 @@ int launch_balanced_merge(const AttnArgs& a, float* out, float* out_lse, void* s
   const int nrg = (a.rows + rt - 1) / rt;
   const int64_t grid = (int64_t)a.num_kv_heads * nrg * a.num_seqs;
   if (grid > 0x7fffffff) return PA_ERR_DIMS;
+  // one wave per row of the tile: up to 16 per workgroup, more rows over more workgroups
   const int rows_in_tile = a.rows < rt ? a.rows : rt;
-  const int waves = rows_in_tile < 16 ? rows_in_tile : 16;
+  const int ysplit = (rows_in_tile + 15) / 16;
+  const int waves = (rows_in_tile + ysplit - 1) / ysplit;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.head_dim == 64)
-    hipLaunchKernelGGL(balanced_merge_kernel<64>, dim3((unsigned)grid), dim3(kWave * waves), 0, s,
-                       a, rt, out, out_lse);
+    hipLaunchKernelGGL(balanced_merge_kernel<64>, dim3((unsigned)grid, ysplit),
+                       dim3(kWave * waves), 0, s, a, rt, out, out_lse);
   else
-    hipLaunchKernelGGL(balanced_merge_kernel<128>, dim3((unsigned)grid), dim3(kWave * waves), 0, s,
-                       a, rt, out, out_lse);
+    hipLaunchKernelGGL(balanced_merge_kernel<128>, dim3((unsigned)grid, ysplit),
+                       dim3(kWave * waves), 0, s, a, rt, out, out_lse);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
