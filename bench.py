@@ -722,7 +722,7 @@ def main():
             w2 = W.generate(name, poison=False)
             copies = 1 if name == "long_128k" else 2
             r2 = Runner(P, w2, "step", None, copies=copies, layout=args.layout)
-            s = summarize(w2, *_m(r2, args, steps=min(args.steps, 20), warmup=3))
+            s = summarize(w2, *_m(r2, args, steps=min(args.steps, 40), warmup=3))
             s["path"] = r2.path
             s["layout"] = args.layout
             s["workgroups"] = r2.G
