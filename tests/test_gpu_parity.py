@@ -832,3 +832,63 @@ def test_full_kv_append_quant_llama3_8b_int8(P):
     assert np.array_equal(dks.cpu().numpy().view(np.uint32), oks.view(np.uint32))
     assert np.array_equal(dvs.cpu().numpy().view(np.uint32), ovs.view(np.uint32))
     assert np.array_equal(r(dkst.cpu()), okst) and np.array_equal(r(dvst.cpu()), ovst)
+
+
+# ---- HIP graph capture: the calls allocate nothing, set no memory and never sync --------
+def test_decode_step_and_split_in_a_graph(P):
+    """The decode step + merge and the split + lse_merge pair captured in one HIP graph
+    (torch.cuda.graph, the library launching on the capturing stream) and replayed several
+    times with eager work and synchronisations between replays: every replay must give
+    exactly the eager results (the kernels are deterministic) and the same cache."""
+    wl = _small("llama3_8b", batch=6, length_range=(1, 700))
+    c = wl.cfg
+    say(f"[case] graph replay {c.name} B={c.batch} seed={wl.meta['seed']}")
+    dv = Dev(wl, interleave=True)
+    d = dims_of(P, wl, dv)
+    sm = float(np.float32(wl.sm_scale))
+    G = P.paged_attn_balanced_workgroups(d, 1)
+    ws = torch.empty((P.paged_attn_balanced_workspace_bytes(d, 1, G),), dtype=torch.uint8,
+                     device="cuda:0")
+    pt, maxp = 128, 8
+    po = torch.empty((c.batch, c.num_q_heads, maxp, c.head_dim), device="cuda:0")
+    pl = torch.empty((c.batch, c.num_q_heads, maxp), device="cuda:0")
+    out1 = torch.empty((c.batch, 1, c.num_q_heads, c.head_dim), device="cuda:0")
+    lse1 = torch.empty((c.batch, 1, c.num_q_heads), device="cuda:0")
+    out2 = torch.empty((c.batch, c.num_q_heads, c.head_dim), device="cuda:0")
+
+    def work():
+        P.paged_decode_step(d, dv.q, dv.k_new, dv.v_new, dv.k_cache, dv.v_cache,
+                            dv.block_tables, dv.seq_lens, sm, G, ws, out1, lse1)
+        P.paged_attn_balanced_merge(d, 1, G, ws, out1, lse1)
+        P.paged_decode_attn_split(d, dv.q, dv.k_cache, dv.v_cache, None, None, dv.block_tables,
+                                  dv.seq_lens, sm, pt, maxp, po, pl)
+        P.lse_merge(d, po, pl, dv.seq_lens, pt, maxp, out2)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()                                   # eager, on the stream to be captured
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref1, ref_lse, ref2 = out1.clone(), lse1.clone(), out2.clone()
+    cache = dv.comb.clone()
+    kc, vc = oracle_caches(wl)
+    ref, _ = oracle_attention(wl, kc, vc)
+    assert max_err(out1, ref) <= TOL[c.kv_dtype] and max_err(out2[:, None], ref) <= TOL[c.kv_dtype]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(4):
+        for t in (out1, lse1, out2):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}")
+        assert torch.equal(out1, ref1) and torch.equal(out2, ref2)
+        assert torch.equal(lse1, ref_lse)
+        assert torch.equal(dv.comb.view(torch.int16), cache.view(torch.int16))  # (NaN poison)
+        with torch.cuda.stream(side):            # eager work between the replays
+            work()
+        torch.cuda.synchronize()
