@@ -613,9 +613,10 @@ def pmc_summary(args, fetch_dir, write_dir):
 
 
 def trace_summary(args, trace_dir):
-    """Markdown summary of a rocprofv3 --kernel-trace run of this script: per kernel and
-    workload, calls and mean / median duration (the first 3 calls of each workload, the
-    warm-up, are left out)."""
+    """Markdown summary of a rocprofv3 --kernel-trace run of this script, given the same
+    --steps / --warmup / --no-cpu / --path / --layout as the traced run: per kernel and
+    workload, calls and mean / median duration (the warm-up calls are left out: --warmup
+    of them for the main workload, 3 for the others)."""
     import re
     import sqlite3
     db = sqlite3.connect(os.path.join(trace_dir, "run_results.db"))
@@ -651,17 +652,20 @@ def trace_summary(args, trace_dir):
             cur.setdefault(k, []).append((e - s0) / 1000)
     names = ["llama3_8b", "llama2_70b_prefix", "long_128k", "verify_int8", "mistral_7b_window",
              "llama3_8b_fp8"]
+    run_flags = (f"--steps {args.steps} --warmup {args.warmup}" +
+                 (" --no-cpu" if args.no_cpu else "") +
+                 f" --path {args.path} --layout {args.layout}")
     lines = [f"# rocprofv3 kernel trace: bench.py --path {args.path} --layout {args.layout}", "",
              "Command (MI355X, one GPU):", "",
              f"    rocprofv3 --kernel-trace --stats -d {trace_dir} -o run -- python bench.py "
-             f"--steps 20 --warmup 3 --no-cpu --path {args.path} --layout {args.layout}",
-             f"    python bench.py --path {args.path} --layout {args.layout} --trace-summary "
-             f"{trace_dir}", "",
+             f"{run_flags}",
+             f"    python bench.py {run_flags} --trace-summary {trace_dir}", "",
              f"Kernel sources sha: {kernel_source_hash()}", "",
              "| workload | kernel | calls | mean us | median us |", "|---|---|---|---|---|"]
     for name, g in zip(names, groups):
+        skip = args.warmup if name == names[0] else 3
         for k, v in g.items():
-            v = v[3:] if len(v) > 3 else v
+            v = v[skip:] if len(v) > skip else v
             lines.append(f"| {name} | `{k}` | {len(v)} | {np.mean(v):.2f} | {np.median(v):.2f} |")
     if copies:
         # copy_blocks_bench: 4 warm-up + n bulk launches (2048 pairs), then the same for
