@@ -892,3 +892,57 @@ def test_decode_step_and_split_in_a_graph(P):
         with torch.cuda.stream(side):            # eager work between the replays
             work()
         torch.cuda.synchronize()
+
+
+# ---- seeded random sweep over shapes, element types and modes ---------------------------
+def _sweep_case(i):
+    """Case i of the sweep: a seeded draw of the shape, element type, lengths, query
+    positions, window, layout and launch mode."""
+    rng = np.random.default_rng(7000 + i)
+    kv = str(rng.choice(["f32", "bf16", "bf16", "i8", "fp8"]))
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([1, 2, 4, 8]))
+    nq = int(rng.choice([1, 1, 1, 2, 5, 6, 9]))
+    batch = int(rng.integers(1, 9))
+    lmax = int(rng.choice([40, 300, 700]))
+    eight = kv in ("i8", "fp8")
+    append = nq == 1 and not eight and bool(rng.integers(0, 2))
+    window = int(rng.choice([0, 0, 0, 17, 64, 200]))
+    tree = nq > 1 and window == 0 and bool(rng.integers(0, 2))
+    kw = dict(batch=batch, num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=d,
+              q_dtype="f32" if kv == "f32" else "bf16", kv_dtype=kv, num_q_pos=nq,
+              length_range=(1 if append else 0, lmax), append=append,
+              sliding_window=window, tree=tree, seed=7000 + i)
+    modes = ["direct", "balanced"]
+    if nq == 1:
+        modes.append("split")
+        if append:
+            modes.append("step")
+    if nq > 1:
+        modes.append("multi")
+    mode = modes[int(rng.integers(0, len(modes)))]
+    if tree:
+        mode = "multi"
+    if append and rng.integers(0, 2):
+        mode = "step"
+    return kw, mode, bool(rng.integers(0, 2)), int(rng.choice([0, 1, 3, 7, 40]))
+
+
+@pytest.mark.parametrize("i", range(128))
+def test_random_sweep(P, i):
+    kw, mode, interleave, G = _sweep_case(i)
+    wl = _small("llama3_8b", **kw)
+    say(f"[sweep {i}] mode={mode} G={G} {kw}")
+    if mode == "step":
+        _check_decode_step(P, wl, G, interleave=interleave)
+    elif mode == "multi":
+        _check_multi_query(P, wl, interleave=interleave)
+    elif mode == "split":
+        pt = int(np.random.default_rng(i).choice([16, 64, 256]))
+        _check_attention(P, wl, split=(pt, 1 + int(wl.seq_lens.max()) // pt),
+                         interleave=interleave)
+    elif mode == "balanced":
+        _check_attention(P, wl, balanced=G, interleave=interleave)
+    else:
+        _check_attention(P, wl, interleave=interleave)
