@@ -226,3 +226,31 @@ def test_grid_limits_are_checked_before_any_launch():
     big = _dims(num_q_heads=64, num_kv_heads=1)
     assert P.lib.paged_multi_query_attn(ctypes.byref(big), 2 ** 30, f, f, f, None, None, f, f, None,
                                         ctypes.c_float(0.1), f, None, None) == -2
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    """The ABI header is usable from C: a C99 translation unit that includes it, takes the
+    address of every declared function and fills a pa_dims compiles warning-free."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = declared_functions()
+    src = ["#include \"paged_attn.h\"", "#include <stddef.h>", "",
+           "int main(void) {",
+           "  pa_dims d = {0};",
+           "  d.block_size = 16;",
+           "  typedef void (*fn_t)(void);",
+           "  const fn_t fns[] = {"]
+    src += [f"    (fn_t)&{n}," for n in names]
+    src += ["  };", "  return (int)(sizeof fns / sizeof fns[0]) - (int)d.block_size + 16 - "
+            f"{len(names)};", "}"]
+    c_file = tmp_path / "abi.c"
+    c_file.write_text("\n".join(src) + "\n")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    for std in ("c99", "c11"):
+        r = subprocess.run([cc, f"-std={std}", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                            "-I", inc, "-c", str(c_file), "-o", str(tmp_path / "abi.o")],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
