@@ -341,7 +341,8 @@ size_t paged_attn_balanced_workspace_bytes(const pa_dims* dims, int32_t num_q_po
                                            int32_t num_workgroups);
 
 /* A good num_workgroups for paged_attn_balanced on the current HIP device: one per compute
- * unit for up to 16 query rows per KV head (nq * Hq / Hkv), two per unit for more (fewer if
+ * unit for up to 16 query rows per KV head (nq * Hq / Hkv) over an fp32 or bf16 cache, two
+ * per unit for more rows or an 8-bit cache (fewer if
  * the kernel cannot keep two resident); a negative PA_ERR_* code on failure.  This call
  * queries the device (HIP calls), unlike the argument checks. */
 int paged_attn_balanced_workgroups(const pa_dims* dims, int32_t num_q_pos);

@@ -1336,8 +1336,10 @@ int occupancy_one() {
   // Measured on MI355X (Llama-3-8B decode, shared-prefix and 128K bf16 workloads; int8
   // verify): with one row tile a wave per SIMD (one workgroup per unit) streams fastest
   // (108 / 66 / 326 us against 110 / 73 / 347 us with two per unit); with two row tiles
-  // (more compute per byte) two workgroups per unit hide it better (85 against 95 us).
-  const int want = NT == 1 ? 1 : 2;
+  // (more compute per byte) two workgroups per unit hide it better (85 against 95 us), and
+  // so they do for 8-bit tiles (half the bytes per block and an fp16 decode of each:
+  // Llama-3-8B fp8 decode 48.4 against 49.7 us).
+  const int want = NT == 1 && !Scaled8<KV>::value ? 1 : 2;
   const int64_t n = (int64_t)cus * (per_cu >= want ? want : (per_cu > 0 ? per_cu : 1));
   return n > 0x7fffffff ? 0x7fffffff : (int)n;
 }
