@@ -66,6 +66,9 @@ def parse():
                     help="first run a 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into the traffic file and exit")
+    ap.add_argument("--counter-summary", metavar="PMC_DIR",
+                    help="summarise one rocprofv3 --pmc run of this script (profiles/) and "
+                         "exit")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
                     help="summarise a rocprofv3 --kernel-trace run of this script (profiles/) "
                          "and exit")
@@ -691,6 +694,82 @@ def trace_summary(args, trace_dir):
     print("\n".join(lines))
 
 
+def counter_summary(args, pmc_dir):
+    """Markdown summary of one rocprofv3 --pmc run of this script (given the same --steps /
+    --warmup / --no-cpu as the profiled run): per workload and kernel, the mean per-dispatch
+    value of every counter collected (warm-up dispatches left out as in trace_summary), and
+    per-wave ratios where the counters allow them."""
+    import re
+    import sqlite3
+    db = sqlite3.connect(os.path.join(pmc_dir, "run_results.db"))
+    rows = db.execute("select dispatch_id, kernel_name, counter_name, value from "
+                      "counters_collection order by dispatch_id").fetchall()
+    disp = {}
+    for did, name, cname, val in rows:
+        d = disp.setdefault(did, {"name": name, "c": {}})
+        d["c"][cname] = d["c"].get(cname, 0.0) + float(val)
+
+    def short(n):
+        n = n.replace("(anonymous namespace)::", "")
+        m = re.match(r"void pa::(\w+)<(.*)>\(", n)
+        return f"{m.group(1)}<{m.group(2)}>" if m else n.split("(")[0][:60]
+    names = ["llama3_8b", "llama2_70b_prefix", "long_128k", "verify_int8", "mistral_7b_window",
+             "llama3_8b_fp8"]
+    groups, cur, last, extra = [], None, None, {}
+    for did in sorted(disp):
+        k = short(disp[did]["name"])
+        c = disp[did]["c"]
+        if "kv_copy_blocks" in k or "kv_append_quant" in k or k.startswith("paged_attn_kernel"):
+            extra.setdefault(k, []).append(c)
+            continue
+        if "copyBuffer" in k or "elementwise" in k or "fill" in k.lower():
+            last = "copy"
+            continue
+        if k.startswith("paged_attn") and (cur is None or last == "copy"):
+            cur = {}
+            groups.append(cur)
+        last = k
+        if cur is not None:
+            cur.setdefault(k, []).append(c)
+    counters = sorted({cn for d in disp.values() for cn in d["c"]})
+    run_flags = (f"--steps {args.steps} --warmup {args.warmup}" +
+                 (" --no-cpu" if args.no_cpu else "") +
+                 f" --path {args.path} --layout {args.layout}")
+    lines = [f"# rocprofv3 counters: bench.py {run_flags}", "",
+             "Command (MI355X, one GPU):", "",
+             f"    rocprofv3 --pmc {' '.join(counters)} -d {pmc_dir} -o run -- python "
+             f"bench.py {run_flags}",
+             f"    python bench.py {run_flags} --counter-summary {pmc_dir}", "",
+             f"Kernel sources sha: {kernel_source_hash()}", "",
+             "Mean per dispatch (counters summed over the device). Derived, where collected: "
+             "VALU/wave = SQ_INSTS_VALU / SQ_WAVES, MFMA/wave = SQ_INSTS_MFMA / SQ_WAVES, "
+             "VALU issue = SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES.", "",
+             "| workload | kernel | dispatches | " + " | ".join(counters) +
+             " | VALU/wave | MFMA/wave | VALU issue |",
+             "|---|---|---|" + "---|" * (len(counters) + 3)]
+
+    def row(label, k, cs):
+        mean = {cn: float(np.mean([c.get(cn, 0.0) for c in cs])) for cn in counters}
+        w = mean.get("SQ_WAVES", 0.0)
+        der = [f"{mean['SQ_INSTS_VALU'] / w:.0f}" if w and "SQ_INSTS_VALU" in mean else "",
+               f"{mean['SQ_INSTS_MFMA'] / w:.0f}" if w and "SQ_INSTS_MFMA" in mean else "",
+               f"{mean['SQ_ACTIVE_INST_VALU'] / mean['SQ_WAVE_CYCLES']:.3f}"
+               if mean.get("SQ_WAVE_CYCLES") and "SQ_ACTIVE_INST_VALU" in mean else ""]
+        lines.append(f"| {label} | `{k}` | {len(cs)} | " +
+                     " | ".join(f"{mean[cn]:.4g}" for cn in counters) + " | " +
+                     " | ".join(der) + " |")
+    for name, g in zip(names, groups):
+        skip = args.warmup if name == names[0] else 3
+        for k, cs in g.items():
+            row(name, k, cs[skip:] if len(cs) > skip else cs)
+    for k, cs in extra.items():
+        row("(other)", k, cs[3:] if len(cs) > 3 else cs)
+    out = os.path.join(ROOT, "profiles", "kernel_counters.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -698,6 +777,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args, args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args, args.counter_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path is single-GPU); got --gpus {args.gpus}",
