@@ -66,9 +66,9 @@ def parse():
                     help="first run a 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into the traffic file and exit")
-    ap.add_argument("--counter-summary", metavar="PMC_DIR",
-                    help="summarise one rocprofv3 --pmc run of this script (profiles/) and "
-                         "exit")
+    ap.add_argument("--counter-summary", nargs="+", metavar=("PMC_DIR", "NAME"),
+                    help="summarise one rocprofv3 --pmc run of this script into "
+                         "profiles/NAME.md (default kernel_counters) and exit")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
                     help="summarise a rocprofv3 --kernel-trace run of this script (profiles/) "
                          "and exit")
@@ -694,7 +694,7 @@ def trace_summary(args, trace_dir):
     print("\n".join(lines))
 
 
-def counter_summary(args, pmc_dir):
+def counter_summary(args, pmc_dir, out_name="kernel_counters"):
     """Markdown summary of one rocprofv3 --pmc run of this script (given the same --steps /
     --warmup / --no-cpu as the profiled run): per workload and kernel, the mean per-dispatch
     value of every counter collected (warm-up dispatches left out as in trace_summary), and
@@ -739,7 +739,8 @@ def counter_summary(args, pmc_dir):
              "Command (MI355X, one GPU):", "",
              f"    rocprofv3 --pmc {' '.join(counters)} -d {pmc_dir} -o run -- python "
              f"bench.py {run_flags}",
-             f"    python bench.py {run_flags} --counter-summary {pmc_dir}", "",
+             f"    python bench.py {run_flags} --counter-summary {pmc_dir}"
+             f"{'' if out_name == 'kernel_counters' else ' ' + out_name}", "",
              f"Kernel sources sha: {kernel_source_hash()}", "",
              "Mean per dispatch (counters summed over the device). Derived, where collected: "
              "VALU/wave = SQ_INSTS_VALU / SQ_WAVES, MFMA/wave = SQ_INSTS_MFMA / SQ_WAVES, "
@@ -764,7 +765,7 @@ def counter_summary(args, pmc_dir):
             row(name, k, cs[skip:] if len(cs) > skip else cs)
     for k, cs in extra.items():
         row("(other)", k, cs[3:] if len(cs) > 3 else cs)
-    out = os.path.join(ROOT, "profiles", "kernel_counters.md")
+    out = os.path.join(ROOT, "profiles", f"{out_name}.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -779,7 +780,7 @@ def main():
         trace_summary(args, args.trace_summary)
         return
     if args.counter_summary:
-        counter_summary(args, args.counter_summary)
+        counter_summary(args, *args.counter_summary[:2])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path is single-GPU); got --gpus {args.gpus}",
