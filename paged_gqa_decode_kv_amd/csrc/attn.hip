@@ -717,27 +717,35 @@ __device__ __forceinline__ void write_rows(const AttnArgs& a, const Rows<KV, D, 
 // `slot` is the partition index (split mode).  SW: a sliding window is in force (each row
 // also has a first visible token).  Every wave of the workgroup must call this together
 // (it contains barriers).
-template <class KV, int D, int NT, int W, int NBUF, bool SW, bool TREE = false>
+template <class KV, int D, int NT, int W, int NBUF, bool SW, bool TREE = false, int RG = 1>
 __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int b, int g, int rg,
                                             int L, int lo, int hi, int64_t slot) {
   constexpr int ND = D / 16;
   constexpr bool kScaled = Scaled8<KV>::value;
   constexpr int kStage = 64;  // table entries staged in LDS per wave
+  constexpr int WS = W / RG;  // waves per row tile
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int row16 = lane & 15;
   const int grp = lane >> 4;
+  // RG > 1: the workgroup serves RG row tiles (rg is then the index of that group of
+  // tiles), WS waves each, which read the same blocks side by side (one HBM read of a
+  // block serves them all); a tile past the last one reads nothing but keeps the barriers
+  const int sub = w / WS, wl = w % WS;
+  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
+  const int rt = rg * RG + sub;
+  const bool live = rt < nrg;
 
   const int jb = lo / kBlockTokens;
-  const int je = (hi + kBlockTokens - 1) / kBlockTokens;
-  // this wave's blocks: jb + w + W * k for k in [0, nk)
-  const int nk = je - jb - w > 0 ? (je - jb - w + W - 1) / W : 0;
+  const int je = live ? (hi + kBlockTokens - 1) / kBlockTokens : jb;
+  // this wave's blocks: jb + wl + WS * k for k in [0, nk)
+  const int nk = je - jb - wl > 0 ? (je - jb - wl + WS - 1) / WS : 0;
 
   typename KV::Q qop[NT];
   int lim[NT], lo_row[NT], lo_max;
   TreeRows<NT> tr;
-  const int lim_min = load_rows<KV, D, NT, SW, TREE>(a, b, g, rg, L, hi, qop, lim, lo_row,
-                                                     lo_max, tr, row16, grp);
+  const int lim_min = load_rows<KV, D, NT, SW, TREE>(a, b, g, live ? rt : 0, L, hi, qop, lim,
+                                                     lo_row, lo_max, tr, row16, grp);
 
   const int64_t tile_bytes = a.tile_stride;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache);
@@ -754,7 +762,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
     const int k = k0 + lane;
     int ph = -1;
     if (k < nk) {
-      ph = table[jb + w + W * k];
+      ph = table[jb + wl + WS * k];
       if (ph < 0 || (int64_t)ph >= a.num_blocks) ph = -1;
     }
     s_tbl[w][lane] = ph;
@@ -812,7 +820,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   };
   auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, const Slot& sl) {
     if (sl.ph < 0) return;
-    const int tok0 = (jb + w + W * kidx) * kBlockTokens;
+    const int tok0 = (jb + wl + WS * kidx) * kBlockTokens;
     st.template update<SW, TREE, true>(qop, lim, lim_min, lo_row, lo_max, tr, hi, kk, vv, tok0,
               a.scale_log2 * (kScaled ? sl.ks : 1.f), sl.vs, grp);
   };
@@ -840,49 +848,50 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   }
   st.totals();
 
-  // ---- merge the W waves through LDS (wave 0 finishes) -------------------------------
-  if constexpr (W > 1) {
-    __shared__ float sm_m[W - 1][NT * 16];
-    __shared__ float sm_l[W - 1][NT * 16];
-    __shared__ f32x4 sm_acc[W - 1][NT][ND][kWave];
-    if (w > 0) {
+  // ---- merge the WS waves of each row tile through LDS (its wave 0 finishes) ----------
+  if constexpr (WS > 1) {
+    __shared__ float sm_m[RG][WS - 1][NT * 16];
+    __shared__ float sm_l[RG][WS - 1][NT * 16];
+    __shared__ f32x4 sm_acc[RG][WS - 1][NT][ND][kWave];
+    if (wl > 0) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         if (grp == 0) {
-          sm_m[w - 1][nt * 16 + row16] = st.m[nt];
-          sm_l[w - 1][nt * 16 + row16] = st.l[nt];
+          sm_m[sub][wl - 1][nt * 16 + row16] = st.m[nt];
+          sm_l[sub][wl - 1][nt * 16 + row16] = st.l[nt];
         }
 #pragma unroll
-        for (int t = 0; t < ND; ++t) sm_acc[w - 1][nt][t][lane] = st.acc[nt][t];
+        for (int t = 0; t < ND; ++t) sm_acc[sub][wl - 1][nt][t][lane] = st.acc[nt][t];
       }
     }
     __syncthreads();
-    if (w == 0) {
+    if (wl == 0) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float M = st.m[nt];
 #pragma unroll
-        for (int x = 0; x < W - 1; ++x) M = fmaxf(M, sm_m[x][nt * 16 + row16]);
+        for (int x = 0; x < WS - 1; ++x) M = fmaxf(M, sm_m[sub][x][nt * 16 + row16]);
         const float Mu = (M == -INFINITY) ? 0.f : M;
         const float f0 = __builtin_amdgcn_exp2f(st.m[nt] - Mu);
         float lsum = st.l[nt] * f0;
 #pragma unroll
         for (int t = 0; t < ND; ++t) st.acc[nt][t] *= f0;
 #pragma unroll
-        for (int x = 0; x < W - 1; ++x) {
-          const float fx = __builtin_amdgcn_exp2f(sm_m[x][nt * 16 + row16] - Mu);
-          lsum += sm_l[x][nt * 16 + row16] * fx;
+        for (int x = 0; x < WS - 1; ++x) {
+          const float fx = __builtin_amdgcn_exp2f(sm_m[sub][x][nt * 16 + row16] - Mu);
+          lsum += sm_l[sub][x][nt * 16 + row16] * fx;
 #pragma unroll
-          for (int t = 0; t < ND; ++t) st.acc[nt][t] += sm_acc[x][nt][t][lane] * fx;
+          for (int t = 0; t < ND; ++t) st.acc[nt][t] += sm_acc[sub][x][nt][t][lane] * fx;
         }
         st.m[nt] = M;
         st.l[nt] = lsum;
       }
     }
     __syncthreads();
-    if (w != 0) return;
+    if (wl != 0) return;
   }
-  write_rows<KV, D, NT>(a, st, mode, b, g, rg, slot, mode == kDirect ? a.ws_out_lse : nullptr,
+  if (!live) return;
+  write_rows<KV, D, NT>(a, st, mode, b, g, rt, slot, mode == kDirect ? a.ws_out_lse : nullptr,
                         row16, grp);
 }
 
@@ -907,10 +916,11 @@ template <class KV, int NT> struct WavesPerEU {
 
 // Direct and split modes: one unit per (KV head, sequence, row group, partition).
 // TREE: multi-query rows whose candidates are filtered by a visibility mask (direct mode).
-template <class KV, int D, int NT, int W, int NBUF, bool SW, bool TREE = false>
+// RG > 1: each workgroup serves RG row tiles of its (sequence, KV head) (multi-query rows).
+template <class KV, int D, int NT, int W, int NBUF, bool SW, bool TREE = false, int RG = 1>
 __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(WavesPerEU<KV, NT>::value)))
 void paged_attn_kernel(AttnArgs a) {
-  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
+  const int nrg = (a.rows + 16 * NT * RG - 1) / (16 * NT * RG);  // (groups of) row tiles
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg * a.max_parts;
   const int64_t u = xcd_logical_id();
   if (u >= units) return;
@@ -938,8 +948,8 @@ void paged_attn_kernel(AttnArgs a) {
     lo = lo > w0 ? lo : w0;
     if (hi < lo) hi = lo;  // lo is a multiple of 16 here, so the unit reads no block
   }
-  attend_unit<KV, D, NT, W, NBUF, SW, TREE>(a, a.split ? kSplit : kDirect, b, g, rg, L, lo, hi,
-                                            p);
+  attend_unit<KV, D, NT, W, NBUF, SW, TREE, RG>(a, a.split ? kSplit : kDirect, b, g, rg, L, lo,
+                                                hi, p);
 }
 
 // Balanced mode.  All (segment, block) pairs of the batch are laid out in one flat list --
@@ -1355,16 +1365,21 @@ int occupancy_one() {
 #define PA_NBUF_2 2
 #endif
 
-// multi-query rows with a candidate mask: two row tiles per unit
+// multi-query rows with a candidate mask: two row tiles per wave, PA_TREE_RG such row
+// tiles per workgroup
+#ifndef PA_TREE_RG
+#define PA_TREE_RG 2
+#endif
 template <class KV, int D, int NBUF>
 int launch_tree_one(const AttnArgs& a, void* stream) {
-  constexpr int NT = 2, W = PA_WAVES;
-  const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
+  constexpr int NT = 2, W = PA_WAVES, RG = PA_TREE_RG;
+  const int nrg = (a.rows + 16 * NT * RG - 1) / (16 * NT * RG);
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg;
   const int64_t grid = (units + 7) / 8 * 8;
   if (grid > 0x7fffffff) return PA_ERR_DIMS;
-  hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, false, true>), dim3((unsigned)grid),
-                     dim3(kWave * W), 0, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, false, true, RG>),
+                     dim3((unsigned)grid), dim3(kWave * W), 0, static_cast<hipStream_t>(stream),
+                     a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -543,7 +543,9 @@ def test_multi_query_causal_mask_matches_causal_rows(P):
     a, la = gpu_multi_query(P, wl, dv)
     b, lb = gpu_multi_query(P, wl, dv, tree=causal.contiguous())
     torch.cuda.synchronize()
-    assert torch.allclose(a, b, rtol=0, atol=1e-6) and torch.allclose(la, lb, rtol=0, atol=1e-6)
+    # (the two launches split a row tile's blocks over different numbers of waves, so only
+    # the order of the fp32 sums differs)
+    assert torch.allclose(a, b, rtol=0, atol=2e-5) and torch.allclose(la, lb, rtol=0, atol=2e-5)
 
 
 def test_full_prefill_chunk(P):
