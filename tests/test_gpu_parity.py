@@ -729,6 +729,27 @@ def test_block_relabel_and_batch_order_bit_identical(P):
     assert torch.equal(_bits(out1), _bits(out2))
     assert torch.equal(_bits(out1[bperm]), _bits(out3))
     assert torch.equal(_bits(out1), _bits(out4))
+    # the balanced mode deals logical positions, so a relabelled pool gives the same bits,
+    # and so does a repeat (the merge order is fixed)
+    wlr = W.relabel_blocks(wl, perm)
+    b1, _, l1 = gpu_attention(P, wl, Dev(wl), balanced=0)
+    b2, _, l2 = gpu_attention(P, wlr, Dev(wlr), balanced=0)
+    b3, _, l3 = gpu_attention(P, wl, Dev(wl), balanced=0)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(b1), _bits(b2)) and torch.equal(_bits(b1), _bits(b3))
+    assert torch.equal(_bits(l1), _bits(l2)) and torch.equal(_bits(l1), _bits(l3))
+
+
+def test_multi_query_repeat_bit_identical(P):
+    for name, kw in (("prefill_chunk", dict(batch=2, num_q_pos=40, length_range=(40, 400))),
+                     ("tree_verify", dict(batch=3, num_q_pos=20, length_range=(20, 300)))):
+        wl = _small(name, **kw)
+        say(f"[case] multi-query repeat {name}")
+        dv = Dev(wl)
+        a, la = gpu_multi_query(P, wl, dv)
+        b, lb = gpu_multi_query(P, wl, dv)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(a), _bits(b)) and torch.equal(_bits(la), _bits(lb))
 
 
 def test_split_count_invariance(P):
