@@ -421,6 +421,7 @@ def cpu_baseline(wl, seconds):
     elem = {"f32": 4, "bf16": 2, "i8": 1}[c.kv_dtype]
     pairs_done, nbytes, t_depage = 0, 0, 0.0
     t0 = time.perf_counter()
+    c0 = time.process_time()           # CPU time of all the process's threads
     done = False
     while not done:
         for b in range(c.batch):
@@ -443,9 +444,15 @@ def cpu_baseline(wl, seconds):
                 break
     # t_depage estimates the de-page time of all pairs from every 16th one; the sampled
     # calls themselves (t_depage / 16) were extra work and leave the oracle's time
-    dt = max(time.perf_counter() - t0 - t_depage / 16, 1e-9)
+    wall = time.perf_counter() - t0
+    busy = (time.process_time() - c0) / max(wall, 1e-9)   # threads busy on average
+    dt = max(wall - t_depage / 16, 1e-9)
     npairs = c.batch * c.num_kv_heads
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+    # cores: the threads the oracle kept busy on average (CPU time / wall time), at least
+    # one; blas_threads: the pool numpy's BLAS could use
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s",
+            "cores": max(1, int(round(busy))), "cpu_time_per_wall": round(busy, 2),
+            "blas_threads": _blas_threads(),
             "oracle_ms_per_pass": round(dt / (pairs_done / npairs) * 1e3, 1),
             "depage_share": round(min(1.0, t_depage / dt), 3),
             "kind": "oracle",
@@ -468,13 +475,17 @@ def cpu_oracle_others(W, seconds=3.0):
             return None
         return x.view(torch.int16).numpy() if x.dtype == torch.bfloat16 else x.numpy()
 
+    busy = []   # threads kept busy on average (CPU time / wall time), per timed sample
+
     def timed(fn):
-        n, t0 = 0, time.perf_counter()
+        n, t0, c0 = 0, time.perf_counter(), time.process_time()
         while True:
             fn(n)
             n += 1
             if time.perf_counter() - t0 > seconds:
-                return n, time.perf_counter() - t0
+                wall = time.perf_counter() - t0
+                busy.append((time.process_time() - c0) / wall)
+                return n, wall
 
     res = {}
     for name in ("mistral_7b_window", "llama3_8b_fp8", "prefill_chunk", "tree_verify"):
@@ -520,8 +531,10 @@ def cpu_oracle_others(W, seconds=3.0):
     n, dt = timed(lambda i: quant.append_quant(*cache, raw(kn), raw(kn), slots, np.arange(T)))
     res["kv_append_quant"] = {"value": round(n * T * h / dt, 1), "unit": "token-heads/s",
                               "sample": f"{n} calls of {T} tokens x {h} heads, {dt:.1f} s"}
-    for v in res.values():
-        v.update(kind="oracle", cores=_blas_threads())
+    assert len(busy) == len(res)
+    for v, bz in zip(res.values(), busy):
+        v.update(kind="oracle", cores=max(1, int(round(bz))), cpu_time_per_wall=round(bz, 2),
+                 blas_threads=_blas_threads())
     return res
 
 
