@@ -76,10 +76,10 @@ enum {
   PA_ERR_DTYPE = -3,      /* element-type combination not supported by the call           */
   PA_ERR_HEAD_DIM = -4,   /* head_dim is not 64 or 128                                     */
   PA_ERR_BLOCK_SIZE = -5, /* block_size is not 16                                          */
-  PA_ERR_PARTITION = -6,  /* partition_tokens not a positive multiple of 16, or
-                             max_partitions < 1                                            */
+  PA_ERR_WORKSPACE = -6,  /* workspace smaller than the size query returns, or misaligned  */
   PA_ERR_LAUNCH = -7,     /* a kernel launch failed (or a device query failed)             */
-  PA_ERR_WORKSPACE = -8,  /* workspace smaller than the size query returns, or misaligned  */
+  PA_ERR_PARTITION = -8,  /* partition_tokens not a positive multiple of 16, or
+                             max_partitions < 1                                            */
   PA_ERR_ALIGN = -9       /* q, k_cache, v_cache or out not 16-byte aligned                */
 };
 
@@ -104,7 +104,9 @@ typedef struct pa_dims {
                                  call honours it; kv_append, kv_gather and kv_copy_blocks
                                  ignore it.  < 0 is PA_ERR_DIMS                             */
 } pa_dims;
-/* Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, I8), (BF16, FP8). */
+/* Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, I8), (BF16, FP8).
+ * q may hold any finite value of its type on every cache type (8-bit K codes meet q as
+ * exact bf16 operands); only the scores sm_scale * q . K must stay finite in fp32. */
 
 /*
  * kv_append -- write each new token's K and V into its cache slot.

@@ -16,7 +16,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_a
 PA_F32, PA_BF16, PA_I8, PA_FP8 = 0, 1, 2, 3
 PA_OK = 0
 PA_ERR_NULL, PA_ERR_DIMS, PA_ERR_DTYPE, PA_ERR_HEAD_DIM = -1, -2, -3, -4
-PA_ERR_BLOCK_SIZE, PA_ERR_PARTITION, PA_ERR_LAUNCH, PA_ERR_WORKSPACE = -5, -6, -7, -8
+PA_ERR_BLOCK_SIZE, PA_ERR_WORKSPACE, PA_ERR_LAUNCH, PA_ERR_PARTITION = -5, -6, -7, -8
 PA_ERR_ALIGN = -9
 
 _DTYPE_CODE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8,

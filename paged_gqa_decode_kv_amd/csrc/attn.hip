@@ -20,8 +20,9 @@
 //  * P feeds the bf16 P*V MFMA in two 16-bit pieces (hi + lo) so the product keeps ~16
 //    significant bits of the fp32 probabilities; the int8 path rounds P once to fp16
 //    (11 bits) and the fp32 path uses fp32 MFMA directly.
-//  * int8 K/V are decoded to exact fp16 in registers; the per-(block, head) K scale
-//    multiplies the scores and the V scale is folded into P.
+//  * int8 / fp8 K/V are decoded in registers to exact bf16 (K, beside the bf16 q) and fp16
+//    (V, beside the fp16 weights); the per-(block, head) K scale multiplies the scores and
+//    the V scale is folded into P.
 //  * Direct / split modes: a workgroup of W waves owns one (sequence, KV head, row group,
 //    partition); its waves take interleaved blocks and are merged through LDS at the end
 //    (same LSE identity as the cross-workgroup split).  Balanced mode: every wave streams
@@ -296,24 +297,22 @@ struct I8Kv {
   static constexpr int kQElem = 2;
   // weights below 2^3: times the V-scale factor (at most 4096) they stay inside fp16
   static constexpr float kLazy = 3.f;
-  struct Q { f16x8 v[2 * NH]; };
+  // q stays bf16 (any bf16 value, no narrowing): the codes are decoded to exact bf16 for
+  // the q.K MFMA; only the P.V side uses fp16 operands
+  struct Q { bf16x8 v[2 * NH]; };
   struct K { u32x4 v[NH]; };
   struct V { uint32_t v[ND]; };
 
+  // d index of step 2h + s, element j: 64h + 16 grp + 8s + j
   __device__ static void load_q(Q& q, const void* row, bool valid, int grp) {
     const uint16_t* p = static_cast<const uint16_t*>(row) + 16 * grp;
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        u32x4 x = valid ? *reinterpret_cast<const u32x4*>(p + 64 * h + 8 * s) : u32x4{0, 0, 0, 0};
-        f16x8 f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f[2 * j] = (_Float16)bf16_bits_to_f32(x[j] & 0xFFFFu);
-          f[2 * j + 1] = (_Float16)bf16_bits_to_f32(x[j] >> 16);
-        }
-        q.v[2 * h + s] = f;
+        const u32x4 x =
+            valid ? *reinterpret_cast<const u32x4*>(p + 64 * h + 8 * s) : u32x4{0, 0, 0, 0};
+        q.v[2 * h + s] = __builtin_bit_cast(bf16x8, x);
       }
   }
   __device__ static void load_k(K& k, const void* tile, int lane) {
@@ -352,17 +351,18 @@ struct I8Kv {
       w[3 * TPG + u] = d;
     }
   }
-  // int8 codes decoded once per block to exact fp16 MFMA operands (shared by all row tiles)
-  struct KMat { f16x8 v[2 * NH]; };
+  // int8 codes decoded once per block to exact MFMA operands (shared by all row tiles):
+  // K to bf16 (beside the bf16 q), V to fp16 (beside the fp16 weights)
+  struct KMat { bf16x8 v[2 * NH]; };
   struct VMat { f16x4 v[ND]; };
   __device__ static KMat k_mat(const K& k) {
     KMat m;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const f16x4 a0 = i8x4_to_f16x4(k.v[h].x), a1 = i8x4_to_f16x4(k.v[h].y);
-      const f16x4 a2 = i8x4_to_f16x4(k.v[h].z), a3 = i8x4_to_f16x4(k.v[h].w);
-      m.v[2 * h] = f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      m.v[2 * h + 1] = f16x8{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
+      const bf16x4 a0 = i8x4_to_bf16x4(k.v[h].x), a1 = i8x4_to_bf16x4(k.v[h].y);
+      const bf16x4 a2 = i8x4_to_bf16x4(k.v[h].z), a3 = i8x4_to_bf16x4(k.v[h].w);
+      m.v[2 * h] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      m.v[2 * h + 1] = bf16x8{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
     }
     return m;
   }
@@ -378,7 +378,7 @@ struct I8Kv {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 2 * NH; ++s)
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(k.v[s], q.v[s], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k.v[s], q.v[s], c, 0, 0, 0);
     return c;
   }
   __device__ static void mask_v(V&, int, int) {}  // codes are finite; P = 0 removes them
@@ -402,14 +402,21 @@ struct I8Kv {
 };
 
 // fp8 e4m3 codes (OCP format) with the same per-(block, KV head) scales and tile layout as
-// int8.  gfx950 converts two e4m3 bytes to two fp16 values in one instruction
-// (v_cvt_scalef32_pk_f16_fp8, scale 1); every e4m3 value, subnormals included, is exact in
-// fp16, so the MFMA operands are exact as for int8.  Unlike int8, any byte pattern of an
-// unused slot may be a NaN code, so V codes past the sequence end are zeroed.
+// int8.  gfx950 converts two e4m3 bytes to two fp16 or two bf16 values in one instruction
+// (v_cvt_scalef32_pk_{f16,bf16}_fp8, scale 1); every e4m3 value, subnormals included, is
+// exact in both (4 significant bits, exponents 2^-9 .. 2^8), so the MFMA operands are exact
+// as for int8: K in bf16 beside the bf16 q, V in fp16 beside the fp16 weights.  Unlike
+// int8, any byte pattern of an unused slot may be a NaN code, so V codes past the sequence
+// end are zeroed.
 __device__ __forceinline__ f16x4 fp8x4_to_f16x4(uint32_t w) {
   const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
   const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
   return f16x4{a[0], a[1], b[0], b[1]};
+}
+__device__ __forceinline__ bf16x4 fp8x4_to_bf16x4(uint32_t w) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return bf16x4{a[0], a[1], b[0], b[1]};
 }
 
 template <int D>
@@ -425,10 +432,10 @@ struct Fp8Kv : I8Kv<D> {
     KMat m;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const f16x4 a0 = fp8x4_to_f16x4(k.v[h].x), a1 = fp8x4_to_f16x4(k.v[h].y);
-      const f16x4 a2 = fp8x4_to_f16x4(k.v[h].z), a3 = fp8x4_to_f16x4(k.v[h].w);
-      m.v[2 * h] = f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      m.v[2 * h + 1] = f16x8{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
+      const bf16x4 a0 = fp8x4_to_bf16x4(k.v[h].x), a1 = fp8x4_to_bf16x4(k.v[h].y);
+      const bf16x4 a2 = fp8x4_to_bf16x4(k.v[h].z), a3 = fp8x4_to_bf16x4(k.v[h].w);
+      m.v[2 * h] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      m.v[2 * h + 1] = bf16x8{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
     }
     return m;
   }
@@ -508,9 +515,11 @@ struct Rows {
     float vfac = 1.f;
     if constexpr (kScaled) {
       vfac = vs * inv_vref256;
-      if (vfac > 4096.f) {
-        // this block's V scale is far above the reference: move the reference to it so
-        // p * vfac stays well inside the fp16 range
+      if (vs > 0.f && (vfac > 4096.f || vfac < 16.f)) {
+        // this block's V scale is more than 16x above or below the reference: move the
+        // reference to it, so that p * vfac (p <= 2^kLazy) stays below the fp16 maximum and
+        // weights down to 2^-18 stay above the fp16 subnormals (a reference stuck at an
+        // outlier block's scale would leave the later blocks' weights there)
         const float r = v_ref / vs;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)

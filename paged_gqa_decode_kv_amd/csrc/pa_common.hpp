@@ -14,6 +14,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -53,6 +54,17 @@ __device__ __forceinline__ f16x4 i8x4_to_f16x4(uint32_t w) {
   const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
   const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
   return f16x4{a[0], a[1], b[0], b[1]};
+}
+
+// 4 packed int8 codes -> 4 exact bf16 values (|code| <= 128 needs 8 significant bits, which
+// bf16 has): each byte is sign-extended into an fp32 (v_cvt_f32_i32 with a byte select) and
+// pairs are packed to bf16 (v_cvt_pk_bf16_f32, exact for these integers).
+__device__ __forceinline__ bf16x4 i8x4_to_bf16x4(uint32_t w) {
+  const float a = (float)(int8_t)(w & 0xFFu);
+  const float b = (float)(int8_t)((w >> 8) & 0xFFu);
+  const float c = (float)(int8_t)((w >> 16) & 0xFFu);
+  const float d = (float)(int8_t)(w >> 24);
+  return bf16x4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
 }
 
 // Lanes l, l^16, l^32 and l^48 hold the same query row.  gfx950's permlane swaps exchange

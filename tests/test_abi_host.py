@@ -130,8 +130,8 @@ def test_verify_and_split_checks():
                                    None) == -2
     for pt, mp in [(0, 4), (24, 4), (-16, 4), (16, 0)]:
         assert P.lib.paged_decode_attn_split(ctypes.byref(d), f, f, f, None, None, f, f, 0.1,
-                                             pt, mp, f, f, None) == -6
-        assert P.lib.lse_merge(ctypes.byref(d), f, f, f, pt, mp, f, None, None) == -6
+                                             pt, mp, f, f, None) == -8
+        assert P.lib.lse_merge(ctypes.byref(d), f, f, f, pt, mp, f, None, None) == -8
     assert P.lib.paged_decode_attn_split(ctypes.byref(d), f, f, f, None, None, f, f, 0.1, 32, 4,
                                          None, f, None) == -1
     assert P.lib.kv_gather(ctypes.byref(d), f, f, f, f, -1, f, f, None) == -2
@@ -158,11 +158,11 @@ def test_balanced_checks_and_sizes():
     assert P.paged_attn_balanced_workspace_bytes(_dims(num_blocks=1 << 29), 1, 8) > 0
     call = P.lib.paged_attn_balanced
     assert call(ctypes.byref(d), 1, f, f, f, None, None, f, f, 0.1, 8, f, n - 1, f, None,
-                None) == -8
+                None) == -6
     assert call(ctypes.byref(d), 1, f, f, f, None, None, f, f, 0.1, 8, ctypes.c_void_p(FAKE + 4),
-                n, f, None, None) == -8                                 # misaligned
+                n, f, None, None) == -6                                 # misaligned
     assert call(ctypes.byref(d), 1, f, f, f, None, None, f, f, 0.1, 0, f, n, f, None, None) == -2
-    assert P.lib.paged_attn_balanced_merge(ctypes.byref(d), 1, 8, f, n - 1, f, None, None) == -8
+    assert P.lib.paged_attn_balanced_merge(ctypes.byref(d), 1, 8, f, n - 1, f, None, None) == -6
     assert P.lib.paged_split_workspace_bytes(ctypes.byref(d), 3) == 2 * 8 * 3 * (64 + 1) * 4
 
 

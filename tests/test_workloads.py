@@ -175,3 +175,27 @@ def test_relabel_moves_data_with_tables():
         K2, V2 = paging.depage(w2.k_cache.numpy(), w2.v_cache.numpy(), "f32",
                                w2.block_tables[b].numpy(), L, 1)
         assert np.array_equal(K1, K2, equal_nan=True) and np.array_equal(V1, V2, equal_nan=True)
+
+
+def test_v_scale_outliers():
+    """An outlier element in each sequence's first block raises that block's V scale to
+    outlier / 127 (int8) and leaves the block's other codes at 0; a first-block factor
+    scales the first block's V scale by the factor."""
+    base = dict(batch=4, length_range=(40, 200))
+    big = W.generate(W.scaled("verify_int8", v_outlier=4e4, **base), poison=False)
+    ref = W.generate(W.scaled("verify_int8", **base), poison=False)
+    small = W.generate(W.scaled("verify_int8", v_first_block_factor=1e-4, **base), poison=False)
+    v = big.v_cache.transpose(2, 3)                       # token-major codes
+    for b in range(4):
+        first = int(big.block_tables[b, 0])
+        assert torch.allclose(big.v_scale[first], torch.full((8,), 4e4 / 127), rtol=1e-6)
+        sign = 1 - 2 * (b % 2)
+        assert (v[first, :, 0, 5] == 127 * sign).all()
+        others = v[first].clone()
+        others[:, 0, 5] = 0
+        assert int(others.abs().max()) == 0                # N(0,1) values round to code 0
+        r = small.v_scale[first] / ref.v_scale[first]
+        assert torch.allclose(r, torch.full((8,), 1e-4), rtol=1e-5)
+        # later blocks are untouched
+        rest = big.block_tables[b, 1:int(-(-int(big.seq_lens[b]) // 16))].long()
+        assert torch.equal(big.v_scale[rest], ref.v_scale[rest])

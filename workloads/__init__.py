@@ -150,6 +150,13 @@ class Config:
     peaked_factor: float = 8.0
     sliding_window: int = 0           # 0 = whole context; W = the W most recent tokens
     tree: bool = False                # the nq query positions form a speculative tree
+    # outlier V scales (per-(block, head) scales exist because of outliers, in-depth guide
+    # section 5.2): every sequence's first block has its V multiplied by this factor, and,
+    # if v_outlier is set, element (token 0, dim v_outlier_dim) of that block's V set to
+    # +-v_outlier (the sign alternating over sequences), before the 8-bit encoding
+    v_first_block_factor: float = 1.0
+    v_outlier: float = 0.0
+    v_outlier_dim: int = 5
     seed: int = 0
 
     @property
@@ -308,6 +315,16 @@ def generate(cfg, seed=None, *, poison=True, spare_blocks=0, shuffle_batch=False
         pick = torch.randperm(nslots, generator=gen)[: round(cfg.peaked_fraction * nslots)]
         blk, off = pick // BLOCK_SIZE, pick % BLOCK_SIZE
         k32[blk, :, off, :] *= cfg.peaked_factor
+    if cfg.v_first_block_factor != 1.0 or cfg.v_outlier != 0.0:
+        done = set()
+        for i, L in enumerate(lens):
+            if L <= 0 or alloc.block_tables[i][0] in done:
+                continue
+            blk = alloc.block_tables[i][0]
+            done.add(blk)
+            v32[blk] *= cfg.v_first_block_factor
+            if cfg.v_outlier != 0.0:
+                v32[blk, :, 0, cfg.v_outlier_dim] = cfg.v_outlier * (1 - 2 * (i % 2))
     q32 = torch.randn((B, cfg.num_q_pos, Hq, d), generator=gen)
     q = q32.to(_TORCH_DT[cfg.q_dtype])
 
