@@ -80,7 +80,9 @@ enum {
   PA_ERR_LAUNCH = -7,     /* a kernel launch failed (or a device query failed)             */
   PA_ERR_PARTITION = -8,  /* partition_tokens not a positive multiple of 16, or
                              max_partitions < 1                                            */
-  PA_ERR_ALIGN = -9       /* q, k_cache, v_cache or out not 16-byte aligned                */
+  PA_ERR_ALIGN = -9,      /* q, k_cache, v_cache or out not 16-byte aligned                */
+  PA_ERR_SCRATCH = -10    /* paged_decode_step_noalloc: the call needs more workspace than
+                             the library's static scratch (PA_NOALLOC_SCRATCH_BYTES)       */
 };
 
 /* Shapes and element types shared by every call. */
@@ -337,6 +339,30 @@ int paged_decode_step(const pa_dims* dims, const void* q, const void* k_new, con
 int paged_attn_balanced_merge(const pa_dims* dims, int32_t num_q_pos, int32_t num_workgroups,
                               void* workspace, size_t workspace_bytes, float* out,
                               float* out_lse, void* stream);
+
+/*
+ * paged_decode_step_noalloc -- for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops that must not call hipMalloc, harnesses that forbid
+ * it): paged_decode_step followed by paged_attn_balanced_merge, with the workspace taken
+ * from a static device array of the library instead of a caller buffer.  Arguments and
+ * results as paged_decode_step (num_q_pos = 1); out_lse may be NULL.
+ *   The array holds PA_NOALLOC_SCRATCH_BYTES (16 MiB) on each device the library runs on,
+ *   for the life of the process; its address is looked up (hipGetSymbolAddress, no
+ *   allocation) on the first call on each device, which is the only HIP call besides the
+ *   two launches.  A call whose paged_attn_balanced_workspace_bytes(dims, 1,
+ *   num_workgroups) exceeds it returns PA_ERR_SCRATCH before any HIP call (Llama-3-8B
+ *   shapes at the default workgroup count fit up to ~2,000 (sequence, KV head) pairs).
+ *   Every call on one device shares that device's array, and no part of it needs to start
+ *   at zero (each call writes what it reads); calls that overlap on one device -- on
+ *   different streams, or from different threads without ordering -- race on it and must
+ *   be serialised by the caller.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int paged_decode_step_noalloc(const pa_dims* dims, const void* q, const void* k_new,
+                              const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              float sm_scale, int32_t num_workgroups, float* out, float* out_lse,
+                              void* stream);
 
 /* Workspace bytes paged_attn_balanced needs (0 if the arguments are invalid). */
 size_t paged_attn_balanced_workspace_bytes(const pa_dims* dims, int32_t num_q_pos,

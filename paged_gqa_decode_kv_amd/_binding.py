@@ -17,7 +17,8 @@ PA_F32, PA_BF16, PA_I8, PA_FP8 = 0, 1, 2, 3
 PA_OK = 0
 PA_ERR_NULL, PA_ERR_DIMS, PA_ERR_DTYPE, PA_ERR_HEAD_DIM = -1, -2, -3, -4
 PA_ERR_BLOCK_SIZE, PA_ERR_WORKSPACE, PA_ERR_LAUNCH, PA_ERR_PARTITION = -5, -6, -7, -8
-PA_ERR_ALIGN = -9
+PA_ERR_ALIGN, PA_ERR_SCRATCH = -9, -10
+PA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _DTYPE_CODE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8,
                torch.float8_e4m3fn: PA_FP8,
@@ -56,6 +57,7 @@ def _load(path=_LIB_PATH):
         "paged_attn_balanced_workgroups": [D, I32],
         "paged_attn_balanced_merge": [D, I32, I32, P, ctypes.c_size_t, P, P, P],
         "paged_decode_step": [D, P, P, P, P, P, P, P, F32, I32, P, ctypes.c_size_t, P, P, P],
+        "paged_decode_step_noalloc": [D, P, P, P, P, P, P, P, F32, I32, P, P, P],
         "kv_copy_blocks": [D, P, I32, P, P, P, P, P],
         "kv_append_quant": [D, P, P, P, P, I32, I32, P, P, P, P, P, P, P],
         "paged_multi_query_attn": [D, I32, P, P, P, P, P, P, P, P, F32, P, P, P],
@@ -210,6 +212,14 @@ def paged_decode_step(dims, q, k_new, v_new, k_cache, v_cache, block_tables, seq
         ctypes.byref(dims), _p(q), _p(k_new), _p(v_new), _p(k_cache), _p(v_cache),
         _p(block_tables), _p(seq_lens), sm_scale, num_workgroups, _p(workspace), nbytes, _p(out),
         _p(out_lse), _stream(stream)))
+
+
+def paged_decode_step_noalloc(dims, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens,
+                              sm_scale, num_workgroups, out, out_lse=None, stream=None):
+    _check("paged_decode_step_noalloc", lib.paged_decode_step_noalloc(
+        ctypes.byref(dims), _p(q), _p(k_new), _p(v_new), _p(k_cache), _p(v_cache),
+        _p(block_tables), _p(seq_lens), sm_scale, num_workgroups, _p(out), _p(out_lse),
+        _stream(stream)))
 
 
 def paged_attn_balanced_merge(dims, num_q_pos, num_workgroups, workspace, out, out_lse=None,

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpaged_attn.so")
-SOURCES = ["attn.hip", "merge.hip", "append.hip", "api.cpp"]
+SOURCES = ["attn.hip", "merge.hip", "append.hip", "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 # packed-fp32 VALU forms are kept out of the generated code
@@ -51,7 +51,7 @@ def _compile(src, verbose):
 
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs

@@ -345,21 +345,14 @@ int paged_decode_step(const pa_dims* dims, const void* q, const void* k_new, con
                       const int32_t* seq_lens, float sm_scale, int32_t num_workgroups,
                       void* workspace, size_t workspace_bytes, float* out, float* out_lse,
                       void* stream) {
-  int st = check_dims(dims);
+  pa::AttnArgs a{};
+  int st = pa::decode_step_args(dims, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens,
+                                sm_scale, num_workgroups, out, out_lse, &a);
   if (st != PA_OK) return st;
-  if (dims->kv_dtype != PA_F32 && dims->kv_dtype != PA_BF16) return PA_ERR_DTYPE;
-  st = check_attn_inputs(dims, q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens);
+  if (!workspace) return PA_ERR_NULL;
+  st = pa::bind_balanced_workspace(dims, 1, num_workgroups, workspace, workspace_bytes, out,
+                                   out_lse, &a);
   if (st != PA_OK) return st;
-  st = check_balanced(dims, 1, num_workgroups);
-  if (st != PA_OK) return st;
-  if (!k_new || !v_new || !out || !workspace) return PA_ERR_NULL;
-  if (!aligned16(out) || !aligned16(k_new)) return PA_ERR_ALIGN;
-  pa::AttnArgs a = make_args(dims, 1, q, k_cache, v_cache, nullptr, nullptr, block_tables,
-                             seq_lens, sm_scale);
-  st = balanced_args(dims, 1, num_workgroups, workspace, workspace_bytes, out, out_lse, &a);
-  if (st != PA_OK) return st;
-  a.k_new = k_new;
-  a.v_new = v_new;
   return pa::launch_balanced_append(a, dims->q_dtype, dims->kv_dtype, stream);
 }
 
@@ -394,8 +387,44 @@ const char* paged_status_string(int status) {
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_WORKSPACE: return "workspace too small or not 16-byte aligned";
     case PA_ERR_ALIGN: return "q, k_cache, v_cache or out not 16-byte aligned";
+    case PA_ERR_SCRATCH:
+      return "the decode step needs more workspace than the library's static scratch "
+             "(PA_NOALLOC_SCRATCH_BYTES): use paged_decode_step with a caller workspace";
     default: return "unknown status";
   }
 }
 
 }  // extern "C"
+
+namespace pa {
+
+int decode_step_args(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
+                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                     const int32_t* seq_lens, float sm_scale, int32_t num_workgroups, float* out,
+                     float* out_lse, AttnArgs* a) {
+  int st = check_dims(dims);
+  if (st != PA_OK) return st;
+  if (dims->kv_dtype != PA_F32 && dims->kv_dtype != PA_BF16) return PA_ERR_DTYPE;
+  st = check_attn_inputs(dims, q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens);
+  if (st != PA_OK) return st;
+  st = check_balanced(dims, 1, num_workgroups);
+  if (st != PA_OK) return st;
+  if (!k_new || !v_new || !out) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(k_new)) return PA_ERR_ALIGN;
+  *a = make_args(dims, 1, q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens,
+                 sm_scale);
+  a->k_new = k_new;
+  a->v_new = v_new;
+  a->out = out;
+  a->ws_out_lse = out_lse;
+  return PA_OK;
+}
+
+int bind_balanced_workspace(const pa_dims* dims, int32_t num_q_pos, int32_t num_workgroups,
+                            void* workspace, size_t workspace_bytes, float* out, float* out_lse,
+                            AttnArgs* a) {
+  return balanced_args(dims, num_q_pos, num_workgroups, workspace, workspace_bytes, out, out_lse,
+                       a);
+}
+
+}  // namespace pa

@@ -2,7 +2,10 @@
 // Arguments arrive here already validated.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
+
+#include "../../include/paged_attn.h"
 
 namespace pa {
 
@@ -67,6 +70,18 @@ int launch_balanced_append(const AttnArgs& a, int q_dtype, int kv_dtype, void* s
 
 // merge of the balanced mode's partials into out [B][nq][Hq][d] (and out_lse, if given)
 int launch_balanced_merge(const AttnArgs& a, float* out, float* out_lse, void* stream);
+
+// The host checks of the decode step (paged_decode_step's arguments, the workspace aside)
+// and its launch arguments in *a; PA_OK or the status the entry point returns.  No HIP call.
+int decode_step_args(const pa_dims* dims, const void* q, const void* k_new, const void* v_new,
+                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                     const int32_t* seq_lens, float sm_scale, int32_t num_workgroups, float* out,
+                     float* out_lse, AttnArgs* a);
+// Points the balanced mode's workspace fields of *a into `workspace` (PA_ERR_WORKSPACE if
+// it is smaller than paged_attn_balanced_workspace_bytes or not 16-byte aligned).
+int bind_balanced_workspace(const pa_dims* dims, int32_t num_q_pos, int32_t num_workgroups,
+                            void* workspace, size_t workspace_bytes, float* out, float* out_lse,
+                            AttnArgs* a);
 
 int launch_merge(const float* part_out, const float* part_lse, const int32_t* seq_lens,
                  int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_blocks,

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
               "paged_attn_balanced_workspace_bytes", "paged_attn_balanced_workgroups",
               "paged_split_workspace_bytes", "kv_gather", "paged_status_string",
               "paged_decode_step", "kv_copy_blocks", "kv_append_quant",
-              "paged_multi_query_attn"]:
+              "paged_multi_query_attn", "paged_decode_step_noalloc"]:
         assert n in names
 
 
@@ -167,7 +167,7 @@ def test_balanced_checks_and_sizes():
 
 
 def test_status_strings():
-    for st in range(0, -10, -1):
+    for st in range(0, -11, -1):
         assert P.paged_status_string(st) and P.paged_status_string(st) != "unknown status"
     assert P.paged_status_string(-99) == "unknown status"
 
@@ -254,3 +254,24 @@ def test_header_compiles_as_plain_c(tmp_path):
                             "-I", inc, "-c", str(c_file), "-o", str(tmp_path / "abi.o")],
                            capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def test_noalloc_decode_step_checks():
+    """The allocation-free decode step runs the decode step's host checks, and a call that
+    needs more than the static scratch is refused, all before any HIP call."""
+    f = ctypes.c_void_p(FAKE)
+
+    def call(d, G=8, out=FAKE, k_new=FAKE):
+        return P.lib.paged_decode_step_noalloc(
+            ctypes.byref(d), f, ctypes.c_void_p(k_new) if k_new else None, f, f, f, f, f,
+            ctypes.c_float(0.1), G, ctypes.c_void_p(out) if out else None, None, None)
+    assert call(_dims(head_dim=80)) == -4
+    assert call(_dims(kv_dtype="i8")) == -3
+    assert call(_dims(), k_new=None) == -1
+    assert call(_dims(), out=FAKE + 4) == -9
+    assert call(_dims(), G=0) == -2
+    # 2048 sequences x 8 KV heads: 16,384 segments of 16 rows x 128 dims, ~134 MB
+    big = _dims(num_seqs=2048, num_q_heads=32, num_kv_heads=8, head_dim=128)
+    assert P.paged_attn_balanced_workspace_bytes(big, 1, 256) > P.PA_NOALLOC_SCRATCH_BYTES
+    assert call(big, G=256) == -10
+    assert "scratch" in P.paged_status_string(-10)
