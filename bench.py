@@ -1,12 +1,12 @@
 """Benchmark: paged GQA decode attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--path step|balanced|split|direct]
-                    [--layout interleaved|separate]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--event-steps E]
+                    [--path step|balanced|split|direct] [--layout interleaved|separate]
 
 One step is one decode step of one attention layer of the Llama-3-8B-shaped workload
 (batch 64, 32 query / 8 KV heads, head_dim 128, bf16 KV, contexts U[512, 4096], seed
 1001): the append of the 64 new tokens and paged decode attention over the cache that
-includes them.  Paths:
+includes them.  Paths for that workload:
   step      (default) paged_decode_step + paged_attn_balanced_merge: the append folded
             into the balanced attention kernel, then the merge of cut segments
   balanced  kv_append, paged_attn_balanced, paged_attn_balanced_merge
@@ -17,16 +17,26 @@ default) or two separate pools.  Inputs are resident in HBM before the timed reg
 two copies of the KV pool are used in turn so that consecutive steps do not find the
 previous step's KV in the 256 MB Infinity Cache.
 
-Printed: ONE JSON line.  value = algorithmic KV bytes per step / step time (GB/s);
-roofline.achieved = the same bytes / the attention kernel's mean duration, timed with
-HIP events (no system fence) on the stream the kernels run on.  The other workloads (Llama-2-70B shared
-prefix, 128K context, int8 verify) are timed the same way and reported under "others".
-cpu_baseline times the fp64 oracle on a bounded sample of the same workload.
+Timing: W untimed warm-up steps, then EXACTLY K steps between two synchronisations with
+no events in between (value, ms_per_step), then a separate pass of E steps in which HIP
+events (no system fence, on the stream the kernels run on) bracket the attention kernel
+and the merge of every step (kernel means and percentiles, roofline.achieved).
 
-    python bench.py --pmc-summary FETCH_DIR WRITE_DIR
+Printed: ONE JSON line.  value = algorithmic KV bytes per step / wall-clock step time
+(GB/s).  "configs" holds the same columns for the five configurations of the task -- c1
+tiny fp32 (with a standalone kv_append), c2 Llama-3-8B (the headline), c3 Llama-2-70B
+shared prefix, c4 128K context (decode step, and split + LSE merge at the partition size
+the bench picks), c5 int8 speculative verify -- each with its max abs error against the
+fp64 oracle over every output element and the oracle's own time on the same inputs.
+"others" holds the further workloads (sliding window, fp8, block copy, quantising
+append, chunked prefill, tree verify); cpu_baseline times the oracle on a bounded sample
+of the headline workload.
 
-writes the HBM-traffic summary of the attention kernel (profiles/) from two rocprofv3
---pmc runs of this script with --calibrate (FETCH_SIZE, then WRITE_SIZE).
+Profiler summaries (profiles/) from rocprofv3 runs of this script with the same flags:
+    --trace-summary DIR            kernel trace (per workload and kernel)
+    --counter-summary DIR [NAME]   one --pmc pass of counters
+    --pmc-summary FETCH_DIR WRITE_DIR   HBM bytes per launch of every workload's kernels
+                                   (FETCH_SIZE and WRITE_SIZE passes, with --calibrate)
 """
 import argparse
 import json
@@ -40,11 +50,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged decode attention: KV-read GB/s (% of HBM peak) and µs/step per layer"
 
-# partition sizes (tokens) used by the split path, per workload
+# partition sizes (tokens) tried by the split path, per workload; the 128K configuration
+# picks the fastest of its candidates
 PARTITION = {"llama3_8b": 512, "llama2_70b_prefix": 1024, "long_128k": 2048,
              "verify_int8": None, "tiny_fp32": None}
+SPLIT_CANDIDATES = (1024, 2048, 4096, 8192)
+
+# the task's configurations: label, workload, attention path
+CONFIGS = [("c1", "tiny_fp32", "step"), ("c2", "llama3_8b", "step"),
+           ("c3", "llama2_70b_prefix", "step"), ("c4", "long_128k", "step"),
+           ("c5", "verify_int8", "step")]
+TOL = {"f32": 1e-5, "bf16": 2e-3, "i8": 4e-3, "fp8": 4e-3}
+
+# Workloads in the order the bench runs them; each starts with a separator kernel (mark),
+# which is how the profiler summaries tell them apart.  (name, warm-up launches of its
+# kernels before the timed ones)
+ORDER = ["llama3_8b", "tiny_fp32", "llama2_70b_prefix", "long_128k", "long_128k_split",
+         "verify_int8", "mistral_7b_window", "llama3_8b_fp8", "kv_copy_blocks",
+         "kv_append_quant", "prefill_chunk", "tree_verify"]
 
 
 def parse():
@@ -52,20 +78,20 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--event-steps", type=int, default=50,
+                    help="steps of the separate pass whose kernels are bracketed by events")
     ap.add_argument("--path", choices=["step", "balanced", "split", "direct"], default="step")
     ap.add_argument("--layout", choices=["interleaved", "separate"], default="interleaved")
     ap.add_argument("--workgroups", type=int, default=0, help="balanced path; 0 = library default")
     ap.add_argument("--partition", type=int, default=None)
-    ap.add_argument("--event-every", type=int, default=4,
-                    help="bracket the attention kernel with HIP events on every n-th timed step "
-                         "from the second on")
-    ap.add_argument("--no-others", action="store_true")
-    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="the headline workload only (no other configurations or workloads)")
+    ap.add_argument("--no-cpu", action="store_true", help="no oracle timing or parity")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="summarise two rocprofv3 --pmc runs into the traffic file and exit")
+                    help="summarise two rocprofv3 --pmc runs into profiles/hbm_traffic.json")
     ap.add_argument("--counter-summary", nargs="+", metavar=("PMC_DIR", "NAME"),
                     help="summarise one rocprofv3 --pmc run of this script into "
                          "profiles/NAME.md (default kernel_counters) and exit")
@@ -74,6 +100,10 @@ def parse():
                          "and exit")
     return ap.parse_args()
 
+
+def log(msg):
+    """Progress on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 class HipEvent:
     """A HIP timing event recorded on the current torch stream (the stream the binding
@@ -125,9 +155,8 @@ class HipEvent:
         except Exception:       # interpreter shutdown
             pass
 
-
 class Runner:
-    """Device-resident inputs of one workload and one decode step through the C ABI."""
+    """Device-resident inputs of one workload and one step through the C ABI."""
 
     def __init__(self, P, wl, path, partition, copies=2, workgroups=0, layout="interleaved"):
         import torch
@@ -171,6 +200,7 @@ class Runner:
         self.split = path == "split" and c.num_q_pos == 1 and partition
         if path == "split" and not self.split:
             self.path = "direct"
+        self.pt = self.maxp = None
         if self.split:
             self.pt = partition
             self.maxp = -(-int(wl.seq_lens.max()) // partition)
@@ -178,14 +208,16 @@ class Runner:
                                         dtype=torch.float32, device=dev)
             self.part_lse = torch.empty((c.batch, c.num_q_heads, self.maxp),
                                         dtype=torch.float32, device=dev)
-        if path in ("balanced", "step"):
+        self.G = None
+        if self.path in ("balanced", "step"):
             self.G = workgroups or P.paged_attn_balanced_workgroups(self.dims, c.num_q_pos)
             nbytes = P.paged_attn_balanced_workspace_bytes(self.dims, c.num_q_pos, self.G)
             self.ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
 
     def step(self, i, ev=None):
-        """One decode step.  With ev, HIP events bracket the attention kernel only (append
-        and merge are left unbracketed; rocprofv3 gives their durations)."""
+        """One step.  With ev = (e0, e1, e2), HIP events bracket the attention kernel
+        (e0 .. e1) and the merge (e1 .. e2); the append of the non-fused paths is left
+        outside them."""
         P, c = self.P, self.wl.cfg
         kc, vc, ks, vs = self.pools[i % len(self.pools)]
         if self.append and self.path != "step":
@@ -211,27 +243,207 @@ class Runner:
         elif self.split:
             P.lse_merge(self.dims, self.part_out, self.part_lse, self.lens, self.pt, self.maxp,
                         self.out)
+        if ev is not None:
+            ev[2].record()
 
-    def measure(self, steps, warmup, every=4):
-        """Wall time of `steps` steps; the attention kernel is bracketed by HIP events on
-        every `every`-th step of the same timed region from the second on (steps 1,
-        1 + every, ...): the first step starts on the queue the warm-up's synchronisation
-        left idle and runs ~10-20% long, which is not the kernel's sustained duration."""
+    def measure(self, steps, warmup, event_steps):
+        """Wall time of exactly `steps` steps with nothing else in between, then a separate
+        pass of `event_steps` steps with the attention kernel and the merge of each step
+        bracketed by events.  Returns (wall seconds, attention us array, merge us array)."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        evs = {i: [HipEvent() for _ in range(2)]
-               for i in range(min(1, steps - 1), steps, every)}
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.step(i, evs.get(i))
+            self.step(i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        attn = [e[0].elapsed_time(e[1]) * 1e3 for e in evs.values()]     # us
-        return wall, np.array(attn)
+        evs = [[HipEvent() for _ in range(3)] for _ in range(event_steps)]
+        torch.cuda.synchronize()
+        for i in range(event_steps):
+            self.step(i, evs[i])
+        torch.cuda.synchronize()
+        attn = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+        merge = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
+        return wall, attn, merge
 
+
+def pct(a, p):
+    """Percentile by the rule int((n - 1) * p) of the sorted samples."""
+    s = np.sort(np.asarray(a))
+    return float(s[int((len(s) - 1) * p)])
+
+
+def summarize(wl, wall, steps, attn, merge):
+    kv = wl.kv_bytes()
+    us_step = wall / steps * 1e6
+    kern = attn + merge
+    return {
+        "kv_bytes": kv,
+        "us_per_step": us_step,
+        "kv_GBps": kv / (us_step * 1e-6) / 1e9,
+        "pct_hbm_peak": kv / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS * 100,
+        "attn_kernel_us_mean": float(attn.mean()),
+        "attn_kernel_us_median": float(np.median(attn)),
+        "attn_kernel_us_p95": pct(attn, 0.95),
+        "merge_us_mean": float(merge.mean()),
+        "merge_us_p95": pct(merge, 0.95),
+        "kernels_us_mean": float(kern.mean()),
+        "attn_kernel_GBps": kv / (attn.mean() * 1e-6) / 1e9,
+        "kernels_GBps": kv / (kern.mean() * 1e-6) / 1e9,
+        "event_samples": len(attn),
+    }
+
+
+def total_bytes(wl):
+    """Bytes a step moves beyond the KV stream, added to it: queries read, outputs written,
+    the used block-table entries and lengths read once, the appended tokens (K and V rows
+    read, then written into their slots)."""
+    c = wl.cfg
+    qe = {"f32": 4, "bf16": 2}[c.q_dtype]
+    ke = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1}[c.kv_dtype]
+    rows = c.batch * c.num_q_pos * c.num_q_heads * c.head_dim
+    ents = sum(-(-int(L) // 16) for L in wl.seq_lens.tolist())
+    app = 2 * 2 * c.batch * c.num_kv_heads * c.head_dim * ke if wl.slot_mapping is not None else 0
+    return wl.kv_bytes() + rows * qe + rows * 4 + ents * 4 + c.batch * 4 + app
+
+
+def unique_kv_bytes(wl):
+    """KV bytes of the distinct physical blocks the batch reads (shared blocks once)."""
+    c = wl.cfg
+    elem = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1}[c.kv_dtype]
+    return int(wl.occupancy.sum()) * 2 * c.num_kv_heads * c.head_dim * elem
+
+
+_ORACLE = {}   # workload name -> (reference output, seconds, threads): one pass each
+
+
+def oracle_parity(wl, out):
+    """The fp64 oracle over every (sequence, KV head) pair of the workload, on the caches
+    after the step's append; returns (max |out - oracle| over every element, oracle
+    seconds, threads it kept busy).  A workload measured twice (the 128K decode step and
+    its split path) reuses the first pass."""
+    key = (wl.cfg.name, wl.meta["seed"])
+    if key in _ORACLE:
+        ref, dt, cores = _ORACLE[key]
+        g = out.detach().cpu().numpy().astype(np.float64).reshape(ref.shape)
+        err = float(np.abs(g - ref).max()) if np.isfinite(g).all() else float("inf")
+        return err, dt, cores
+    import torch
+    from oracle import attention, paging
+
+    def raw(x):
+        if x is None:
+            return None
+        return x.view(torch.int16).numpy() if x.dtype == torch.bfloat16 else x.numpy()
+    c = wl.cfg
+    kc, vc = raw(wl.k_cache), raw(wl.v_cache)
+    t0, c0 = time.perf_counter(), time.process_time()
+    if wl.slot_mapping is not None:
+        kc, vc = paging.append(kc, vc, raw(wl.k_new), raw(wl.v_new), wl.slot_mapping.numpy())
+    ref, _ = attention.paged_attention(raw(wl.q), c.q_dtype, kc, vc, c.kv_dtype,
+                                       wl.block_tables.numpy(), wl.seq_lens.numpy(),
+                                       float(np.float32(c.sm_scale)), c.num_q_pos,
+                                       raw(wl.k_scale), raw(wl.v_scale),
+                                       window=c.sliding_window)
+    dt = time.perf_counter() - t0
+    busy = (time.process_time() - c0) / max(dt, 1e-9)
+    _ORACLE.clear()
+    _ORACLE[key] = (ref, dt, max(1, int(round(busy))))
+    g = out.detach().cpu().numpy().astype(np.float64).reshape(ref.shape)
+    err = float(np.abs(g - ref).max()) if np.isfinite(g).all() else float("inf")
+    return err, dt, max(1, int(round(busy)))
+
+
+def config_entry(P, torch, W, label, name, path, args, partition=None, main=None):
+    """One configuration's columns: wall-clock step, kernel times and percentiles, bytes,
+    rates, HBM fraction, counter-measured HBM bytes (when the committed summary matches
+    the kernel sources), and parity with the oracle over every output element."""
+    wl = W.generate(name, poison=False)
+    copies = 1 if name == "long_128k" else 2
+    if main is None:
+        r = Runner(P, wl, path, partition, copies=copies)
+        wall, attn, merge = r.measure(args.steps, 3, args.event_steps)
+    else:
+        r, wall, attn, merge = main
+    s = summarize(wl, wall, args.steps, attn, merge)
+    c = wl.cfg
+    e = {"workload": name, "path": r.path, "workgroups": r.G,
+         "partition_tokens": r.pt, "kv_dtype": c.kv_dtype, "batch": c.batch,
+         "q_heads": c.num_q_heads, "kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
+         "num_q_pos": c.num_q_pos, "seed": wl.meta["seed"]}
+    e.update({k: (round(v, 3) if isinstance(v, float) else v) for k, v in s.items()})
+    e["total_bytes"] = total_bytes(wl)
+    e["attn_kernel_frac_of_peak"] = round(s["attn_kernel_GBps"] / HBM_PEAK_GBS, 4)
+    e["kernels_frac_of_peak"] = round(s["kernels_GBps"] / HBM_PEAK_GBS, 4)
+    if c.shared_groups:
+        # shared prefix: the HBM fractions are taken over the distinct blocks' bytes (each
+        # read at most once from HBM); the logical rate is reported beside them
+        ub = unique_kv_bytes(wl)
+        e["unique_kv_bytes"] = ub
+        e["logical_kv_GBps"] = e["kv_GBps"]
+        e["unique_kv_GBps"] = round(ub / (s["us_per_step"] * 1e-6) / 1e9, 1)
+        e["pct_hbm_peak"] = round(e["unique_kv_GBps"] / HBM_PEAK_GBS * 100, 2)
+        e["attn_kernel_frac_of_peak"] = round(ub / (s["attn_kernel_us_mean"] * 1e-6) / 1e9 /
+                                              HBM_PEAK_GBS, 4)
+        e["kernels_frac_of_peak"] = round(ub / (s["kernels_us_mean"] * 1e-6) / 1e9 /
+                                          HBM_PEAK_GBS, 4)
+    tr = measured_traffic(name if r.path != "split" else name + "_split")
+    e["fetched_bytes"] = None if tr is None else tr.get("attn_fetch_bytes")
+    e["hbm_traffic_step_bytes"] = None if tr is None else tr.get("step_traffic_bytes")
+    if not args.no_cpu:
+        err, dt, cores = oracle_parity(wl, r.out)
+        e["max_abs_err"] = err
+        e["tol"] = TOL[c.kv_dtype]
+        e["oracle"] = {"seconds": round(dt, 3), "kv_GBps": round(wl.kv_bytes() / dt / 1e9, 4),
+                       "cores": cores, "kind": "oracle", "sample": "every (sequence, KV head) "
+                       "pair of the workload, one pass, fp64 numpy"}
+    return e, r, wl
+
+
+def split_entry(P, torch, W, name, args):
+    """Split + LSE merge on a workload: every candidate partition size timed over a short
+    run, the fastest measured in full (its kv_append is outside the events)."""
+    wl = W.generate(name, poison=False)
+    cand = {}
+    for p in SPLIT_CANDIDATES:
+        r = Runner(P, wl, "split", p, copies=1)
+        _, attn, merge = r.measure(5, 2, 10)
+        cand[p] = round(float((attn + merge).mean()), 2)
+        del r
+        torch.cuda.empty_cache()
+    best = min(cand, key=cand.get)
+    e, r, _ = config_entry(P, torch, W, "split", name, "split", args, partition=best)
+    e["candidates_us"] = {str(k): v for k, v in cand.items()}
+    del r
+    torch.cuda.empty_cache()
+    return e
+
+
+def append_entry(P, torch, W, steps):
+    """kv_append alone on the tiny configuration: its 4 new tokens (fp32, 2 KV heads, d 64)
+    written into their slots, launches back to back between two events."""
+    wl = W.generate("tiny_fp32", poison=False)
+    c = wl.cfg
+    dev = torch.device("cuda:0")
+    kc, vc = wl.k_cache.to(dev), wl.v_cache.to(dev)
+    kn, vn, sm = wl.k_new.to(dev), wl.v_new.to(dev), wl.slot_mapping.to(dev)
+    d = P.make_dims(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, wl.block_tables.shape[1],
+                    kc.shape[0], c.q_dtype, c.kv_dtype)
+    for _ in range(3):
+        P.kv_append(d, kn, vn, sm, c.batch, kc, vc)
+    torch.cuda.synchronize()
+    e0, e1 = HipEvent(), HipEvent()
+    e0.record()
+    for _ in range(steps):
+        P.kv_append(d, kn, vn, sm, c.batch, kc, vc)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = 2 * 2 * c.batch * c.num_kv_heads * c.head_dim * 4
+    return {"tokens": c.batch, "kv_heads": c.num_kv_heads, "bytes": nbytes,
+            "us_per_launch": round(us, 2), "launches": steps}
 
 def copy_blocks_bench(P, torch, W, steps):
     """kv_copy_blocks on the Llama-3-8B pool (interleaved layout): a bulk copy of 2048
@@ -274,7 +486,6 @@ def copy_blocks_bench(P, torch, W, steps):
     torch.cuda.empty_cache()
     return res
 
-
 def append_quant_bench(P, torch, W, steps):
     """kv_append_quant for one decode step of a Llama-3-8B-shaped int8 cache: 64 new tokens
     (one per sequence, at the end of each sequence of the seeded Llama-3-8B lengths) into
@@ -316,10 +527,6 @@ def append_quant_bench(P, torch, W, steps):
     torch.cuda.empty_cache()
     return {"tokens": c.batch, "kv_heads": h, "bytes": nbytes, "us_per_launch": round(us, 2),
             "GBps": round(nbytes / us / 1e3, 1)}
-
-
-MFMA_BF16_PEAK_TFLOPS = 2500.0
-
 
 def multi_query_bench(P, torch, W, name, steps):
     """paged_multi_query_attn on a multi-query workload (chunked prefill: 256 causal
@@ -377,23 +584,6 @@ def multi_query_bench(P, torch, W, name, steps):
             "frac_of_bf16_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "kv_GBps": round(wl.kv_bytes() / us / 1e3, 1)}
 
-
-def summarize(wl, wall, steps, attn):
-    kv = wl.kv_bytes()
-    us_step = wall / steps * 1e6
-    srt = np.sort(attn)
-    return {
-        "kv_bytes": kv,
-        "us_per_step": us_step,
-        "kv_GBps": kv / (us_step * 1e-6) / 1e9,
-        "attn_kernel_us_mean": float(attn.mean()),
-        "attn_kernel_us_median": float(np.median(attn)),
-        "attn_kernel_us_p95": float(srt[int((len(srt) - 1) * 0.95)]),
-        "attn_kernel_GBps": kv / (attn.mean() * 1e-6) / 1e9,
-        "attn_kernel_samples": len(attn),
-    }
-
-
 def _blas_threads():
     """Threads numpy's BLAS may use (the oracle's matrix-vector products)."""
     try:
@@ -401,7 +591,6 @@ def _blas_threads():
         return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         return int(os.environ.get("OMP_NUM_THREADS", "1"))
-
 
 def cpu_baseline(wl, seconds):
     """The fp64 oracle, as it stands, run on the host over the same workload: whole
@@ -461,12 +650,11 @@ def cpu_baseline(wl, seconds):
                       f"{dt:.1f} s",
             "host_cpus": len(os.sched_getaffinity(0))}
 
-
 def cpu_oracle_others(W, seconds=3.0):
-    """The oracle beside the other measured paths, each on a bounded sample for about
-    `seconds` of host time, in the unit the GPU line reports: attention workloads in GB/s
-    of KV (window, fp8) or TFLOP/s (multi-query rows) over whole (sequence, KV head)
-    pairs; the block copy in GB/s moved; the quantising append in tokens x heads / s."""
+    """The oracle beside the measured paths that have no full oracle pass in "configs" /
+    "others", each on a bounded sample for about `seconds` of host time, in the unit the GPU
+    line reports: the multi-query rows in TFLOP/s over whole (sequence, KV head) pairs; the
+    block copy in GB/s moved; the quantising append in tokens x heads / s."""
     import torch
     from oracle import attention, paging, quant
 
@@ -488,7 +676,7 @@ def cpu_oracle_others(W, seconds=3.0):
                 return n, wall
 
     res = {}
-    for name in ("mistral_7b_window", "llama3_8b_fp8", "prefill_chunk", "tree_verify"):
+    for name in ("prefill_chunk", "tree_verify"):
         wl = W.generate(W.scaled(name, append=False), poison=False)
         c = wl.cfg
         pairs = [(b, g) for b in range(c.batch) for g in range(c.num_kv_heads)]
@@ -537,12 +725,20 @@ def cpu_oracle_others(W, seconds=3.0):
                  blas_threads=_blas_threads())
     return res
 
+def calibration_copy(torch, nbytes=1 << 30):
+    """A plain device-to-device copy of known size, for scaling the HBM counters."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
 
-KERNEL_SOURCES = ["paged_gqa_decode_kv_amd/csrc/attn.hip", "paged_gqa_decode_kv_amd/csrc/pa_common.hpp"]
-
-
-def traffic_file(path, layout):
-    return os.path.join(ROOT, "profiles", f"llama3_8b_{path}_{layout}_traffic.json")
+KERNEL_SOURCES = ["paged_gqa_decode_kv_amd/csrc/attn.hip", "paged_gqa_decode_kv_amd/csrc/merge.hip",
+                  "paged_gqa_decode_kv_amd/csrc/append.hip", "paged_gqa_decode_kv_amd/csrc/pa_common.hpp",
+                  "paged_gqa_decode_kv_amd/csrc/launch.hpp"]
+TRAFFIC_FILE = "hbm_traffic.json"
+MARKER = "FillFunctor<short>"
 
 
 def kernel_source_hash():
@@ -554,165 +750,89 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(path, layout):
-    """HBM bytes per launch of the attention kernel from the committed counter summary,
-    or None if there is none or the kernel source changed since it was taken."""
+def measured_traffic(workload):
+    """HBM bytes per launch of a workload's kernels from the committed counter summary,
+    or None if there is none or the kernel sources changed since it was taken."""
     try:
-        with open(traffic_file(path, layout)) as fh:
+        with open(os.path.join(ROOT, "profiles", TRAFFIC_FILE)) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha") != kernel_source_hash():
         return None
-    return t.get("traffic_bytes_per_launch")
+    return t.get("workloads", {}).get(workload)
 
 
-def calibration_copy(torch, nbytes=1 << 30):
-    """A plain device-to-device copy of known size, for scaling the HBM counters."""
-    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
+def mark(torch):
+    """A small fill kernel (int16, used nowhere else) that opens a workload in a profiler
+    trace; the summaries split the dispatch list at it."""
+    torch.empty(64, dtype=torch.int16, device="cuda:0").fill_(1)
     torch.cuda.synchronize()
-    del a, b
 
 
-KERNEL_NAME = {"step": "paged_attn_balanced_kernel (decode step: append folded in)",
-               "balanced": "paged_attn_balanced_kernel",
-               "split": "paged_attn_kernel (split)", "direct": "paged_attn_kernel (direct)"}
+def _short(n):
+    import re
+    if "pa::" not in n:
+        return None
+    n = n.replace("(anonymous namespace)::", "")
+    m = re.match(r"void pa::(\w+)<(.*)>\(", n)
+    if m:
+        return f"{m.group(1)}<{m.group(2)}>"
+    m = re.match(r"void pa::(\w+)\(", n)
+    return m.group(1) if m else n.split("(")[0][:60]
 
 
-def pmc_summary(args, fetch_dir, write_dir):
-    """Traffic file from two rocprofv3 --pmc runs of this script (--calibrate): the
-    attention kernel's per-dispatch FETCH_SIZE / WRITE_SIZE (KiB), each scaled by what the
-    same counter reads for the 1 GiB calibration copy (copy bytes / counter bytes)."""
-    import sqlite3
-    copy_bytes = 1 << 30
+def _grouped(rows):
+    """(kernel name, value) pairs in dispatch order -> [(workload, {kernel: [values]})],
+    one group per marker, named by ORDER."""
+    groups, cur = [], None
+    for name, val in rows:
+        if MARKER in name:
+            cur = {}
+            groups.append(cur)
+            continue
+        k = _short(name)
+        if cur is None or k is None:
+            continue
+        cur.setdefault(k, []).append(val)
+    return list(zip(ORDER, groups))
 
-    def load(d, counter):
-        db = sqlite3.connect(os.path.join(d, "run_results.db"))
-        rows = db.execute("select kernel_name, value from counters_collection "
-                          "where counter_name=? order by dispatch_id", (counter,)).fetchall()
-        cal = [v for k, v in rows if "copyBuffer" in k][:3]
-        att = [v for k, v in rows if "paged_attn_balanced_kernel" in k or
-               ("paged_attn_kernel" in k and "balanced" not in k)]
-        return float(np.mean(cal)), float(np.mean(att)), len(att)
-    cf, fetch, n = load(fetch_dir, "FETCH_SIZE")
-    cw, write, _ = load(write_dir, "WRITE_SIZE")
-    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
-    import workloads as W
-    wl = W.generate("llama3_8b", poison=False)
-    out = {
-        "kernel": KERNEL_NAME[args.path],
-        "workload": "llama3_8b_layer_decode (batch 64, 32q/8kv, d128, bf16, contexts "
-                    "U[512,4096] seed 1001), library-default workgroups",
-        "path": args.path, "layout": args.layout,
-        "kernel_source_sha": kernel_source_hash(), "kernel_sources": KERNEL_SOURCES,
-        "algorithmic_bytes_per_launch": wl.kv_bytes(),
-        "fetch_bytes_per_launch": round(fetch * 1024 * fs),
-        "write_bytes_per_launch": round(write * 1024 * ws),
-        "traffic_bytes_per_launch": round(fetch * 1024 * fs + write * 1024 * ws),
-        "calibration": {"copy_bytes": copy_bytes, "FETCH_SIZE_KiB": round(cf, 1),
-                        "WRITE_SIZE_KiB": round(cw, 1), "fetch_scale": round(fs, 5),
-                        "write_scale": round(ws, 5)},
-        "raw_KiB_per_dispatch": {"FETCH_SIZE": round(fetch, 2), "WRITE_SIZE": round(write, 2),
-                                 "dispatches": n},
-        "commands": [
-            f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run -- python bench.py --steps 10 "
-            f"--warmup 2 --no-others --no-cpu --calibrate --path {args.path} --layout {args.layout}",
-            f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run -- python bench.py --steps 10 "
-            f"--warmup 2 --no-others --no-cpu --calibrate --path {args.path} --layout {args.layout}",
-            f"python bench.py --path {args.path} --layout {args.layout} --pmc-summary "
-            f"{fetch_dir} {write_dir}"],
-    }
-    with open(traffic_file(args.path, args.layout), "w") as fh:
-        json.dump(out, fh, indent=1)
-    print(json.dumps(out))
+
+def _warm(name, args):
+    return args.warmup if name == ORDER[0] else 3
+
+
+def _flags(args):
+    return (f"--steps {args.steps} --warmup {args.warmup} --event-steps {args.event_steps}" +
+            (" --no-cpu" if args.no_cpu else "") + f" --path {args.path} --layout {args.layout}")
 
 
 def trace_summary(args, trace_dir):
-    """Markdown summary of a rocprofv3 --kernel-trace run of this script, given the same
-    --steps / --warmup / --no-cpu / --path / --layout as the traced run: per kernel and
-    workload, calls and mean / median duration (the warm-up calls are left out: --warmup
-    of them for the main workload, 3 for the others)."""
-    import re
+    """Markdown summary of a rocprofv3 --kernel-trace run of this script (same flags):
+    per workload and kernel, launches and mean / median duration, warm-up launches left
+    out (the split workload's figures pool all its candidate partition sizes)."""
     import sqlite3
     db = sqlite3.connect(os.path.join(trace_dir, "run_results.db"))
     rows = db.execute("select name, start, end from kernels order by start").fetchall()
-
-    def short(n):
-        n = n.replace("(anonymous namespace)::", "")
-        m = re.match(r"void pa::(\w+)<(.*)>\(", n)
-        return f"{m.group(1)}<{m.group(2)}>" if m else n.split("(")[0][:60]
-    # the attention kernels start a new workload whenever their instantiation changes or
-    # a run of calls ends with a copy (the next workload's uploads)
-    groups, cur, last = [], None, None
-    copies, quants, rows_k = [], [], {}
-    for n, s0, e in rows:
-        k = short(n)
-        if "kv_copy_blocks" in k:
-            copies.append((e - s0) / 1000)
-            continue
-        if "kv_append_quant" in k:
-            quants.append((e - s0) / 1000)
-            continue
-        if k.startswith("paged_attn_kernel"):       # the multi-query rows (direct kernel)
-            rows_k.setdefault(k, []).append((e - s0) / 1000)
-            continue
-        if "copyBuffer" in k or "elementwise" in k or "fill" in k.lower():
-            last = "copy"
-            continue
-        if k.startswith("paged_attn") and (cur is None or last == "copy"):
-            cur = {}
-            groups.append(cur)
-        last = k
-        if cur is not None:
-            cur.setdefault(k, []).append((e - s0) / 1000)
-    names = ["llama3_8b", "llama2_70b_prefix", "long_128k", "verify_int8", "mistral_7b_window",
-             "llama3_8b_fp8"]
-    run_flags = (f"--steps {args.steps} --warmup {args.warmup}" +
-                 (" --no-cpu" if args.no_cpu else "") +
-                 f" --path {args.path} --layout {args.layout}")
-    lines = [f"# rocprofv3 kernel trace: bench.py --path {args.path} --layout {args.layout}", "",
+    groups = _grouped([(n, (e - s0) / 1000) for n, s0, e in rows])
+    lines = [f"# rocprofv3 kernel trace: bench.py {_flags(args)}", "",
              "Command (MI355X, one GPU):", "",
-             f"    rocprofv3 --kernel-trace --stats -d {trace_dir} -o run -- python bench.py "
-             f"{run_flags}",
-             f"    python bench.py {run_flags} --trace-summary {trace_dir}", "",
+             f"    rocprofv3 --kernel-trace --stats -d {trace_dir} -o run -- python bench.py {_flags(args)}",
+             f"    python bench.py {_flags(args)} --trace-summary {trace_dir}", "",
              f"Kernel sources sha: {kernel_source_hash()}", "",
-             "| workload | kernel | calls | mean us | median us |", "|---|---|---|---|---|"]
-    for name, g in zip(names, groups):
-        skip = args.warmup if name == names[0] else 3
+             "| workload | kernel | launches | mean us | median us |", "|---|---|---|---|---|"]
+    for name, g in groups:
         for k, v in g.items():
-            v = v[skip:] if len(v) > skip else v
+            w = _warm(name, args)
+            v = v[w:] if len(v) > w else v
             lines.append(f"| {name} | `{k}` | {len(v)} | {np.mean(v):.2f} | {np.median(v):.2f} |")
-    if copies:
-        # copy_blocks_bench: 4 warm-up + n bulk launches (2048 pairs), then the same for
-        # the 64-pair copy-on-write step
-        half = len(copies) // 2
-        for label, v in (("kv_copy_blocks 2048 pairs", copies[4:half]),
-                         ("kv_copy_blocks 64 pairs", copies[half + 4:])):
-            if v:
-                lines.append(f"| llama3_8b pool | `{label}` | {len(v)} | {np.mean(v):.2f} | "
-                             f"{np.median(v):.2f} |")
-    if quants:
-        v = quants[3:]      # 3 warm-up launches
-        lines.append(f"| llama3_8b int8 cache | `kv_append_quant` 64 tokens x 8 heads | {len(v)} | "
-                     f"{np.mean(v):.2f} | {np.median(v):.2f} |")
-    for (label, (k, v)) in zip(("prefill_chunk", "tree_verify"), rows_k.items()):
-        v = v[3:]       # 3 warm-up launches
-        lines.append(f"| {label} | `{k}` | {len(v)} | {np.mean(v):.2f} | {np.median(v):.2f} |")
     out = os.path.join(ROOT, "profiles", f"{args.path}_{args.layout}_kernel_trace.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def counter_summary(args, pmc_dir, out_name="kernel_counters"):
-    """Markdown summary of one rocprofv3 --pmc run of this script (given the same --steps /
-    --warmup / --no-cpu as the profiled run): per workload and kernel, the mean per-dispatch
-    value of every counter collected (warm-up dispatches left out as in trace_summary), and
-    per-wave ratios where the counters allow them."""
-    import re
+def _pmc_rows(pmc_dir):
     import sqlite3
     db = sqlite3.connect(os.path.join(pmc_dir, "run_results.db"))
     rows = db.execute("select dispatch_id, kernel_name, counter_name, value from "
@@ -721,38 +841,21 @@ def counter_summary(args, pmc_dir, out_name="kernel_counters"):
     for did, name, cname, val in rows:
         d = disp.setdefault(did, {"name": name, "c": {}})
         d["c"][cname] = d["c"].get(cname, 0.0) + float(val)
+    return [(disp[d]["name"], disp[d]["c"]) for d in sorted(disp)]
 
-    def short(n):
-        n = n.replace("(anonymous namespace)::", "")
-        m = re.match(r"void pa::(\w+)<(.*)>\(", n)
-        return f"{m.group(1)}<{m.group(2)}>" if m else n.split("(")[0][:60]
-    names = ["llama3_8b", "llama2_70b_prefix", "long_128k", "verify_int8", "mistral_7b_window",
-             "llama3_8b_fp8"]
-    groups, cur, last, extra = [], None, None, {}
-    for did in sorted(disp):
-        k = short(disp[did]["name"])
-        c = disp[did]["c"]
-        if "kv_copy_blocks" in k or "kv_append_quant" in k or k.startswith("paged_attn_kernel"):
-            extra.setdefault(k, []).append(c)
-            continue
-        if "copyBuffer" in k or "elementwise" in k or "fill" in k.lower():
-            last = "copy"
-            continue
-        if k.startswith("paged_attn") and (cur is None or last == "copy"):
-            cur = {}
-            groups.append(cur)
-        last = k
-        if cur is not None:
-            cur.setdefault(k, []).append(c)
-    counters = sorted({cn for d in disp.values() for cn in d["c"]})
-    run_flags = (f"--steps {args.steps} --warmup {args.warmup}" +
-                 (" --no-cpu" if args.no_cpu else "") +
-                 f" --path {args.path} --layout {args.layout}")
-    lines = [f"# rocprofv3 counters: bench.py {run_flags}", "",
+
+def counter_summary(args, pmc_dir, out_name="kernel_counters"):
+    """Markdown summary of one rocprofv3 --pmc run of this script (same flags): per
+    workload and kernel, the mean per-dispatch value of every counter collected (warm-up
+    dispatches left out), and per-wave ratios where the counters allow them."""
+    disp = _pmc_rows(pmc_dir)
+    groups = _grouped(disp)
+    counters = sorted({cn for _, c in disp for cn in c})
+    lines = [f"# rocprofv3 counters: bench.py {_flags(args)}", "",
              "Command (MI355X, one GPU):", "",
              f"    rocprofv3 --pmc {' '.join(counters)} -d {pmc_dir} -o run -- python "
-             f"bench.py {run_flags}",
-             f"    python bench.py {run_flags} --counter-summary {pmc_dir}"
+             f"bench.py {_flags(args)}",
+             f"    python bench.py {_flags(args)} --counter-summary {pmc_dir}"
              f"{'' if out_name == 'kernel_counters' else ' ' + out_name}", "",
              f"Kernel sources sha: {kernel_source_hash()}", "",
              "Mean per dispatch (counters summed over the device). Derived, where collected: "
@@ -761,27 +864,83 @@ def counter_summary(args, pmc_dir, out_name="kernel_counters"):
              "| workload | kernel | dispatches | " + " | ".join(counters) +
              " | VALU/wave | MFMA/wave | VALU issue |",
              "|---|---|---|" + "---|" * (len(counters) + 3)]
-
-    def row(label, k, cs):
-        mean = {cn: float(np.mean([c.get(cn, 0.0) for c in cs])) for cn in counters}
-        w = mean.get("SQ_WAVES", 0.0)
-        der = [f"{mean['SQ_INSTS_VALU'] / w:.0f}" if w and "SQ_INSTS_VALU" in mean else "",
-               f"{mean['SQ_INSTS_MFMA'] / w:.0f}" if w and "SQ_INSTS_MFMA" in mean else "",
-               f"{mean['SQ_ACTIVE_INST_VALU'] / mean['SQ_WAVE_CYCLES']:.3f}"
-               if mean.get("SQ_WAVE_CYCLES") and "SQ_ACTIVE_INST_VALU" in mean else ""]
-        lines.append(f"| {label} | `{k}` | {len(cs)} | " +
-                     " | ".join(f"{mean[cn]:.4g}" for cn in counters) + " | " +
-                     " | ".join(der) + " |")
-    for name, g in zip(names, groups):
-        skip = args.warmup if name == names[0] else 3
+    for name, g in groups:
         for k, cs in g.items():
-            row(name, k, cs[skip:] if len(cs) > skip else cs)
-    for k, cs in extra.items():
-        row("(other)", k, cs[3:] if len(cs) > 3 else cs)
+            w = _warm(name, args)
+            cs = cs[w:] if len(cs) > w else cs
+            mean = {cn: float(np.mean([c.get(cn, 0.0) for c in cs])) for cn in counters}
+            wv = mean.get("SQ_WAVES", 0.0)
+            der = [f"{mean['SQ_INSTS_VALU'] / wv:.0f}" if wv and "SQ_INSTS_VALU" in mean else "",
+                   f"{mean['SQ_INSTS_MFMA'] / wv:.0f}" if wv and "SQ_INSTS_MFMA" in mean else "",
+                   f"{mean['SQ_ACTIVE_INST_VALU'] / mean['SQ_WAVE_CYCLES']:.3f}"
+                   if mean.get("SQ_WAVE_CYCLES") and "SQ_ACTIVE_INST_VALU" in mean else ""]
+            lines.append(f"| {name} | `{k}` | {len(cs)} | " +
+                         " | ".join(f"{mean[cn]:.4g}" for cn in counters) + " | " +
+                         " | ".join(der) + " |")
     out = os.path.join(ROOT, "profiles", f"{out_name}.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def pmc_summary(args, fetch_dir, write_dir):
+    """profiles/hbm_traffic.json from two rocprofv3 --pmc runs of this script with
+    --calibrate (FETCH_SIZE, then WRITE_SIZE): per workload, the attention kernel's and the
+    merge's HBM bytes per launch, each counter scaled by what it reads for the 1 GiB
+    calibration copy (copy bytes / counter bytes)."""
+    copy_bytes = 1 << 30
+
+    def load(d, counter):
+        disp = _pmc_rows(d)
+        cal = [c[counter] for n, c in disp if "copyBuffer" in n and counter in c][:3]
+        scale = copy_bytes / (float(np.mean(cal)) * 1024)
+        res = {}
+        for name, g in _grouped(disp):
+            for k, cs in g.items():
+                w = _warm(name, args)
+                cs = cs[w:] if len(cs) > w else cs
+                role = ("attn" if k.startswith("paged_attn") else
+                        "merge" if "merge" in k else "append" if "append" in k else None)
+                if role is None or counter not in cs[0]:
+                    continue
+                res.setdefault(name, {})[role] = (k, float(np.mean([c[counter] for c in cs])) *
+                                                  1024 * scale, len(cs))
+        return float(np.mean(cal)), scale, res
+    cf, fs, fetch = load(fetch_dir, "FETCH_SIZE")
+    cw, wsc, write = load(write_dir, "WRITE_SIZE")
+    import workloads as W
+    out = {"kernel_source_sha": kernel_source_hash(), "kernel_sources": KERNEL_SOURCES,
+           "calibration": {"copy_bytes": copy_bytes, "FETCH_SIZE_KiB": round(cf, 1),
+                           "WRITE_SIZE_KiB": round(cw, 1), "fetch_scale": round(fs, 5),
+                           "write_scale": round(wsc, 5)},
+           "commands": [
+               f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run -- python bench.py {_flags(args)} --calibrate",
+               f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run -- python bench.py {_flags(args)} --calibrate",
+               f"python bench.py {_flags(args)} --pmc-summary {fetch_dir} {write_dir}"],
+           "workloads": {}}
+    for name in fetch:
+        f, w = fetch[name], write.get(name, {})
+        e = {}
+        for role in ("attn", "merge", "append"):
+            if role in f:
+                e[f"{role}_kernel"] = f[role][0]
+                e[f"{role}_fetch_bytes"] = round(f[role][1])
+                e[f"{role}_write_bytes"] = round(w[role][1]) if role in w else None
+                e[f"{role}_dispatches"] = f[role][2]
+        e["step_traffic_bytes"] = sum(v for k, v in e.items()
+                                      if k.endswith(("_fetch_bytes", "_write_bytes")) and v)
+        base = name[:-len("_split")] if name.endswith("_split") else name
+        if base in W.CONFIGS:
+            e["algorithmic_kv_bytes"] = W.generate(base, poison=False).kv_bytes()
+        out["workloads"][name] = e
+    with open(os.path.join(ROOT, "profiles", TRAFFIC_FILE), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+KERNEL_NAME = {"step": "paged_attn_balanced_kernel (decode step: append folded in)",
+               "balanced": "paged_attn_balanced_kernel",
+               "split": "paged_attn_kernel (split)", "direct": "paged_attn_kernel (direct)"}
 
 
 def main():
@@ -808,47 +967,67 @@ def main():
     if args.calibrate:
         calibration_copy(torch)
 
+    # ---- headline: the Llama-3-8B decode step (c2) --------------------------------------
+    mark(torch)
     main_name = "llama3_8b"
     wl = W.generate(main_name, poison=False)
     part = args.partition or PARTITION[main_name]
     r = Runner(P, wl, args.path, part, workgroups=args.workgroups, layout=args.layout)
-    res = summarize(wl, *_m(r, args))
-    G = getattr(r, "G", None)
+    wall, attn, merge = r.measure(args.steps, args.warmup, args.event_steps)
+    log(f"{main_name} {args.path}: {wall / args.steps * 1e6:.2f} us/step, attention "
+        f"{attn.mean():.2f} us, merge {merge.mean():.2f} us")
+    configs = {}
+    configs["c2"], _, _ = config_entry(P, torch, W, "c2", main_name, args.path, args,
+                                       main=(r, wall, attn, merge))
+    res = summarize(wl, wall, args.steps, attn, merge)
     del r
     torch.cuda.empty_cache()
 
     others = {}
     if not args.no_others:
-        for name in ("llama2_70b_prefix", "long_128k", "verify_int8", "mistral_7b_window",
-                     "llama3_8b_fp8"):
-            w2 = W.generate(name, poison=False)
-            copies = 1 if name == "long_128k" else 2
-            r2 = Runner(P, w2, "step", None, copies=copies, layout=args.layout)
-            s = summarize(w2, *_m(r2, args, steps=min(args.steps, 40), warmup=3))
-            s["path"] = r2.path
-            s["layout"] = args.layout
-            s["workgroups"] = r2.G
-            s["pct_hbm_peak"] = s["kv_GBps"] / HBM_PEAK_GBS * 100
-            s["attn_kernel_frac_of_peak"] = s["attn_kernel_GBps"] / HBM_PEAK_GBS
-            if w2.cfg.shared_groups:
-                # shared prefix: the bytes of distinct physical blocks (each read once from
-                # HBM at best) beside the logical bytes every sequence attends
-                c2 = w2.cfg
-                elem = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1}[c2.kv_dtype]
-                ub = int(w2.occupancy.sum()) * 2 * c2.num_kv_heads * c2.head_dim * elem
-                s["unique_kv_bytes"] = ub
-                s["unique_attn_kernel_GBps"] = ub / (s["attn_kernel_us_mean"] * 1e-6) / 1e9
-            others[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in s.items()}
-            del r2, w2
+        mark(torch)
+        kv_app = append_entry(P, torch, W, max(args.steps, 20))
+        configs["c1"], r1, _ = config_entry(P, torch, W, "c1", "tiny_fp32", "step", args)
+        configs["c1"]["kv_append"] = kv_app
+        del r1
+        log(f"c1 done: {configs['c1']['us_per_step']:.2f} us/step, kv_append "
+            f"{kv_app['us_per_launch']} us")
+        for label, name in (("c3", "llama2_70b_prefix"), ("c4", "long_128k")):
+            mark(torch)
+            configs[label], rr, _ = config_entry(P, torch, W, label, name, "step", args)
+            del rr
             torch.cuda.empty_cache()
-
+            log(f"{label} done: {configs[label]['us_per_step']:.2f} us/step")
+        mark(torch)
+        configs["c4"]["split"] = split_entry(P, torch, W, "long_128k", args)
+        log(f"c4 split done: partition {configs['c4']['split']['partition_tokens']}, "
+            f"{configs['c4']['split']['us_per_step']:.2f} us/step")
+        mark(torch)
+        configs["c5"], rr, _ = config_entry(P, torch, W, "c5", "verify_int8", "step", args)
+        del rr
+        torch.cuda.empty_cache()
+        log(f"c5 done: {configs['c5']['us_per_step']:.2f} us/step")
+        for name in ("mistral_7b_window", "llama3_8b_fp8"):
+            mark(torch)
+            others[name], rr, _ = config_entry(P, torch, W, name, name, "step", args)
+            del rr
+            torch.cuda.empty_cache()
+            log(f"{name} done")
+        mark(torch)
         others["kv_copy_blocks"] = copy_blocks_bench(P, torch, W, min(args.steps, 40))
+        mark(torch)
         others["kv_append_quant"] = append_quant_bench(P, torch, W, min(args.steps, 40))
         for name in ("prefill_chunk", "tree_verify"):
+            mark(torch)
             others[name] = multi_query_bench(P, torch, W, name, min(args.steps, 20))
+        log("others done")
 
+    c2 = configs["c2"]
+    tr = measured_traffic(main_name if args.path != "split" else main_name + "_split")
+    traffic = None
+    if tr is not None and tr.get("attn_fetch_bytes") is not None:
+        traffic = tr["attn_fetch_bytes"] + (tr.get("attn_write_bytes") or 0)
     achieved = res["attn_kernel_GBps"]
-    kernel = KERNEL_NAME[args.path]
     line = {
         "metric": METRIC,
         "value": round(res["kv_GBps"], 2),
@@ -865,20 +1044,26 @@ def main():
         "config": {"workload": "llama3_8b_layer_decode", "batch": 64, "q_heads": 32,
                    "kv_heads": 8, "head_dim": 128, "block_size": 16, "kv_dtype": "bf16",
                    "context": "uniform [512, 4096] (+ the appended token)", "seed": 1001,
-                   "path": args.path, "layout": args.layout, "workgroups": G,
+                   "path": args.path, "layout": args.layout, "workgroups": c2["workgroups"],
                    "partition_tokens": part if args.path == "split" else None,
                    "kv_bytes_per_step": res["kv_bytes"]},
         "us_per_step": round(res["us_per_step"], 2),
-        "pct_hbm_peak": round(res["kv_GBps"] / HBM_PEAK_GBS * 100, 2),
+        "pct_hbm_peak": round(res["pct_hbm_peak"], 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.path, args.layout),
-                     "kernel": kernel, "kernel_us_mean": round(res["attn_kernel_us_mean"], 2),
+                     "traffic": traffic, "kernel": KERNEL_NAME[args.path],
+                     "kernel_us_mean": round(res["attn_kernel_us_mean"], 2),
                      "bytes_per_launch": res["kv_bytes"]},
-        "timing": dict({k: round(v, 3) for k, v in res.items() if k.endswith("_us_mean") or
-                        k.endswith("_us_median") or k.endswith("_us_p95")},
-                       attn_kernel_samples=res["attn_kernel_samples"],
-                       event_every=args.event_every),
+        # the step as the task defines it: the attention call and its merge together
+        "step_roofline": {"achieved": round(res["kernels_GBps"], 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(res["kernels_GBps"] / HBM_PEAK_GBS, 4),
+                          "kernels_us_mean": round(res["kernels_us_mean"], 2),
+                          "traffic": None if tr is None else tr.get("step_traffic_bytes")},
+        "timing": {k: round(res[k], 3) for k in ("attn_kernel_us_mean", "attn_kernel_us_median",
+                                                 "attn_kernel_us_p95", "merge_us_mean",
+                                                 "merge_us_p95", "kernels_us_mean")}
+                  | {"event_samples": res["event_samples"]},
+        "configs": configs,
         "others": others,
     }
     if not args.no_cpu:
@@ -886,13 +1071,6 @@ def main():
         if not args.no_others:
             line["cpu_oracle_others"] = cpu_oracle_others(W)
     print(json.dumps(line), flush=True)
-
-
-def _m(r, args, steps=None, warmup=None):
-    steps = args.steps if steps is None else steps
-    warmup = args.warmup if warmup is None else warmup
-    wall, attn = r.measure(steps, warmup, args.event_every)
-    return (wall, steps, attn)
 
 
 if __name__ == "__main__":

@@ -993,6 +993,9 @@ constexpr int kWaitVmem0 = 0x0F70;
 #ifndef PA_BAL_WAVES_PER_EU
 #define PA_BAL_WAVES_PER_EU 2
 #endif
+#ifndef PA_BAL_PRIO
+#define PA_BAL_PRIO 1
+#endif
 template <class KV, int NT> struct BalancedWavesPerEU {
   static constexpr int value = WavesPerEU<KV, NT>::value < PA_BAL_WAVES_PER_EU
                                    ? WavesPerEU<KV, NT>::value
@@ -1228,8 +1231,26 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     KV::load_k(kk, kbase + tl * tile_bytes, lane);
     KV::load_v(vv, vbase + tl * tile_bytes, row16, grp);
   };
+  // Issue priority by progress: two waves sharing a SIMD (two workgroups per compute unit)
+  // would otherwise be served oldest first, so the younger one streams far behind and ends
+  // alone with half the loads in flight.  A wave's user priority drops by one at each
+  // quarter of its slice, so whichever wave is behind is issued first.
+  int quarter = -1;
+  auto set_priority = [&](int k) {
+    if constexpr (PA_BAL_PRIO) {
+      const int q4 = (int)(((int64_t)4 * k) / (n > 0 ? n : 1));
+      if (q4 != quarter) {
+        quarter = q4;
+        if (q4 == 0) __builtin_amdgcn_s_setprio(3);
+        else if (q4 == 1) __builtin_amdgcn_s_setprio(2);
+        else if (q4 == 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
+    }
+  };
   auto consume = [&](typename KV::K& kk, typename KV::V& vv, int k, const Slot& sl) {
     if (k >= n) return;
+    set_priority(k);
     const int x = x0 + k;
     if (x >= cur.end) {
       if (cur.j >= 0) finish();
