@@ -68,9 +68,10 @@ TOL = {"f32": 1e-5, "bf16": 2e-3, "i8": 4e-3, "fp8": 4e-3}
 # Workloads in the order the bench runs them; each starts with a separator kernel (mark),
 # which is how the profiler summaries tell them apart.  (name, warm-up launches of its
 # kernels before the timed ones)
-ORDER = ["llama3_8b", "tiny_fp32", "llama2_70b_prefix", "long_128k", "long_128k_split",
-         "verify_int8", "mistral_7b_window", "llama3_8b_fp8", "kv_copy_blocks",
-         "kv_append_quant", "prefill_chunk", "tree_verify"]
+ORDER = ["llama3_8b", "tiny_fp32", "llama2_70b_prefix", "long_128k",
+         "long_128k_split_candidates", "long_128k_split", "verify_int8", "mistral_7b_window",
+         "llama3_8b_fp8", "kv_copy_blocks_2048", "kv_copy_blocks_64", "kv_append_quant",
+         "prefill_chunk", "tree_verify"]
 
 
 def parse():
@@ -214,16 +215,17 @@ class Runner:
             nbytes = P.paged_attn_balanced_workspace_bytes(self.dims, c.num_q_pos, self.G)
             self.ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
 
-    def step(self, i, ev=None):
-        """One step.  With ev = (e0, e1, e2), HIP events bracket the attention kernel
-        (e0 .. e1) and the merge (e1 .. e2); the append of the non-fused paths is left
-        outside them."""
+    def append_part(self, i):
+        """The separate kv_append of the non-fused paths (nothing for the decode step)."""
+        c = self.wl.cfg
+        kc, vc, _, _ = self.pools[i % len(self.pools)]
+        if self.append and self.path != "step":
+            self.P.kv_append(self.dims, self.k_new, self.v_new, self.slots, c.batch, kc, vc)
+
+    def attention(self, i):
+        """The attention kernel of step i (for the decode step, with the append folded in)."""
         P, c = self.P, self.wl.cfg
         kc, vc, ks, vs = self.pools[i % len(self.pools)]
-        if self.append and self.path != "step":
-            P.kv_append(self.dims, self.k_new, self.v_new, self.slots, c.batch, kc, vc)
-        if ev is not None:
-            ev[0].record()
         if self.path == "step":
             P.paged_decode_step(self.dims, self.q, self.k_new, self.v_new, kc, vc, self.tables,
                                 self.lens, self.sm, self.G, self.ws, self.out)
@@ -236,20 +238,35 @@ class Runner:
         else:
             P.paged_verify_attn(self.dims, c.num_q_pos, self.q, kc, vc, ks, vs, self.tables,
                                 self.lens, self.sm, self.out)
-        if ev is not None:
-            ev[1].record()
+
+    def merge(self, i=0):
+        """The merge that completes the step (nothing for the single-pass kernel)."""
+        P, c = self.P, self.wl.cfg
         if self.path in ("step", "balanced"):
             P.paged_attn_balanced_merge(self.dims, c.num_q_pos, self.G, self.ws, self.out)
         elif self.split:
             P.lse_merge(self.dims, self.part_out, self.part_lse, self.lens, self.pt, self.maxp,
                         self.out)
+
+    def step(self, i, ev=None):
+        """One step; with ev = (e0, e1, e2), HIP events bracket its attention kernel
+        (e0 .. e1) and its merge (e1 .. e2); the separate append stays outside them."""
+        self.append_part(i)
+        if ev is not None:
+            ev[0].record()
+        self.attention(i)
+        if ev is not None:
+            ev[1].record()
+        self.merge()
         if ev is not None:
             ev[2].record()
 
     def measure(self, steps, warmup, event_steps):
         """Wall time of exactly `steps` steps with nothing else in between, then a separate
-        pass of `event_steps` steps with the attention kernel and the merge of each step
-        bracketed by events.  Returns (wall seconds, attention us array, merge us array)."""
+        pass of `event_steps` steps with the attention kernel and the merge of every step
+        bracketed by events (a bracket adds ~1 us to what it measures; kernels launched
+        back to back instead would run into dispatch gaps of the short merge and measure
+        those).  Returns (wall seconds, attention us array, merge us array)."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
@@ -290,6 +307,7 @@ def summarize(wl, wall, steps, attn, merge):
         "merge_us_mean": float(merge.mean()),
         "merge_us_p95": pct(merge, 0.95),
         "kernels_us_mean": float(kern.mean()),
+        "kernels_us_p95": pct(kern, 0.95),
         "attn_kernel_GBps": kv / (attn.mean() * 1e-6) / 1e9,
         "kernels_GBps": kv / (kern.mean() * 1e-6) / 1e9,
         "event_samples": len(attn),
@@ -364,10 +382,10 @@ def config_entry(P, torch, W, label, name, path, args, partition=None, main=None
     copies = 1 if name == "long_128k" else 2
     if main is None:
         r = Runner(P, wl, path, partition, copies=copies)
-        wall, attn, merge = r.measure(args.steps, 3, args.event_steps)
+        meas = r.measure(args.steps, 3, args.event_steps)
     else:
-        r, wall, attn, merge = main
-    s = summarize(wl, wall, args.steps, attn, merge)
+        r, meas = main
+    s = summarize(wl, meas[0], args.steps, *meas[1:])
     c = wl.cfg
     e = {"workload": name, "path": r.path, "workgroups": r.G,
          "partition_tokens": r.pt, "kv_dtype": c.kv_dtype, "batch": c.batch,
@@ -414,6 +432,7 @@ def split_entry(P, torch, W, name, args):
         del r
         torch.cuda.empty_cache()
     best = min(cand, key=cand.get)
+    mark(torch)   # the chosen size, measured in full, is a workload of its own in the traces
     e, r, _ = config_entry(P, torch, W, "split", name, "split", args, partition=best)
     e["candidates_us"] = {str(k): v for k, v in cand.items()}
     del r
@@ -467,6 +486,7 @@ def copy_blocks_bench(P, torch, W, steps):
     pairs = W.copy_pairs(wl, 4096, seed=3).to(dev)
     res = {}
     for label, n in (("bulk", 2048), ("cow_step", c.batch)):
+        mark(torch)    # each copy size is a workload of its own in the traces
         sets = [pairs[:n].contiguous(), pairs[2048:2048 + n].contiguous()]
         for i in range(4):
             P.kv_copy_blocks(dims, sets[i % 2], n, comb, vptr)
@@ -799,12 +819,16 @@ def _grouped(rows):
 
 
 def _warm(name, args):
-    return args.warmup if name == ORDER[0] else 3
+    """Warm-up launches of each kernel of a workload, left out of the summaries."""
+    if name == ORDER[0]:
+        return args.warmup
+    return 4 if name.startswith("kv_copy_blocks") else 3
 
 
 def _flags(args):
     return (f"--steps {args.steps} --warmup {args.warmup} --event-steps {args.event_steps}" +
-            (" --no-cpu" if args.no_cpu else "") + f" --path {args.path} --layout {args.layout}")
+            (" --no-cpu" if args.no_cpu else "") + (" --calibrate" if args.calibrate else "") +
+            f" --path {args.path} --layout {args.layout}")
 
 
 def trace_summary(args, trace_dir):
@@ -914,8 +938,8 @@ def pmc_summary(args, fetch_dir, write_dir):
                            "WRITE_SIZE_KiB": round(cw, 1), "fetch_scale": round(fs, 5),
                            "write_scale": round(wsc, 5)},
            "commands": [
-               f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run -- python bench.py {_flags(args)} --calibrate",
-               f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run -- python bench.py {_flags(args)} --calibrate",
+               f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run -- python bench.py {_flags(args)}",
+               f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run -- python bench.py {_flags(args)}",
                f"python bench.py {_flags(args)} --pmc-summary {fetch_dir} {write_dir}"],
            "workloads": {}}
     for name in fetch:
@@ -973,13 +997,13 @@ def main():
     wl = W.generate(main_name, poison=False)
     part = args.partition or PARTITION[main_name]
     r = Runner(P, wl, args.path, part, workgroups=args.workgroups, layout=args.layout)
-    wall, attn, merge = r.measure(args.steps, args.warmup, args.event_steps)
-    log(f"{main_name} {args.path}: {wall / args.steps * 1e6:.2f} us/step, attention "
-        f"{attn.mean():.2f} us, merge {merge.mean():.2f} us")
+    meas = r.measure(args.steps, args.warmup, args.event_steps)
+    log(f"{main_name} {args.path}: {meas[0] / args.steps * 1e6:.2f} us/step, attention "
+        f"{meas[1].mean():.2f} us, merge {meas[2].mean():.2f} us")
     configs = {}
     configs["c2"], _, _ = config_entry(P, torch, W, "c2", main_name, args.path, args,
-                                       main=(r, wall, attn, merge))
-    res = summarize(wl, wall, args.steps, attn, merge)
+                                       main=(r, meas))
+    res = summarize(wl, meas[0], args.steps, *meas[1:])
     del r
     torch.cuda.empty_cache()
 
@@ -1013,7 +1037,6 @@ def main():
             del rr
             torch.cuda.empty_cache()
             log(f"{name} done")
-        mark(torch)
         others["kv_copy_blocks"] = copy_blocks_bench(P, torch, W, min(args.steps, 40))
         mark(torch)
         others["kv_append_quant"] = append_quant_bench(P, torch, W, min(args.steps, 40))
@@ -1061,7 +1084,8 @@ def main():
                           "traffic": None if tr is None else tr.get("step_traffic_bytes")},
         "timing": {k: round(res[k], 3) for k in ("attn_kernel_us_mean", "attn_kernel_us_median",
                                                  "attn_kernel_us_p95", "merge_us_mean",
-                                                 "merge_us_p95", "kernels_us_mean")}
+                                                 "merge_us_p95", "kernels_us_mean",
+                                                 "kernels_us_p95")}
                   | {"event_samples": res["event_samples"]},
         "configs": configs,
         "others": others,
