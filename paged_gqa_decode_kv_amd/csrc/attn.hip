@@ -41,18 +41,15 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// K/V tiles are read exactly once per call, so their loads carry the non-temporal hint:
-// on MI355X a streaming read of HBM reaches ~7.0 TB/s with it and ~6.2 TB/s without.
-#ifndef PA_NT_LOADS
-#define PA_NT_LOADS 1
-#endif
-template <typename T>
+// Where a K/V tile is read once per call (decode: one row tile per sequence and KV head),
+// its loads carry the non-temporal hint: on MI355X a streaming read of HBM reaches ~7.0
+// TB/s with it and ~6.2 TB/s without.  Where several workgroups read the same tiles (the
+// row tiles of multi-query rows), plain loads let the second and later reads hit L2: the
+// hint kept them from it (candidate-tree verify read 2.6x its unique bytes from HBM).
+template <typename T, bool NTL = true>
 __device__ __forceinline__ T stream_load(const void* p) {
-#if PA_NT_LOADS
-  return __builtin_nontemporal_load(static_cast<const T*>(p));
-#else
-  return *static_cast<const T*>(p);
-#endif
+  if constexpr (NTL) return __builtin_nontemporal_load(static_cast<const T*>(p));
+  else return *static_cast<const T*>(p);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -84,15 +81,17 @@ struct Bf16Kv {
     }
   }
   // lane (token row16, grp) step kk: column 4*kk + grp of the K tile, at kk*1 KiB + lane*16
+  template <bool NTL = true>
   __device__ static void load_k(K& k, const void* tile, int lane) {
     const uint8_t* p = static_cast<const uint8_t*>(tile) + lane * 16;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) k.v[kk] = stream_load<u32x4>(p + 1024 * kk);
+    for (int kk = 0; kk < NK; ++kk) k.v[kk] = stream_load<u32x4, NTL>(p + 1024 * kk);
   }
+  template <bool NTL = true>
   __device__ static void load_v(V& v, const void* tile, int row16, int grp) {
     const uint16_t* p = static_cast<const uint16_t*>(tile) + row16 * 16 + 4 * grp;
 #pragma unroll
-    for (int t = 0; t < ND; ++t) v.v[t] = stream_load<u32x2>(p + t * 256);
+    for (int t = 0; t < ND; ++t) v.v[t] = stream_load<u32x2, NTL>(p + t * 256);
   }
   // the loaded tiles are the MFMA operands already
   using KMat = K;
@@ -158,27 +157,38 @@ struct Bf16Kv {
         reinterpret_cast<uint16_t*>(dst + 2 * D)[16 * t + row16] = (uint16_t)n.v[t];
     }
   }
-  // P = hi + lo (two bf16 terms, relative error ~2^-17) so that P.V keeps fp32-class
-  // accuracy.  FOLD: both terms go through one 16x16x32 MFMA, whose 32-long inner dimension
+  // P = hi + lo (two bf16 terms, relative error below 2^-16) so that P.V keeps fp32-class
+  // accuracy: hi is p cut to its top 16 bits (a bf16 value, exact), lo = p - hi (exact in
+  // fp32) rounded to bf16; a byte permute packs two hi halves, a mask and a subtraction give
+  // each lo.  FOLD: both terms go through one 16x16x32 MFMA, whose 32-long inner dimension
   // holds the lane's 4 tokens twice, against hi then lo (sum_k A B = sum_t v_t (hi_t + lo_t)):
   // half the MFMA cycles for the compute-bound multi-query rows, at the cost of a duplicated
   // operand (two more registers, which the register-tight balanced kernels do not have).
   // Otherwise two 16x16x16 MFMAs.
   template <bool FOLD = false>
   __device__ static void pv(f32x4* acc, const V& v, f32x4 p, float /*vfac*/) {
-    bf16x4 hi, lo;
+    // (the elements are copied to scalars before the bit casts: a bit cast applied directly
+    // to a vector element reads element 0)
+    const float pf[4] = {p[0], p[1], p[2], p[3]};
+    uint32_t u[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      hi[e] = (__bf16)p[e];
-      lo[e] = (__bf16)(p[e] - (float)hi[e]);
-    }
+    for (int e = 0; e < 4; ++e) u[e] = __builtin_bit_cast(uint32_t, pf[e]);
+    bf16x2 lo01, lo23;
+    lo01[0] = (__bf16)(pf[0] - __builtin_bit_cast(float, u[0] & 0xFFFF0000u));
+    lo01[1] = (__bf16)(pf[1] - __builtin_bit_cast(float, u[1] & 0xFFFF0000u));
+    lo23[0] = (__bf16)(pf[2] - __builtin_bit_cast(float, u[2] & 0xFFFF0000u));
+    lo23[1] = (__bf16)(pf[3] - __builtin_bit_cast(float, u[3] & 0xFFFF0000u));
+    const u32x2 hi = {__builtin_amdgcn_perm(u[1], u[0], 0x07060302u),
+                      __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
+    const u32x2 lo = {__builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)};
     if constexpr (FOLD) {
-      const bf16x8 hl = {hi[0], hi[1], hi[2], hi[3], lo[0], lo[1], lo[2], lo[3]};
+      const u32x4 hl = {hi.x, hi.y, lo.x, lo.y};
 #pragma unroll
       for (int t = 0; t < ND; ++t) {
         const u32x4 a = {v.v[t].x, v.v[t].y, v.v[t].x, v.v[t].y};
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), hl,
-                                                         acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                         __builtin_bit_cast(bf16x8, hl), acc[t],
+                                                         0, 0, 0);
       }
     } else {
       const s16x4 h = __builtin_bit_cast(s16x4, hi);
@@ -210,15 +220,17 @@ struct F32Kv {
     for (int u = 0; u < NU; ++u)
       q.v[u] = valid ? *reinterpret_cast<const f32x4*>(p + 16 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  template <bool NTL = true>
   __device__ static void load_k(K& k, const void* tile, int lane) {
     const uint8_t* p = static_cast<const uint8_t*>(tile) + lane * 16;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) k.v[u] = stream_load<f32x4>(p + 1024 * u);
+    for (int u = 0; u < NU; ++u) k.v[u] = stream_load<f32x4, NTL>(p + 1024 * u);
   }
+  template <bool NTL = true>
   __device__ static void load_v(V& v, const void* tile, int row16, int grp) {
     const float* p = static_cast<const float*>(tile) + row16 * 16 + 4 * grp;
 #pragma unroll
-    for (int t = 0; t < ND; ++t) v.v[t] = stream_load<f32x4>(p + t * 256);
+    for (int t = 0; t < ND; ++t) v.v[t] = stream_load<f32x4, NTL>(p + t * 256);
   }
   using KMat = K;
   using VMat = V;
@@ -315,10 +327,11 @@ struct I8Kv {
         q.v[2 * h + s] = __builtin_bit_cast(bf16x8, x);
       }
   }
+  template <bool NTL = true>
   __device__ static void load_k(K& k, const void* tile, int lane) {
     const uint8_t* p = static_cast<const uint8_t*>(tile) + lane * 16;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) k.v[h] = stream_load<u32x4>(p + 1024 * h);
+    for (int h = 0; h < NH; ++h) k.v[h] = stream_load<u32x4, NTL>(p + 1024 * h);
   }
   // V is loaded 16 bytes at a time: lane (row16, grp) takes all 16 tokens of dims
   // 16 * (TPG * grp + u) + row16 (u < TPG = ND / 4), one 16-byte row of the [d][16] tile
@@ -328,11 +341,12 @@ struct I8Kv {
   // loads in the operand order issue four times as many load instructions; the 16-byte
   // form measured 3-6% faster on the 8-bit workloads.)
   static constexpr int TPG = ND / 4;
+  template <bool NTL = true>
   __device__ static void load_v(V& v, const void* tile, int row16, int grp) {
     const uint8_t* p = static_cast<const uint8_t*>(tile) + (16 * TPG * grp + row16) * 16;
 #pragma unroll
     for (int u = 0; u < TPG; ++u) {
-      const u32x4 x = stream_load<u32x4>(p + 256 * u);
+      const u32x4 x = stream_load<u32x4, NTL>(p + 256 * u);
       v.v[4 * u] = x.x;
       v.v[4 * u + 1] = x.y;
       v.v[4 * u + 2] = x.z;
@@ -486,16 +500,20 @@ struct Rows {
   static constexpr bool kScaled = Scaled8<KV>::value;
   f32x4 acc[NT][ND];
   float m[NT], l[NT];
+  float nmu[NT];  // -m, or 0 while m is -inf: the exponent offset of the weights
+  bool big;       // some reference of the wave is 2^20 or more in magnitude
   float v_ref, inv_vref256;
 
   __device__ __forceinline__ void reset(float vref) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       m[nt] = -INFINITY;
+      nmu[nt] = 0.f;
       l[nt] = 0.f;
 #pragma unroll
       for (int t = 0; t < ND; ++t) acc[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    big = false;
     v_ref = kScaled ? vref : 1.f;
     inv_vref256 = kScaled ? 256.f / vref : 1.f;
   }
@@ -532,79 +550,97 @@ struct Rows {
     }
     // (one uniform test: blocks inside every row's range skip the per-token masks)
     const bool need_mask = tok0 + kBlockTokens > lim_min || (SW && tok0 < lo_max);
+    // The scores stay unscaled until the exponent: the scale (positive, so the maximum of
+    // the scaled scores is the scaled maximum, rounding included) enters the row maximum
+    // once per row and each weight through one fused multiply-add, exp2(s * sc - m).  A
+    // zero scale (an 8-bit block whose K scale is 0) is raised to the smallest normal
+    // float, which leaves every product with a finite score at 0 to fp32 precision and keeps
+    // a masked score's -inf an -inf.  The fused form differs from the rounded product
+    // minus m by less than an ulp of m, which stays far below 1 while every reference of
+    // the wave is below 2^20 in magnitude; beyond that (scores at the fp32 limits) the
+    // weights take the rounded product, as the maximum does, so that the largest weight
+    // is exactly 1.
+    const float scp = fmaxf(sc, 1.17549435e-38f);
     f32x4 pr[NT];
+    float lm[NT];
     const auto& km = KV::k_mat(kk);
     // Lazy reference: a row's reference m moves only when a score of the block exceeds it
     // by more than KV::kLazy (log2 units), so the weights exp2(s - m) stay below 2^kLazy
     // and most blocks skip the rescale of the accumulators.  Softmax does not depend on
-    // the reference, so the result is the same up to rounding.
+    // the reference, so the result is the same up to rounding.  Whether the block moves
+    // any reference is decided from each lane's own 4 scores; the row maximum is reduced
+    // across the row's four lanes only when it does.
     bool move = false;
-    if constexpr (!TREE) {
-      // Blocks inside every row's range skip the per-token tests (four instructions a
-      // score) in a wave-wide branch, and whether the block moves any reference is decided
-      // from each lane's own 4 scores, so the row maximum is reduced across the row's four
-      // lanes only when it does.
+    // The lane's maximum is taken right after the MFMAs, in the same basic block: there the
+    // wait states a VALU read of an MFMA result needs are counted exactly, while a first
+    // read placed behind a branch was seen to get too few (stale maxima, run-to-run
+    // differences in the last bits).  Masked blocks take it again after the masks.
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) pr[nt] = KV::qk(km, qop[nt]) * sc;
-      if (__any(need_mask)) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = tok0 + 4 * grp + e;
-            if (t >= lim[nt] || (SW && t < lo[nt])) pr[nt][e] = -INFINITY;
-          }
-      }
+    for (int nt = 0; nt < NT; ++nt) {
+      pr[nt] = KV::qk(km, qop[nt]);
+      lm[nt] = fmaxf(fmaxf(pr[nt][0], pr[nt][1]), fmaxf(pr[nt][2], pr[nt][3]));
+    }
+    // blocks inside every row's range skip the per-token tests (a wave-wide branch)
+    if (__any(need_mask)) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float lm = fmaxf(fmaxf(pr[nt][0], pr[nt][1]), fmaxf(pr[nt][2], pr[nt][3]));
-        move |= lm > m[nt] + KV::kLazy;
-      }
-    } else {
-      // candidate masks: every row's maximum is reduced on every block (measured faster
-      // here than the branch above: the mask words keep the register budget tight)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 sv = KV::qk(km, qop[nt]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float x = sv[e] * sc;
-          if (need_mask) {
-            const int t = tok0 + 4 * grp + e;
-            if (t >= lim[nt]) x = -INFINITY;
+          const int t = tok0 + 4 * grp + e;
+          bool hide = t >= lim[nt] || (SW && t < lo[nt]);
+          if constexpr (TREE) {
+            // candidates: visible only where the row's mask bit is set
             const int j = t - tr.base;
             if (j >= 0) {
               const uint32_t wd = j < 32 ? tr.w[nt][0]
                                          : (j < 64 ? tr.w[nt][1] : (j < 96 ? tr.w[nt][2] : tr.w[nt][3]));
-              if (((wd >> (j & 31)) & 1u) == 0u) x = -INFINITY;
+              hide |= ((wd >> (j & 31)) & 1u) == 0u;
             }
           }
-          sv[e] = x;
+          if (hide) pr[nt][e] = -INFINITY;
         }
-        pr[nt] = sv;
-        const float bm = wave_max_across_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-        move |= bm > m[nt] + KV::kLazy;
-      }
-    }
-    if (__any(move)) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float lm = fmaxf(fmaxf(pr[nt][0], pr[nt][1]), fmaxf(pr[nt][2], pr[nt][3]));
-        const float mn = fmaxf(m[nt], wave_max_across_groups(lm));
-        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[nt] - mn);
-        m[nt] = mn;
-        l[nt] *= alpha;
-#pragma unroll
-        for (int t = 0; t < ND; ++t) acc[nt][t] *= alpha;
+        lm[nt] = fmaxf(fmaxf(pr[nt][0], pr[nt][1]), fmaxf(pr[nt][2], pr[nt][3]));
       }
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float mu = m[nt] == -INFINITY ? 0.f : m[nt];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pr[nt][e] = __builtin_amdgcn_exp2f(pr[nt][e] - mu);
-      l[nt] += (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
+      lm[nt] *= scp;
+      move |= lm[nt] > m[nt] + KV::kLazy;
     }
+    if (__any(move)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float mn = fmaxf(m[nt], wave_max_across_groups(lm[nt]));
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[nt] - mn);
+        m[nt] = mn;
+        nmu[nt] = mn == -INFINITY ? 0.f : -mn;
+        l[nt] *= alpha;
+#pragma unroll
+        for (int t = 0; t < ND; ++t) acc[nt][t] *= alpha;
+      }
+      bool b = false;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) b |= m[nt] != -INFINITY && fabsf(m[nt]) >= 1048576.f;
+      big = __any(b);
+    }
+    if (!big) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[nt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(pr[nt][e], scp, nmu[nt]));
+    } else {
+      // (two roundings on purpose: the product must not be contracted into the addition)
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = pr[nt][e] * scp;
+          pr[nt][e] = __builtin_amdgcn_exp2f(x + nmu[nt]);
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) l[nt] += (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
     if (tok0 + kBlockTokens > hi) KV::mask_v(vv, hi - tok0, grp);
     const auto& vm = KV::v_mat(vv);
 #pragma unroll
@@ -726,7 +762,8 @@ __device__ __forceinline__ void write_rows(const AttnArgs& a, const Rows<KV, D, 
 // `slot` is the partition index (split mode).  SW: a sliding window is in force (each row
 // also has a first visible token).  Every wave of the workgroup must call this together
 // (it contains barriers).
-template <class KV, int D, int NT, int W, int NBUF, bool SW, bool TREE = false, int RG = 1>
+template <class KV, int D, int NT, int W, int NBUF, bool SW, bool TREE = false, int RG = 1,
+          bool REUSE = false>
 __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int b, int g, int rg,
                                             int L, int lo, int hi, int64_t slot) {
   constexpr int ND = D / 16;
@@ -824,8 +861,8 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, OutMode mode, int
   // blocks stay in flight while one is consumed.
   auto issue = [&](typename KV::K& kk, typename KV::V& vv, int ph) {
     const int64_t tl = kv_tile(ph >= 0 ? ph : 0, g, a.num_kv_heads);
-    KV::load_k(kk, kbase + tl * tile_bytes, lane);
-    KV::load_v(vv, vbase + tl * tile_bytes, row16, grp);
+    KV::template load_k<!REUSE>(kk, kbase + tl * tile_bytes, lane);
+    KV::template load_v<!REUSE>(vv, vbase + tl * tile_bytes, row16, grp);
   };
   auto consume = [&](typename KV::K& kk, typename KV::V& vv, int kidx, const Slot& sl) {
     if (sl.ph < 0) return;
@@ -926,7 +963,9 @@ template <class KV, int NT> struct WavesPerEU {
 // Direct and split modes: one unit per (KV head, sequence, row group, partition).
 // TREE: multi-query rows whose candidates are filtered by a visibility mask (direct mode).
 // RG > 1: each workgroup serves RG row tiles of its (sequence, KV head) (multi-query rows).
-template <class KV, int D, int NT, int W, int NBUF, bool SW, bool TREE = false, int RG = 1>
+// REUSE: several workgroups read each tile (plain loads, which L2 keeps).
+template <class KV, int D, int NT, int W, int NBUF, bool SW, bool TREE = false, int RG = 1,
+          bool REUSE = false>
 __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(WavesPerEU<KV, NT>::value)))
 void paged_attn_kernel(AttnArgs a) {
   const int nrg = (a.rows + 16 * NT * RG - 1) / (16 * NT * RG);  // (groups of) row tiles
@@ -957,8 +996,8 @@ void paged_attn_kernel(AttnArgs a) {
     lo = lo > w0 ? lo : w0;
     if (hi < lo) hi = lo;  // lo is a multiple of 16 here, so the unit reads no block
   }
-  attend_unit<KV, D, NT, W, NBUF, SW, TREE, RG>(a, a.split ? kSplit : kDirect, b, g, rg, L, lo,
-                                                hi, p);
+  attend_unit<KV, D, NT, W, NBUF, SW, TREE, RG, REUSE>(a, a.split ? kSplit : kDirect, b, g, rg,
+                                                       L, lo, hi, p);
 }
 
 // Balanced mode.  All (segment, block) pairs of the batch are laid out in one flat list --
@@ -1341,12 +1380,21 @@ int launch_one(const AttnArgs& a, void* stream) {
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg * a.max_parts;
   const int64_t grid = (units + 7) / 8 * 8;
   if (grid > 0x7fffffff) return PA_ERR_DIMS;
-  if (a.window > 0)
-    hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, true>), dim3((unsigned)grid),
-                       dim3(kWave * W), 0, static_cast<hipStream_t>(stream), a);
-  else
-    hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, false>), dim3((unsigned)grid),
-                       dim3(kWave * W), 0, static_cast<hipStream_t>(stream), a);
+  const dim3 gr((unsigned)grid), bl(kWave * W);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // several row tiles of a (sequence, KV head) read the same blocks (multi-query rows)
+  const bool reuse = nrg > 1;
+  if (a.window > 0) {
+    if (reuse)
+      hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, true, false, 1, true>), gr, bl, 0, st, a);
+    else
+      hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, true>), gr, bl, 0, st, a);
+  } else {
+    if (reuse)
+      hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, false, false, 1, true>), gr, bl, 0, st, a);
+    else
+      hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, false>), gr, bl, 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -1396,9 +1444,11 @@ int occupancy_one() {
 #endif
 
 // multi-query rows with a candidate mask: two row tiles per wave, PA_TREE_RG such row
-// tiles per workgroup
+// tiles per workgroup (measured on MI355X, candidate-tree verify batch 32 x 64 rows: one
+// tile 230 us, two 238 us, four 244 us, once plain loads let L2 serve the re-reads; two
+// were faster while the loads bypassed it)
 #ifndef PA_TREE_RG
-#define PA_TREE_RG 2
+#define PA_TREE_RG 1
 #endif
 template <class KV, int D, int NBUF>
 int launch_tree_one(const AttnArgs& a, void* stream) {
@@ -1407,9 +1457,14 @@ int launch_tree_one(const AttnArgs& a, void* stream) {
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg;
   const int64_t grid = (units + 7) / 8 * 8;
   if (grid > 0x7fffffff) return PA_ERR_DIMS;
-  hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, false, true, RG>),
-                     dim3((unsigned)grid), dim3(kWave * W), 0, static_cast<hipStream_t>(stream),
-                     a);
+  if (nrg > 1)
+    hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, false, true, RG, true>),
+                       dim3((unsigned)grid), dim3(kWave * W), 0, static_cast<hipStream_t>(stream),
+                       a);
+  else
+    hipLaunchKernelGGL((paged_attn_kernel<KV, D, NT, W, NBUF, false, true, RG>),
+                       dim3((unsigned)grid), dim3(kWave * W), 0, static_cast<hipStream_t>(stream),
+                       a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
