@@ -530,6 +530,29 @@ struct Rows {
                                          const int* lo, int lo_max, const TreeRows<NT>& tr,
                                          int hi, typename KV::K& kk, typename KV::V& vv,
                                          int tok0, float sc, float vs, int grp) {
+    f32x4 pr[NT];
+    const auto& km = KV::k_mat(kk);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) pr[nt] = KV::qk(km, qop[nt]);
+    consume<SW, TREE, FOLD>(pr, lim, lim_min, lo, lo_max, tr, hi, vv, tok0, sc, vs, grp);
+  }
+
+  // The same for a block whose raw scores q.K (unscaled) are already in pr (they are
+  // overwritten).
+  template <bool SW, bool TREE = false, bool FOLD = false>
+  __device__ __forceinline__ void consume(f32x4* pr, const int* lim, int lim_min, const int* lo,
+                                          int lo_max, const TreeRows<NT>& tr, int hi,
+                                          typename KV::V& vv, int tok0, float sc, float vs,
+                                          int grp) {
+    // The lane's maximum is taken first: inlined right after the MFMAs of update(), it sits
+    // in their basic block, where the wait states a VALU read of an MFMA result needs are
+    // counted exactly, while a first read placed behind a branch was seen to get too few
+    // (stale maxima, run-to-run differences in the last bits).  Masked blocks take it again
+    // after the masks.
+    float lm[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      lm[nt] = fmaxf(fmaxf(pr[nt][0], pr[nt][1]), fmaxf(pr[nt][2], pr[nt][3]));
     float vfac = 1.f;
     if constexpr (kScaled) {
       vfac = vs * inv_vref256;
@@ -561,9 +584,6 @@ struct Rows {
     // weights take the rounded product, as the maximum does, so that the largest weight
     // is exactly 1.
     const float scp = fmaxf(sc, 1.17549435e-38f);
-    f32x4 pr[NT];
-    float lm[NT];
-    const auto& km = KV::k_mat(kk);
     // Lazy reference: a row's reference m moves only when a score of the block exceeds it
     // by more than KV::kLazy (log2 units), so the weights exp2(s - m) stay below 2^kLazy
     // and most blocks skip the rescale of the accumulators.  Softmax does not depend on
@@ -571,15 +591,6 @@ struct Rows {
     // any reference is decided from each lane's own 4 scores; the row maximum is reduced
     // across the row's four lanes only when it does.
     bool move = false;
-    // The lane's maximum is taken right after the MFMAs, in the same basic block: there the
-    // wait states a VALU read of an MFMA result needs are counted exactly, while a first
-    // read placed behind a branch was seen to get too few (stale maxima, run-to-run
-    // differences in the last bits).  Masked blocks take it again after the masks.
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      pr[nt] = KV::qk(km, qop[nt]);
-      lm[nt] = fmaxf(fmaxf(pr[nt][0], pr[nt][1]), fmaxf(pr[nt][2], pr[nt][3]));
-    }
     // blocks inside every row's range skip the per-token tests (a wave-wide branch)
     if (__any(need_mask)) {
 #pragma unroll
@@ -964,6 +975,26 @@ template <class KV, int NT> struct WavesPerEU {
 // TREE: multi-query rows whose candidates are filtered by a visibility mask (direct mode).
 // RG > 1: each workgroup serves RG row tiles of its (sequence, KV head) (multi-query rows).
 // REUSE: several workgroups read each tile (plain loads, which L2 keeps).
+// The sequence of rank r in the batch ordered by decreasing length (ties by index), for
+// batches of up to 64 sequences (one per lane; larger batches keep their order).  Units are
+// dealt in rank order, so every XCD starts on its longest units and the short ones fill
+// in behind them (longest-processing-time-first): with 4 to 32 sequences of uneven length
+// the last workgroups otherwise ran alone for a fifth of the time.
+constexpr int kRankedSeqs = 64;
+__device__ __forceinline__ int seq_by_rank(const AttnArgs& a, int r) {
+  const int B = a.num_seqs;
+  if (B > kRankedSeqs) return r;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int Li = lane < B ? clamp_len(a.seq_lens[lane], a.max_blocks) : -1;
+  int rank = 0;
+  for (int j = 0; j < B; ++j) {
+    const int Lj = __builtin_amdgcn_readlane(Li, j);
+    rank += (Lj > Li || (Lj == Li && j < lane)) ? 1 : 0;
+  }
+  const uint64_t hit = __ballot(lane < B && rank == r);
+  return hit != 0 ? (int)__builtin_ctzll(hit) : r;
+}
+
 template <class KV, int D, int NT, int W, int NBUF, bool SW, bool TREE = false, int RG = 1,
           bool REUSE = false>
 __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(WavesPerEU<KV, NT>::value)))
@@ -976,7 +1007,7 @@ void paged_attn_kernel(AttnArgs a) {
   int64_t rest = u / a.max_parts;
   const int rg = (int)(rest % nrg);
   rest /= nrg;
-  const int b = (int)(rest % a.num_seqs);
+  const int b = __builtin_amdgcn_readfirstlane(seq_by_rank(a, (int)(rest % a.num_seqs)));
   const int g = (int)(rest / a.num_seqs);
   const int L = clamp_len(a.seq_lens[b], a.max_blocks);
   int lo = 0, hi = L;
@@ -1450,9 +1481,12 @@ int occupancy_one() {
 #ifndef PA_TREE_RG
 #define PA_TREE_RG 1
 #endif
+#ifndef PA_MQ_NT
+#define PA_MQ_NT 2
+#endif
 template <class KV, int D, int NBUF>
 int launch_tree_one(const AttnArgs& a, void* stream) {
-  constexpr int NT = 2, W = PA_WAVES, RG = PA_TREE_RG;
+  constexpr int NT = PA_MQ_NT, W = PA_WAVES, RG = PA_TREE_RG;
   const int nrg = (a.rows + 16 * NT * RG - 1) / (16 * NT * RG);
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg;
   const int64_t grid = (units + 7) / 8 * 8;
@@ -1485,7 +1519,7 @@ int dispatch_dim(const AttnArgs& a, Op op, void* stream) {
     }
     return occupancy_one<KV, D, 1, W, PA_NBUF_1>();
   }
-  if (op == kLaunch) return launch_one<KV, D, 2, W, PA_NBUF_2>(a, stream);
+  if (op == kLaunch) return launch_one<KV, D, PA_MQ_NT, W, PA_MQ_NT == 1 ? PA_NBUF_1 : PA_NBUF_2>(a, stream);
   if (op == kLaunchBalanced) return launch_balanced_one<KV, D, 2, W, PA_NBUF_2, false>(a, stream);
   if (op == kLaunchBalancedAppend) {
     if constexpr (kCanAppend) return launch_balanced_one<KV, D, 2, W, PA_NBUF_2, true>(a, stream);
