@@ -57,6 +57,7 @@ def test_counter_summary_groups_workloads(tmp_path, monkeypatch):
 
     class A:
         steps, warmup, event_steps, no_cpu, path, layout = 2, 2, 2, True, "step", "interleaved"
+        calibrate = False
     bench.counter_summary(A(), str(tmp_path), "unit")
     text = (out_dir / "unit.md").read_text()
     lines = [l for l in text.splitlines() if l.startswith(("| llama", "| tiny"))]
