@@ -795,6 +795,56 @@ def test_decode_step_lengths_at_block_edges(P):
     _check_decode_step(P, wl, 3, zero_lens=(1, 5))
 
 
+@pytest.mark.parametrize("interleave", [False, True])
+def test_decode_steps_back_to_back(P, interleave):
+    """Six decode steps queued on one stream with no host synchronisation between them, as
+    a serving loop (and the benchmark) issues them: every step appends a fresh token to
+    each sequence and attends over it, all steps share one workspace, and each keeps its
+    own output.  Step s + 1 reads the token step s wrote, and its attention kernel reuses
+    the partial rows step s's merge reads, so stream order is what keeps them apart.  The
+    oracle runs the same steps one after another with its own scatter."""
+    S = 6
+    wl = _small("llama3_8b", batch=10, length_range=(S + 1, 600))
+    c = wl.cfg
+    gen = torch.Generator().manual_seed(33)
+    final = wl.seq_lens.numpy()
+    tables = wl.block_tables.numpy()
+    dv = Dev(wl, interleave)
+    d = dims_of(P, wl, dv)
+    G = P.paged_attn_balanced_workgroups(d, 1)
+    ws = torch.full((P.paged_attn_balanced_workspace_bytes(d, 1, G),), 0xFF, dtype=torch.uint8,
+                    device="cuda:0")
+    sm = float(np.float32(wl.sm_scale))
+    say(f"[case] {S} decode steps back to back B={c.batch} G={G} interleave={interleave}")
+    steps = []
+    for s in range(S):
+        lens = (final - (S - 1) + s).astype(np.int32)
+        q = _rand_bf16(gen, (c.batch, 1, c.num_q_heads, c.head_dim))
+        kn = _rand_bf16(gen, (c.batch, c.num_kv_heads, c.head_dim), 1.0 + s % 3)
+        vn = _rand_bf16(gen, (c.batch, c.num_kv_heads, c.head_dim))
+        steps.append((lens, q, kn, vn, torch.from_numpy(lens).cuda(), q.cuda(), kn.cuda(),
+                      vn.cuda()))
+    outs = [torch.full((c.batch, 1, c.num_q_heads, c.head_dim), float("nan"), device="cuda:0")
+            for _ in range(S)]
+    torch.cuda.synchronize()
+    for s, (_, _, _, _, dl, dq, dk, dvn) in enumerate(steps):
+        P.paged_decode_step(d, dq, dk, dvn, dv.k_cache, dv.v_cache, dv.block_tables, dl, sm, G,
+                            ws, outs[s])
+        P.paged_attn_balanced_merge(d, 1, G, ws, outs[s])
+    torch.cuda.synchronize()
+    kc, vc = raw(wl.k_cache), raw(wl.v_cache)
+    for s, (lens, q, kn, vn, *_) in enumerate(steps):
+        slots = np.array([paging.slot_of(tables[b], int(lens[b]) - 1) for b in range(c.batch)])
+        kc, vc = paging.append(kc, vc, raw(kn), raw(vn), slots)
+        ref, _ = attention.paged_attention(raw(q), c.q_dtype, kc, vc, c.kv_dtype, tables, lens,
+                                           sm, 1)
+        say(f"  step {s}")
+        _assert_close(outs[s], ref, TOL[c.kv_dtype])
+    gk, gv = dv.caches_host()
+    assert np.array_equal(raw(gk).view(np.uint8), kc.view(np.uint8)), "K cache after the steps"
+    assert np.array_equal(raw(gv).view(np.uint8), vc.view(np.uint8)), "V cache after the steps"
+
+
 def test_decode_step_int8_rejected(P):
     wl = _small("verify_int8", batch=2, length_range=(1, 50), num_q_pos=1)
     d = dims_of(P, wl)
