@@ -1080,6 +1080,9 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   constexpr int kStage = 64;
   __shared__ int s_pref[kMaxBalancedSeqs + 1];
   __shared__ int s_fb[SW ? kMaxBalancedSeqs : 1];  // first block a row of the sequence may see
+  // The lengths stay in LDS: a global load of one at a segment switch would be counted with
+  // the tile loads in flight, and waiting for it would drain the wave's ring.
+  __shared__ int s_len[kMaxBalancedSeqs];
   const int64_t wid = xcd_logical_id();
   if (wid >= a.num_workgroups) return;
   const int lane = threadIdx.x & (kWave - 1);
@@ -1099,6 +1102,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     int nb = 0;
     if (bb < B) {
       const int Lb = clamp_len(a.seq_lens[bb], a.max_blocks);
+      s_len[bb] = Lb;
       int lam0 = Lb - a.num_q_pos + 1;
       lam0 = lam0 < 0 ? 0 : lam0;
       int fb = 0;
@@ -1286,7 +1290,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
       iss_end = sg.end;
       if (nxt.j < 0) {
         nxt = sg;
-        const int Ls = clamp_len(a.seq_lens[sg.b], a.max_blocks);
+        const int Ls = __builtin_amdgcn_readfirstlane(s_len[sg.b]);
         lim_min_next = load_rows<KV, D, NT, SW>(a, sg.b, sg.g, sg.rg, Ls, rows_hi(sg, Ls), qnext,
                                                 lim_next, lo_next, lo_max_next, no_tree, row16,
                                                 grp);
@@ -1326,7 +1330,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
       if (cur.j >= 0) finish();
       const bool pre = nxt.j >= 0 && x >= nxt.start && x < nxt.end;
       cur = pre ? nxt : locate(x);
-      L = clamp_len(a.seq_lens[cur.b], a.max_blocks);
+      L = __builtin_amdgcn_readfirstlane(s_len[cur.b]);
       const int hi = rows_hi(cur, L);
       if (pre) {
 #pragma unroll
