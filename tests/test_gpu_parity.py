@@ -795,6 +795,22 @@ def test_decode_step_lengths_at_block_edges(P):
     _check_decode_step(P, wl, 3, zero_lens=(1, 5))
 
 
+@pytest.mark.parametrize("B", [65, 300, 2048])
+def test_large_batches(P, B):
+    """Batches past the direct kernel's longest-first ranking (64 sequences) and past one
+    chunk of the balanced kernel's prefix scan (256 sequences), up to its limit of 2048:
+    direct, balanced and the decode step against the oracle on every output; contexts of
+    1-60 tokens, so that some segments lie inside one wave's slice and others are cut
+    over several."""
+    wl = _small("llama3_8b", batch=B, length_range=(1, 60), num_q_heads=8, num_kv_heads=2,
+                head_dim=64, spare=3)
+    kc, vc = oracle_caches(wl)
+    ref = oracle_attention(wl, kc, vc)
+    _check_attention(P, wl, ref=ref)
+    _check_attention(P, wl, balanced=0, interleave=True, ref=ref)
+    _check_decode_step(P, wl, 0, interleave=True, ref=ref)
+
+
 @pytest.mark.parametrize("interleave", [False, True])
 def test_decode_steps_back_to_back(P, interleave):
     """Six decode steps queued on one stream with no host synchronisation between them, as
