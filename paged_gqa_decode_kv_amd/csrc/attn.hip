@@ -15,11 +15,12 @@
 //    K tiles are stored as 16-byte token columns and V tiles dim-major, which is exactly
 //    the register layout both MFMA A-operands want: each K load instruction reads 1 KiB
 //    in lane order and each V load 512 contiguous bytes.
-//  * Online softmax in the log2 domain: per row a running max and a running sum; the
-//    output accumulators are rescaled only when some row's max grows.
+//  * Online softmax in the log2 domain: per row a running reference (max) and a running
+//    sum; the output accumulators are rescaled only when a block's scores exceed some
+//    row's reference by more than a fixed margin (the weights stay bounded meanwhile).
 //  * P feeds the bf16 P*V MFMA in two 16-bit pieces (hi + lo) so the product keeps ~16
-//    significant bits of the fp32 probabilities; the int8 path rounds P once to fp16
-//    (11 bits) and the fp32 path uses fp32 MFMA directly.
+//    significant bits of the fp32 probabilities; the 8-bit (int8, fp8) paths round P once
+//    to fp16 (11 bits) and the fp32 path uses fp32 MFMA directly.
 //  * int8 / fp8 K/V are decoded in registers to exact bf16 (K, beside the bf16 q) and fp16
 //    (V, beside the fp16 weights); the per-(block, head) K scale multiplies the scores and
 //    the V scale is folded into P.
