@@ -76,21 +76,22 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int nwv = blockDim.x / kWave;
-  const int64_t j = blockIdx.x;
+  // (flat block positions fit in int32, as the host checks: 32-bit divisions here)
+  const int j = blockIdx.x;
   const int B = a.num_seqs;
   const int nrg = (a.rows + row_tile - 1) / row_tile;
-  const int64_t gr = j / B;
-  const int b = (int)(j % B);
-  const int g = (int)(gr / nrg);
-  const int rg = (int)(gr % nrg);
+  const int gr = j / B;
+  const int b = j - gr * B;
+  const int g = gr / nrg;
+  const int rg = gr - g * nrg;
 
-  const int64_t T = a.ws_prefix[B];
-  const int64_t total = T * a.num_kv_heads * nrg;
-  const int64_t per = (total + a.num_workers - 1) / a.num_workers;
-  const int64_t s0 = gr * T + a.ws_prefix[b];
-  const int64_t s1 = gr * T + a.ws_prefix[b + 1];
-  const int64_t w0 = s1 > s0 ? s0 / per : 0;
-  const int64_t w1 = s1 > s0 ? (s1 - 1) / per : -1;
+  const int T = a.ws_prefix[B];
+  const int total = T * a.num_kv_heads * nrg;
+  const int per = (int)(((unsigned)total + (unsigned)a.num_workers - 1u) / (unsigned)a.num_workers);
+  const int s0 = gr * T + a.ws_prefix[b];
+  const int s1 = gr * T + a.ws_prefix[b + 1];
+  const int w0 = s1 > s0 ? (int)((unsigned)s0 / (unsigned)per) : 0;
+  const int w1 = s1 > s0 ? (int)((unsigned)(s1 - 1) / (unsigned)per) : -1;
   if (s1 > s0 && w0 == w1) return;   // written by the attention kernel
 
   // Within a row's wave the lanes split into PG groups of D / 4 lanes: each group takes one
