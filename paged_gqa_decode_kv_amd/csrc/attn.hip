@@ -1004,12 +1004,14 @@ void paged_attn_kernel(AttnArgs a) {
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * nrg * a.max_parts;
   const int64_t u = xcd_logical_id();
   if (u >= units) return;
-  const int p = (int)(u % a.max_parts);
-  int64_t rest = u / a.max_parts;
-  const int rg = (int)(rest % nrg);
-  rest /= nrg;
-  const int b = __builtin_amdgcn_readfirstlane(seq_by_rank(a, (int)(rest % a.num_seqs)));
-  const int g = (int)(rest / a.num_seqs);
+  // (the grid, and so u, fits in int32: 32-bit divisions)
+  const unsigned uu = (unsigned)u;
+  const int p = (int)(uu % (unsigned)a.max_parts);
+  unsigned rest = uu / (unsigned)a.max_parts;
+  const int rg = (int)(rest % (unsigned)nrg);
+  rest /= (unsigned)nrg;
+  const int b = __builtin_amdgcn_readfirstlane(seq_by_rank(a, (int)(rest % (unsigned)a.num_seqs)));
+  const int g = (int)(rest / (unsigned)a.num_seqs);
   const int L = clamp_len(a.seq_lens[b], a.max_blocks);
   int lo = 0, hi = L;
   if (a.split) {
@@ -1134,7 +1136,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   const int nrg = (a.rows + 16 * NT - 1) / (16 * NT);
   const int T = __builtin_amdgcn_readfirstlane(s_pref[B]);
   const int total = T * a.num_kv_heads * nrg;
-  const int per = (int)(((int64_t)total + a.num_workers - 1) / a.num_workers);
+  const int per = (int)(((unsigned)total + (unsigned)a.num_workers - 1u) / (unsigned)a.num_workers);
   const int64_t v = wid * W + w;
   if (v * per >= total) return;
   const int x0 = (int)(v * per);
@@ -1311,9 +1313,11 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   // alone with half the loads in flight.  A wave's user priority drops by one at each
   // quarter of its slice, so whichever wave is behind is issued first.
   int quarter = -1;
+  // quarter q of the slice starts at block ceil(q * n / 4)
+  const int qt1 = (n + 3) / 4, qt2 = (2 * n + 3) / 4, qt3 = (3 * n + 3) / 4;
   auto set_priority = [&](int k) {
     if constexpr (PA_BAL_PRIO) {
-      const int q4 = (int)(((int64_t)4 * k) / (n > 0 ? n : 1));
+      const int q4 = (k >= qt1 ? 1 : 0) + (k >= qt2 ? 1 : 0) + (k >= qt3 ? 1 : 0);
       if (q4 != quarter) {
         quarter = q4;
         if (q4 == 0) __builtin_amdgcn_s_setprio(3);
