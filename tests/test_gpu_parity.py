@@ -811,6 +811,21 @@ def test_large_batches(P, B):
     _check_decode_step(P, wl, 0, interleave=True, ref=ref)
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("llama3_8b_fp8", dict(batch=300, length_range=(1, 60), num_q_heads=8, num_kv_heads=2,
+                           head_dim=64)),
+    ("verify_int8", dict(batch=300, length_range=(6, 90))),   # 24 rows: two row tiles
+])
+def test_large_batches_8bit(P, name, kw):
+    """The 8-bit caches (per-block scales staged with the table entries) and two row tiles
+    per wave past one chunk of the prefix scan: direct and balanced against the oracle."""
+    wl = _small(name, spare=3, **kw)
+    kc, vc = oracle_caches(wl)
+    ref = oracle_attention(wl, kc, vc)
+    _check_attention(P, wl, ref=ref)
+    _check_attention(P, wl, balanced=0, interleave=True, ref=ref)
+
+
 @pytest.mark.parametrize("interleave", [False, True])
 def test_decode_steps_back_to_back(P, interleave):
     """Six decode steps queued on one stream with no host synchronisation between them, as
