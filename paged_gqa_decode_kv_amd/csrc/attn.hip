@@ -31,6 +31,7 @@
 //  * Workgroup ids are remapped so that consecutive units (same KV head, neighbouring
 //    sequences -- e.g. sequences sharing a prefix) land on the same XCD and its L2.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include "launch.hpp"
 #include "pa_common.hpp"
@@ -1098,6 +1099,10 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   // window a sequence's list starts at the block holding its first row's first visible
   // token; the blocks before it are not dealt out at all.
   __shared__ int s_scan[kWave * W];
+  // two row tiles: LDS slot w - 1 holds wave w's parked piece once its flag is set
+  constexpr bool kComb = NT > 1;
+  __shared__ int s_dflag[kComb ? W - 1 : 1];
+  if (kComb && threadIdx.x < W - 1) s_dflag[threadIdx.x] = 0;
   int carry = 0;
   if (threadIdx.x == 0) s_pref[0] = 0;
   for (int c0 = 0; c0 < B; c0 += kWave * W) {
@@ -1279,10 +1284,82 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     const int hi_t = (last - sg.start + sg.fb) * kBlockTokens;
     return hi_t < Ls ? hi_t : Ls;
   };
-  auto finish = [&]() {
+  // ---- two row tiles: a segment cut between waves of one workgroup is combined on chip
+  // (one partial result per workgroup instead of one per wave; with one row tile the
+  // partials are small and the extra state cost registers for no gain): a wave whose
+  // first segment began in an earlier wave's slice of the same workgroup (its "head
+  // piece") parks its rows in LDS slot w - 1 and moves on without waiting; the first wave
+  // of the workgroup that holds the segment -- for which the segment runs on past the end
+  // of its slice, so this is its last one -- adds the parked rows to its own at the end of
+  // its slice and writes the segment (if the workgroup holds all of it) or one partial
+  // result for the merge kernel.  Each wave parks at most one piece, so each slot is used
+  // once per launch.  The wait for a parked piece is bounded (kSpinLimit polls of ~100
+  // cycles): a broken hand-over would end the kernel with wrong rows, not hang it.
+  constexpr int ND = D / 16;
+  constexpr int kSpinLimit = 1 << 20;
+  constexpr int kSlots = kComb ? W - 1 : 1;
+  __shared__ float s_dm[kSlots][kComb ? NT * 16 : 1];
+  __shared__ float s_dl[kSlots][kComb ? NT * 16 : 1];
+  __shared__ f32x4 s_dacc[kSlots][kComb ? NT : 1][kComb ? ND : 1][kComb ? kWave : 1];
+  // workgroup's flat range and its waves' ids
+  const int wv0 = (int)(wid * W);
+  const int wx0 = (int)((int64_t)wv0 * per);
+  const int wx1 = total - wx0 > W * per ? wx0 + W * per : total;
+  auto finish = [&](auto at_end) {
     st.totals();
     const bool whole = cur.start >= x0 && cur.end <= x1;
-    write_rows<KV, D, NT>(a, st, whole ? kDirect : kBalanced, cur.b, cur.g, cur.rg, v + cur.j,
+    if constexpr (!kComb) {
+      write_rows<KV, D, NT>(a, st, whole ? kDirect : kBalanced, cur.b, cur.g, cur.rg, v + cur.j,
+                            a.ws_out_lse, row16, grp);
+      return;
+    }
+    if (!whole && cur.start < x0 && w > 0) {  // park: the segment's first wave takes it
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (grp == 0) {
+          s_dm[w - 1][nt * 16 + row16] = st.m[nt];
+          s_dl[w - 1][nt * 16 + row16] = st.l[nt];
+        }
+#pragma unroll
+        for (int t = 0; t < ND; ++t) s_dacc[w - 1][nt][t][lane] = st.acc[nt][t];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0)
+        __hip_atomic_store(&s_dflag[w - 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return;
+    }
+    if constexpr (decltype(at_end)::value) {
+      // the waves after this one in the workgroup that hold blocks of the segment
+      int wl = w;
+      if (cur.end > x1) {
+        const int last = (int)((unsigned)(cur.end - 1) / (unsigned)per) - wv0;
+        wl = last < W - 1 ? last : W - 1;
+      }
+      for (int sl = w; sl < wl; ++sl) {
+#pragma unroll 1
+        for (int i = 0; i < kSpinLimit; ++i) {
+          if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                  &s_dflag[sl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0)
+            break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float mp = s_dm[sl][nt * 16 + row16];
+          const float M = fmaxf(mp, st.m[nt]);
+          const float Mu = M == -INFINITY ? 0.f : M;
+          const float fp = __builtin_amdgcn_exp2f(mp - Mu);
+          const float fo = __builtin_amdgcn_exp2f(st.m[nt] - Mu);
+          st.l[nt] = s_dl[sl][nt * 16 + row16] * fp + st.l[nt] * fo;
+          st.m[nt] = M;
+#pragma unroll
+          for (int t = 0; t < ND; ++t) st.acc[nt][t] = s_dacc[sl][nt][t][lane] * fp + st.acc[nt][t] * fo;
+        }
+      }
+    }
+    const bool whole_wg = cur.start >= wx0 && cur.end <= wx1;
+    write_rows<KV, D, NT>(a, st, whole_wg ? kDirect : kBalanced, cur.b, cur.g, cur.rg, v + cur.j,
                           a.ws_out_lse, row16, grp);
   };
   auto issue = [&](typename KV::K& kk, typename KV::V& vv, int kn, const Slot& sl) {
@@ -1332,7 +1409,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     set_priority(k);
     const int x = x0 + k;
     if (x >= cur.end) {
-      if (cur.j >= 0) finish();
+      if (cur.j >= 0) finish(std::false_type{});
       const bool pre = nxt.j >= 0 && x >= nxt.start && x < nxt.end;
       cur = pre ? nxt : locate(x);
       L = __builtin_amdgcn_readfirstlane(s_len[cur.b]);
@@ -1410,7 +1487,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
       }
     }
   }
-  if (cur.j >= 0) finish();
+  if (cur.j >= 0) finish(std::true_type{});
   if constexpr (APP) drain();
 }
 

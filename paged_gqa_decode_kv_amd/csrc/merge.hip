@@ -64,9 +64,13 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
 
 // Balanced mode: segment j (KV head g, row group rg, sequence b) occupies flat blocks
 // [S_j, S_{j+1}) with S_j = (g * nrg + rg) * T + prefix[b]; attention wave w covered
-// [w * per, (w + 1) * per), so the waves that wrote a partial for segment j are
-// w = S_j / per .. (S_{j+1} - 1) / per, at partial ids w + j.  A segment inside one slice
-// was written out by the attention kernel and is skipped here; an empty segment gets zeros.
+// [w * per, (w + 1) * per), so the waves that held blocks of segment j are
+// w0 = S_j / per .. w1 = (S_{j+1} - 1) / per.  With two row tiles the attention kernel
+// combines the pieces of one workgroup (W consecutive waves) on chip, so there is one
+// partial per workgroup, at partial id w + j for the first of its waves w in [w0, w1]
+// (with one row tile W counts as 1 here: one partial per wave, at w + j).  A segment
+// inside one workgroup (one wave) was written out by the attention kernel and is skipped
+// here; an empty segment gets zeros.
 // One wave per query row of the segment's row tile, in one workgroup per segment (two for
 // row tiles of more than 16 rows: blockIdx.y picks the half).
 template <int D>
@@ -92,7 +96,11 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
   const int s1 = gr * T + a.ws_prefix[b + 1];
   const int w0 = s1 > s0 ? (int)((unsigned)s0 / (unsigned)per) : 0;
   const int w1 = s1 > s0 ? (int)((unsigned)(s1 - 1) / (unsigned)per) : -1;
-  if (s1 > s0 && w0 == w1) return;   // written by the attention kernel
+  // waves per attention workgroup whose pieces were combined
+  const int W = row_tile > 16 ? a.num_workers / a.num_workgroups : 1;
+  const int k0 = w0 / W;                           // first and last workgroup
+  const int k1 = s1 > s0 ? w1 / W : -1;            // (none for an empty segment)
+  if (s1 > s0 && k0 == k1) return;   // written by the attention kernel
 
   // Within a row's wave the lanes split into PG groups of D / 4 lanes: each group takes one
   // piece per step, each lane four dims of it; U steps are in flight at once.  The pieces'
@@ -102,7 +110,7 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
   constexpr int PG = kWave / LPR;
   constexpr int U = 8;   // (16 spills: a 1024-thread workgroup leaves 128 VGPRs a lane)
   const int pg = lane / LPR, dl = lane % LPR;
-  const int64_t npc = w1 - w0 + 1;  // pieces (0 for an empty segment)
+  const int64_t npc = k1 - k0 + 1;  // pieces (0 for an empty segment)
   // workgroup y of the segment takes rows y * nwv .. of its row tile, one per wave
   for (int rl = blockIdx.y * nwv + wv; rl < row_tile && rl < (int)(blockIdx.y + 1) * nwv;
        rl += nwv) {
@@ -120,7 +128,8 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t q = q0 + u * PG + pg;
-        const int64_t pid = w0 + (q < npc ? q : 0) + j;
+        const int64_t qq = q < npc ? q : 0;
+        const int64_t pid = (qq == 0 ? w0 : (k0 + qq) * W) + j;
         lp[u] = a.ws_lse[pid * row_tile + rl];
         v[u] = *reinterpret_cast<const f32x4*>(a.ws_out + (pid * row_tile + rl) * D + 4 * dl);
         if (q >= npc) lp[u] = -INFINITY;

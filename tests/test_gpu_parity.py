@@ -362,6 +362,23 @@ def test_balanced_edge_cases(P, name, kw):
     _check_attention(P, wl, balanced=5)
 
 
+@pytest.mark.parametrize("G", [1, 2, 5, 33])
+@pytest.mark.parametrize("name,kw", [
+    ("llama3_8b", dict(num_q_pos=6)),                    # bf16, 24 rows
+    ("verify_int8", dict()),                             # int8, 24 rows
+    ("llama3_8b_fp8", dict(num_q_pos=6)),                # fp8, 24 rows
+    ("tiny_fp32", dict(num_q_pos=7, head_dim=128)),      # fp32, 28 rows
+])
+def test_balanced_two_tiles_workgroup_combine(P, name, kw, G):
+    """Two row tiles per wave: a segment cut between waves of one workgroup is combined in
+    LDS (later waves park their rows, the segment's first wave of the workgroup adds them at
+    the end of its slice) and one partial per workgroup reaches the merge kernel.  Lengths
+    from empty to several slices long, and workgroup counts from one (every segment combined
+    on chip) to many (segments crossing several workgroups)."""
+    wl = _small(name, batch=7, lengths=(0, 900, 17, 2000, 1, 333, 1200), append=False, **kw)
+    _check_attention(P, wl, balanced=G)
+
+
 def test_balanced_workspace_errors(P):
     wl = _small("llama3_8b", batch=2, length_range=(1, 50), append=False)
     c = wl.cfg
