@@ -128,11 +128,13 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t q = q0 + u * PG + pg;
-        const int64_t qq = q < npc ? q : 0;
-        const int64_t pid = (qq == 0 ? w0 : (k0 + qq) * W) + j;
-        lp[u] = a.ws_lse[pid * row_tile + rl];
-        v[u] = *reinterpret_cast<const f32x4*>(a.ws_out + (pid * row_tile + rl) * D + 4 * dl);
-        if (q >= npc) lp[u] = -INFINITY;
+        lp[u] = -INFINITY;
+        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (q < npc) {  // (no load for the slots past the last piece)
+          const int64_t pid = (q == 0 ? w0 : (k0 + q) * W) + j;
+          lp[u] = a.ws_lse[pid * row_tile + rl];
+          v[u] = *reinterpret_cast<const f32x4*>(a.ws_out + (pid * row_tile + rl) * D + 4 * dl);
+        }
       }
       // the chunk's maximum over all PG groups
       float mc = M;
