@@ -96,7 +96,8 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
   const int s1 = gr * T + a.ws_prefix[b + 1];
   const int w0 = s1 > s0 ? (int)((unsigned)s0 / (unsigned)per) : 0;
   const int w1 = s1 > s0 ? (int)((unsigned)(s1 - 1) / (unsigned)per) : -1;
-  // waves per attention workgroup whose pieces were combined
+  // waves per attention workgroup whose pieces were combined (the two-tile launches use
+  // balanced_merge_rows_kernel; kept general here)
   const int W = row_tile > 16 ? a.num_workers / a.num_workgroups : 1;
   const int k0 = w0 / W;                           // first and last workgroup
   const int k1 = s1 > s0 ? w1 / W : -1;            // (none for an empty segment)
@@ -170,6 +171,107 @@ __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int ro
   }
 }
 
+// The same merge for two row tiles, whose segments have few pieces (one per attention
+// workgroup): each lane group of D / 4 lanes owns RPG rows and loads U / RPG pieces of each
+// per round trip, so a wave merges PG * RPG rows and a 24-row segment needs 6 waves rather
+// than 24 (the launch of the waves, not their work, set the one-row-per-wave merge's time
+// there).  Every lane of a group reads the same lse values, so no lane exchanges anything.
+template <int D, int RPG>
+__global__ __launch_bounds__(512) void balanced_merge_rows_kernel(AttnArgs a, int row_tile,
+                                                                  float* __restrict__ out,
+                                                                  float* __restrict__ out_lse) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int j = blockIdx.x;
+  const int B = a.num_seqs;
+  const int nrg = (a.rows + row_tile - 1) / row_tile;
+  const int gr = j / B;
+  const int b = j - gr * B;
+  const int g = gr / nrg;
+  const int rg = gr - g * nrg;
+
+  const int T = a.ws_prefix[B];
+  const int total = T * a.num_kv_heads * nrg;
+  const int per = (int)(((unsigned)total + (unsigned)a.num_workers - 1u) / (unsigned)a.num_workers);
+  const int s0 = gr * T + a.ws_prefix[b];
+  const int s1 = gr * T + a.ws_prefix[b + 1];
+  const int w0 = s1 > s0 ? (int)((unsigned)s0 / (unsigned)per) : 0;
+  const int w1 = s1 > s0 ? (int)((unsigned)(s1 - 1) / (unsigned)per) : -1;
+  // waves per attention workgroup whose pieces were combined (two row tiles), else 1
+  const int W = row_tile > 16 ? a.num_workers / a.num_workgroups : 1;
+  const int k0 = w0 / W;
+  const int k1 = s1 > s0 ? w1 / W : -1;
+  if (s1 > s0 && k0 == k1) return;  // written by the attention kernel
+
+  constexpr int LPR = D / 4;
+  constexpr int PG = kWave / LPR;
+  constexpr int U = 8;
+  constexpr int UR = U / RPG;  // pieces of one row per round trip
+  const int pg = lane / LPR, dl = lane % LPR;
+  const int npc = k1 - k0 + 1;  // pieces (0 for an empty segment)
+  int rl[RPG];
+  bool live[RPG];
+  float M[RPG], wsum[RPG];
+  f32x4 acc[RPG];
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    rl[i] = (wv * PG + pg) * RPG + i;
+    live[i] = rl[i] < row_tile && rg * row_tile + rl[i] < a.rows;
+    M[i] = -INFINITY;
+    wsum[i] = 0.f;
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int q0 = 0; q0 < npc; q0 += UR) {
+    float lp[RPG][UR];
+    f32x4 v[RPG][UR];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+#pragma unroll
+      for (int u = 0; u < UR; ++u) {
+        const int q = q0 + u;
+        lp[i][u] = -INFINITY;
+        v[i][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (live[i] && q < npc) {
+          const int64_t pid = (int64_t)(q == 0 ? w0 : (k0 + q) * W) + j;
+          lp[i][u] = a.ws_lse[pid * row_tile + rl[i]];
+          v[i][u] = *reinterpret_cast<const f32x4*>(a.ws_out + (pid * row_tile + rl[i]) * D + 4 * dl);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      float mc = M[i];
+#pragma unroll
+      for (int u = 0; u < UR; ++u) mc = fmaxf(mc, lp[i][u]);
+      if (mc == -INFINITY) continue;
+      if (M[i] != -INFINITY && mc != M[i]) {
+        const float c = __builtin_amdgcn_exp2f((M[i] - mc) * kLog2e);
+        acc[i] *= c;
+        wsum[i] *= c;
+      }
+      M[i] = mc;
+#pragma unroll
+      for (int u = 0; u < UR; ++u) {
+        const float wq = lp[i][u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lp[i][u] - mc) * kLog2e);
+        if (wq != 0.f) acc[i] += wq * v[i][u];
+        wsum[i] += wq;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    if (!live[i]) continue;
+    const int r = rg * row_tile + rl[i];
+    const int qi = r / a.group;
+    const int h = g * a.group + r % a.group;
+    const int64_t orow = (int64_t)(b * a.num_q_pos + qi) * a.num_q_heads + h;
+    const float inv = wsum[i] > 0.f ? 1.f / wsum[i] : 0.f;
+    *reinterpret_cast<f32x4*>(out + orow * D + 4 * dl) = acc[i] * inv;
+    if (out_lse != nullptr && dl == 0)
+      out_lse[orow] = wsum[i] > 0.f ? M[i] + __builtin_amdgcn_logf(wsum[i]) * kLn2 : -INFINITY;
+  }
+}
+
 }  // namespace
 
 int launch_balanced_merge(const AttnArgs& a, float* out, float* out_lse, void* stream) {
@@ -177,11 +279,26 @@ int launch_balanced_merge(const AttnArgs& a, float* out, float* out_lse, void* s
   const int nrg = (a.rows + rt - 1) / rt;
   const int64_t grid = (int64_t)a.num_kv_heads * nrg * a.num_seqs;
   if (grid > 0x7fffffff) return PA_ERR_DIMS;
-  // one wave per row of the tile: up to 16 per workgroup, more rows over more workgroups
   const int rows_in_tile = a.rows < rt ? a.rows : rt;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // two row tiles (one piece per attention workgroup): one workgroup per segment, PG * RPG
+  // rows per wave (RPG = 2).  (Used for one row tile as well when segments span at most 4
+  // slices, it gained nothing on the Llama-3-8B step and cost the fp8 decode step 1.3 us:
+  // ~5 pieces a row take two round trips at 4 per trip.)
+  if (rt > 16) {
+    const int rpw = 2 * (kWave / (a.head_dim / 4));
+    const int waves = (rows_in_tile + rpw - 1) / rpw;
+    if (a.head_dim == 64)
+      hipLaunchKernelGGL((balanced_merge_rows_kernel<64, 2>), dim3((unsigned)grid),
+                         dim3(kWave * waves), 0, s, a, rt, out, out_lse);
+    else
+      hipLaunchKernelGGL((balanced_merge_rows_kernel<128, 2>), dim3((unsigned)grid),
+                         dim3(kWave * waves), 0, s, a, rt, out, out_lse);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  }
+  // one wave per row of the tile: up to 16 per workgroup, more rows over more workgroups
   const int ysplit = (rows_in_tile + 15) / 16;
   const int waves = (rows_in_tile + ysplit - 1) / ysplit;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.head_dim == 64)
     hipLaunchKernelGGL(balanced_merge_kernel<64>, dim3((unsigned)grid, ysplit),
                        dim3(kWave * waves), 0, s, a, rt, out, out_lse);
