@@ -1305,10 +1305,29 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   const int wv0 = (int)(wid * W);
   const int wx0 = (int)((int64_t)wv0 * per);
   const int wx1 = total - wx0 > W * per ? wx0 + W * per : total;
+  // One row tile: a head piece (the slice's first segment, begun in an earlier slice) is
+  // finished while the ring streams on; its rows are parked in LDS and written after the
+  // loop, since global stores issued mid-stream sit in the in-order memory counter in front
+  // of the next tiles' loads (writing it at once cost the Llama-3-8B kernel ~1.4 us).
+  // (LDS rather than registers: the decode-step kernel has none to spare.)
+  __shared__ f32x4 s_hacc[kComb ? 1 : W][kComb ? 1 : ND][kComb ? 1 : kWave];
+  __shared__ float s_hml[kComb ? 1 : W][2][kComb ? 1 : 16];
+  Seg held_seg;
+  held_seg.j = -1;
   auto finish = [&](auto at_end) {
     st.totals();
     const bool whole = cur.start >= x0 && cur.end <= x1;
     if constexpr (!kComb) {
+      if (!decltype(at_end)::value && !whole) {
+#pragma unroll
+        for (int t = 0; t < ND; ++t) s_hacc[w][t][lane] = st.acc[0][t];
+        if (grp == 0) {
+          s_hml[w][0][row16] = st.m[0];
+          s_hml[w][1][row16] = st.l[0];
+        }
+        held_seg = cur;
+        return;
+      }
       write_rows<KV, D, NT>(a, st, whole ? kDirect : kBalanced, cur.b, cur.g, cur.rg, v + cur.j,
                             a.ws_out_lse, row16, grp);
       return;
@@ -1488,6 +1507,14 @@ void paged_attn_balanced_kernel(AttnArgs a) {
     }
   }
   if (cur.j >= 0) finish(std::true_type{});
+  if (!kComb && held_seg.j >= 0) {
+#pragma unroll
+    for (int t = 0; t < ND; ++t) st.acc[0][t] = s_hacc[w][t][lane];
+    st.m[0] = s_hml[w][0][row16];
+    st.l[0] = s_hml[w][1][row16];
+    write_rows<KV, D, NT>(a, st, kBalanced, held_seg.b, held_seg.g, held_seg.rg,
+                          v + held_seg.j, a.ws_out_lse, row16, grp);
+  }
   if constexpr (APP) drain();
 }
 
