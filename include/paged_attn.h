@@ -284,10 +284,12 @@ int kv_copy_blocks(const pa_dims* dims, const int32_t* block_pairs, int32_t num_
  * innermost) and wave v takes the contiguous slice [v * per, (v + 1) * per),
  * per = ceil(total blocks / waves).  A
  * segment that lies inside one slice is written to out (and out_lse) by this call; a
- * segment cut by slice boundaries leaves one partial result per piece in the workspace,
- * and paged_attn_balanced_merge, enqueued next on the same stream with the same
- * arguments, recombines them with the log-sum-exp identity (see lse_merge).  The pair is
- * the complete operation.
+ * segment cut by slice boundaries leaves partial results in the workspace -- one per
+ * piece, or, when a row tile holds more than 16 rows (G * nq > 16), one per workgroup,
+ * the pieces of a workgroup's waves being combined on chip first (a segment inside one
+ * workgroup is then written to out by this call too) -- and paged_attn_balanced_merge,
+ * enqueued next on the same stream with the same arguments, recombines them with the
+ * log-sum-exp identity (see lse_merge).  The pair is the complete operation.
  *   num_q_pos    nq >= 1; q [B][nq][Hq][head_dim]; out [B][nq][Hq][head_dim] fp32
  *   out_lse      device, [B][nq][Hq] fp32 (natural log; -inf for a row that sees no token),
  *                or NULL
