@@ -368,6 +368,8 @@ def test_balanced_edge_cases(P, name, kw):
     ("verify_int8", dict()),                             # int8, 24 rows
     ("llama3_8b_fp8", dict(num_q_pos=6)),                # fp8, 24 rows
     ("tiny_fp32", dict(num_q_pos=7, head_dim=128)),      # fp32, 28 rows
+    ("mistral_7b_window", dict(num_q_pos=6, sliding_window=300)),  # window: lists start late
+    ("llama2_70b_prefix", dict(num_q_pos=3, head_dim=64)),         # d64, 8 heads a group: 24 rows
 ])
 def test_balanced_two_tiles_workgroup_combine(P, name, kw, G):
     """Two row tiles per wave: a segment cut between waves of one workgroup is combined in
