@@ -44,6 +44,12 @@ def test_noalloc_decode_step_matches_the_workspace_step(P):
          False, 0),
         (W.generate(W.scaled("llama3_8b", batch=9, length_range=(1, 700)), spare_blocks=3),
          True, 5),
+        # 32 query heads on one KV head: two row tiles, whose pieces are combined per
+        # workgroup in the attention kernel and merged four rows a wave
+        (W.generate(W.scaled("llama3_8b", batch=5, length_range=(1, 900), num_q_heads=32,
+                             num_kv_heads=1), spare_blocks=3), True, 64),
+        (W.generate(W.scaled("llama3_8b", batch=5, length_range=(1, 900), num_q_heads=32,
+                             num_kv_heads=1), spare_blocks=3), False, 3),
     ]
     for wl, interleave, G in cases:
         c = wl.cfg
