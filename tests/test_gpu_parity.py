@@ -1152,7 +1152,7 @@ def _sweep_case(i):
     return kw, mode, bool(rng.integers(0, 2)), int(rng.choice([0, 1, 3, 7, 40]))
 
 
-@pytest.mark.parametrize("i", range(128))
+@pytest.mark.parametrize("i", range(512))
 def test_random_sweep(P, i):
     kw, mode, interleave, G = _sweep_case(i)
     wl = _small("llama3_8b", **kw)

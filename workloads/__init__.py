@@ -300,7 +300,8 @@ def generate(cfg, seed=None, *, poison=True, spare_blocks=0, shuffle_batch=False
             b += 1
     for bb in range(b, B):
         alloc.allocate(bb, lens[bb])
-    max_blocks = max(len(alloc.block_tables[i]) for i in range(B))
+    # (at least one column: a batch of empty sequences still passes a table, all -1)
+    max_blocks = max(1, max(len(alloc.block_tables[i]) for i in range(B)))
     tables = torch.full((B, max_blocks), -1, dtype=torch.int32)
     for i in range(B):
         row = alloc.block_tables[i]
