@@ -4,8 +4,8 @@
 // denominator.  With M = max_p lse_p and w_p = exp(lse_p - M) the full-context result is
 // sum_p w_p o_p / sum_p w_p and its lse is M + log sum_p w_p: exact, because exp(lse_p)
 // is partition p's share of the full denominator.  One wave per (sequence, query head)
-// row; lane k owns dims k, k + 64, ...  The partition count of each sequence is derived
-// from seq_lens exactly as the split attention kernel derives it.
+// row.  The partition count of each sequence is derived from seq_lens exactly as the split
+// attention kernel derives it.
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
@@ -23,40 +23,76 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
     const float* __restrict__ part_out, const float* __restrict__ part_lse,
     const int32_t* __restrict__ seq_lens, int32_t num_q_heads, int32_t max_blocks,
     int32_t part_tokens, int32_t max_parts, float* __restrict__ out, float* __restrict__ out_lse) {
-  constexpr int PER = D / kWave;
+  // The wave splits into PG groups of D / 4 lanes: each group takes one partition's row per
+  // step (four dims a lane) with its lse, U steps in flight, so one round trip covers PG * U
+  // partitions.  The first round is issued before the sequence length arrives (partitions
+  // past the sequence's count are masked afterwards; every slot below max_parts is inside
+  // the caller's arrays), so a row with up to PG * U partitions costs one round trip after
+  // the launch instead of one per partition.
+  constexpr int LPR = D / 4;
+  constexpr int PG = kWave / LPR;
+  constexpr int U = 8;
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x;
+  const int pg = lane / LPR, dl = lane % LPR;
   const int b = (int)(row / num_q_heads);
-  int L = seq_lens[b];
-  L = L < 0 ? 0 : (L > max_blocks * kBlockTokens ? max_blocks * kBlockTokens : L);
-  int n = L > 0 ? (L + part_tokens - 1) / part_tokens : 0;
-  n = n > max_parts ? max_parts : n;
-
   const float* lse_row = part_lse + row * max_parts;
-  // max over the occupied partitions (lanes stride over p, then a wave reduction)
+  const float* o = part_out + row * max_parts * D;
+  int L = seq_lens[b];
   float M = -INFINITY;
-  for (int p = lane; p < n; p += kWave) M = fmaxf(M, lse_row[p]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-
-  float acc[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  if (M != -INFINITY) {
-    const float* o = part_out + row * max_parts * D;
-    for (int p = 0; p < n; ++p) {
-      const float lp = lse_row[p];
-      if (lp == -INFINITY) continue;
-      const float wgt = __builtin_amdgcn_exp2f((lp - M) * kLog2e);
-      wsum += wgt;
+  int n = max_parts;  // partitions of this row; known once L has arrived
+  for (int q0 = 0; q0 < n; q0 += PG * U) {
+    float lp[U];
+    f32x4 v[U];
 #pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] += wgt * o[(int64_t)p * D + lane + k * kWave];
+    for (int u = 0; u < U; ++u) {
+      const int p = q0 + u * PG + pg;
+      lp[u] = -INFINITY;
+      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (p < n) {
+        lp[u] = lse_row[p];
+        v[u] = *reinterpret_cast<const f32x4*>(o + (int64_t)p * D + 4 * dl);
+      }
+    }
+    if (q0 == 0) {
+      L = L < 0 ? 0 : (L > max_blocks * kBlockTokens ? max_blocks * kBlockTokens : L);
+      const int np = L > 0 ? (L + part_tokens - 1) / part_tokens : 0;
+      n = np > max_parts ? max_parts : np;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (q0 + u * PG + pg >= n) lp[u] = -INFINITY;
+    // the chunk's maximum over all groups, then the rescaled sums
+    float mc = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mc = fmaxf(mc, lp[u]);
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1) mc = fmaxf(mc, __shfl_xor(mc, off));
+    if (mc == -INFINITY) continue;
+    if (M != -INFINITY && mc != M) {
+      const float c = __builtin_amdgcn_exp2f((M - mc) * kLog2e);
+      acc *= c;
+      wsum *= c;
+    }
+    M = mc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wq = lp[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lp[u] - M) * kLog2e);
+      if (wq != 0.f) acc += wq * v[u];
+      wsum += wq;
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  // the groups' partial sums (all groups share M)
 #pragma unroll
-  for (int k = 0; k < PER; ++k) out[row * D + lane + k * kWave] = acc[k] * inv;
+  for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off);
+    wsum += __shfl_xor(wsum, off);
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if (pg == 0) *reinterpret_cast<f32x4*>(out + row * D + 4 * dl) = acc * inv;
   if (out_lse != nullptr && lane == 0)
     out_lse[row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
 }
