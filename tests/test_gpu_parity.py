@@ -381,6 +381,17 @@ def test_balanced_two_tiles_workgroup_combine(P, name, kw, G):
     _check_attention(P, wl, balanced=G)
 
 
+@pytest.mark.parametrize("kv,G", [("bf16", 300), ("i8", 97), ("fp8", 512)])
+def test_balanced_two_tiles_many_pieces(P, kv, G):
+    """One long sequence on one KV head (24 rows) dealt over hundreds of workgroups: its one
+    segment leaves one partial per workgroup, so the two-tile merge runs many rounds of
+    four pieces a row (and the workgroup combine has every slice cut)."""
+    kw = dict(batch=1, lengths=(6000,), num_q_heads=4, num_kv_heads=1, num_q_pos=6,
+              append=False, kv_dtype=kv)
+    wl = _small("llama3_8b", **kw)
+    _check_attention(P, wl, balanced=G)
+
+
 def test_balanced_workspace_errors(P):
     wl = _small("llama3_8b", batch=2, length_range=(1, 50), append=False)
     c = wl.cfg
