@@ -1306,14 +1306,35 @@ void paged_attn_balanced_kernel(AttnArgs a) {
   const int wx0 = (int)((int64_t)wv0 * per);
   const int wx1 = total - wx0 > W * per ? wx0 + W * per : total;
   // One row tile: a head piece (the slice's first segment, begun in an earlier slice) is
-  // finished while the ring streams on; its rows are parked in LDS and written after the
-  // loop, since global stores issued mid-stream sit in the in-order memory counter in front
-  // of the next tiles' loads (writing it at once cost the Llama-3-8B kernel ~1.4 us).
-  // (LDS rather than registers: the decode-step kernel has none to spare.)
+  // finished while the ring streams on; its rows are parked in LDS and written once the
+  // wave has issued its last tile load (or after the loop), since global stores issued
+  // mid-stream sit in the in-order memory counter in front of the next tiles' loads
+  // (writing it at once cost the Llama-3-8B kernel ~1.4 us); stores behind every load
+  // delay none.  (LDS rather than registers: the decode-step kernel has none to spare.)
   __shared__ f32x4 s_hacc[kComb ? 1 : W][kComb ? 1 : ND][kComb ? 1 : kWave];
   __shared__ float s_hml[kComb ? 1 : W][2][kComb ? 1 : 16];
   Seg held_seg;
   held_seg.j = -1;
+  auto write_parked = [&]() {  // (write_rows' partial-result form, streamed from LDS)
+    const int rl = row16;
+    const int r = held_seg.rg * 16 + rl;
+    const float lsum = s_hml[w][1][rl];
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int64_t slot = v + held_seg.j;
+    if (r < a.rows) {
+      float* dst = a.ws_out + (slot * 16 + rl) * D;
+#pragma unroll
+      for (int t = 0; t < ND; ++t) {
+        const f32x4 x = s_hacc[w][t][lane];
+        *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * grp) = x * inv;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (grp == 0)
+        a.ws_lse[slot * 16 + rl] =
+            lsum > 0.f ? (s_hml[w][0][rl] + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+    }
+    held_seg.j = -1;
+  };
   auto finish = [&](auto at_end) {
     st.totals();
     const bool whole = cur.start >= x0 && cur.end <= x1;
@@ -1502,6 +1523,7 @@ void paged_attn_balanced_kernel(AttnArgs a) {
         if ((kn & (kStage - 1)) == 0 && kn < n) stage(kn);
         sb[sn] = slot_at(kn);
         issue(kb[sn], vb[sn], kn, sb[sn]);
+        if (!kComb && kn == n - 1 && held_seg.j >= 0) write_parked();
         consume(kb[s], vb[s], k + s, sb[s]);
       }
     }
