@@ -107,8 +107,9 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
 // (with one row tile W counts as 1 here: one partial per wave, at w + j).  A segment
 // inside one workgroup (one wave) was written out by the attention kernel and is skipped
 // here; an empty segment gets zeros.
-// One wave per query row of the segment's row tile, in one workgroup per segment (two for
-// row tiles of more than 16 rows: blockIdx.y picks the half).
+// This form serves one row tile (up to 16 rows): one wave per query row of the segment's
+// row tile, one workgroup per segment (the blockIdx.y split below covers larger tiles,
+// which balanced_merge_rows_kernel takes instead).
 template <int D>
 __global__ __launch_bounds__(1024) void balanced_merge_kernel(AttnArgs a, int row_tile,
                                                               float* __restrict__ out,
